@@ -1,0 +1,278 @@
+"""Benchmark: paged decode KV GB/s (and chunked prefill TFLOP/s) on one MI355X.
+
+A step is one pa_decode call over the Qwen3-8B per-GPU decode batch: B=32 rows, Hq=16,
+Hkv=4, head_dim 128, page 16, kv lengths U{512..4096}, pages scattered over a 16,384-page
+pool, bf16 K/V, fused Q/K RMSNorm + RoPE (theta 1e6).  Steps cycle over four independent
+K/V pools (same lengths, different pages and contents) so that consecutive steps never find
+their K/V in the 256 MB Infinity Cache: each step streams its K/V from HBM.
+
+Printed (one JSON line): value = algorithmic bytes per step / time per step, where the
+algorithmic bytes are the K and V bytes of every cached key of every KV head plus q, out,
+lse and the CSR metadata the kernel reads (the RoPE table and norm weights are constants
+served from cache and are not counted).  The roofline entry divides the same bytes by the
+decode kernel's average duration, measured with HIP events recorded on the launch stream.
+The chunked-prefill workload (B=4 x 512-query chunks after prefixes 0/1024/2048/3584,
+Hq=32, Hkv=8) is reported alongside with its algorithmic FLOPs (QK^T and PV over the
+causally visible pairs) per call.  The CPU oracle is timed on a bounded sample on the host.
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
+       python bench.py --profile-copy     # plain copy of a known size, for counter scaling
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
+METRIC = "paged decode KV GB/s (% HBM peak); paged prefill TFLOP/s (% MFMA peak)"
+ROTATIONS = 4
+
+
+def decode_bytes(b) -> int:
+    import numpy as np
+
+    D = 128
+    kv = int(np.sum(b.lengths)) * b.num_kv_heads * D * 2 * 2
+    q_out = 2 * b.batch * b.num_q_heads * D * 2
+    lse = b.batch * b.num_q_heads * 4
+    meta = 4 * ((b.batch + 1) + b.nnz + b.batch + b.batch)
+    return kv + q_out + lse + meta
+
+
+def prefill_flops(b) -> int:
+    """4 * D * Hq * sum over queries of visible keys (QK^T and PV, causal pairs only)."""
+    import numpy as np
+
+    total = 0
+    for r in range(b.batch):
+        L = int(b.lengths[r])
+        pos = b.query_position_ids[r].astype(np.int64)
+        total += int(np.sum(np.minimum(pos + 1, L)))
+    return 4 * 128 * b.num_q_heads * total
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+DECODE_SOURCES = ["deterministic_paged_kv_amd/csrc/pa_decode.hip", "deterministic_paged_kv_amd/csrc/pa_internal.h"]
+
+
+def traffic_from_profile(per_launch_alg_bytes):
+    """HBM bytes per decode launch from the committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", "decode_qwen3_8b_counters.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    if doc.get("source_hash") != source_hash(DECODE_SOURCES):
+        return None
+    return doc.get("hbm_bytes_per_launch")
+
+
+def device_rotation(base, i, device):
+    """Pool i of the rotation: the same lengths, a different page permutation and fresh K/V drawn
+    on the device (seeded), so the bytes differ from every other pool."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from tests._paged import DeviceBatch
+
+    if i == 0:
+        return DeviceBatch(base, device)
+    rng = np.random.Generator(np.random.PCG64(5000 + i))
+    order = rng.permutation(base.num_pages).astype(np.int32)
+    indptr, indices, last, keypos = workloads.csr_from_lengths(base.lengths, order)
+    db = DeviceBatch.__new__(DeviceBatch)
+    db.host = None
+    gen = torch.Generator(device=device)
+    gen.manual_seed(7000 + i)
+    shape = base.k_cache.shape
+    db.k_cache = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    db.v_cache = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    db.q = torch.randn(base.q.shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+    db.kv_indptr, db.kv_indices, db.kv_last_page_len = t(indptr), t(indices), t(last)
+    db.query_position_ids = t(base.query_position_ids)
+    db.cache_position = t(base.cache_position)
+    db.key_position_ids = t(keypos)
+    db.q_norm_weight = torch.from_numpy(base.q_norm_weight).to(device)
+    db.k_norm_weight = torch.from_numpy(base.k_norm_weight).to(device)
+    return db
+
+
+def time_calls(fn, sets, steps, warmup):
+    """Run fn(set) over the rotation; return (wall ms per step, mean per-launch event ms)."""
+    import torch
+
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(sets[i % len(sets)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return wall_ms, launch_ms
+
+
+def cpu_baseline_decode(base, alg_bytes_fn):
+    """The CPU oracle on the first rows of the same decode batch, single thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads
+
+    rows = list(range(4))
+    sub = workloads.PagedBatch(**{**base.__dict__})
+    sub_bytes = 0
+    with threadpool_limits(limits=1):
+        args, kwargs = base.oracle_args()
+        t0 = time.perf_counter()
+        oracle.paged_attention(*args, rows=rows, **kwargs)
+        dt = time.perf_counter() - t0
+    D = 128
+    L = base.lengths[rows]
+    sub_bytes = int(np.sum(L)) * base.num_kv_heads * D * 4 + len(rows) * base.num_q_heads * (D * 4 + 4)
+    del sub
+    return {"value": round(sub_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"rows {rows[0]}..{rows[-1]} of the B=32 decode batch (all 16 heads, "
+                      f"{int(np.sum(L))} keys), {dt:.1f} s, numpy with BLAS limited to 1 thread"}
+
+
+def profile_copy():
+    """A plain device copy of 1 GiB, for scaling FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--profile-copy", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="skip prefill and the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path: rows and heads shard across GPUs with no exchange, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.profile_copy:
+        profile_copy()
+        return
+
+    import numpy as np
+    import torch
+
+    import deterministic_paged_kv_amd as pa
+    import workloads
+    from tests._paged import DeviceBatch
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    print("[bench] building inputs", file=sys.stderr, flush=True)
+    base = workloads.qwen3_8b_decode(canary=False)
+    sets = [device_rotation(base, i, device) for i in range(ROTATIONS)]
+    plan = pa.Plan(16, 4, max_batch=32, max_q_len=1, max_pages_per_row=256, rms_eps=base.eps)
+    out = torch.empty_like(sets[0].q)
+    lse = torch.empty(out.shape[:3], dtype=torch.float32, device=device)
+    rep = pa.validate_metadata(plan, batch=32, q_len=1, num_pages=base.num_pages,
+                               kv_indptr=sets[0].kv_indptr, kv_indices=sets[0].kv_indices,
+                               kv_last_page_len=sets[0].kv_last_page_len, cache_position=sets[0].cache_position,
+                               query_position_ids=sets[0].query_position_ids,
+                               key_position_ids=sets[0].key_position_ids)
+    if rep["code"] != 0:
+        raise RuntimeError(f"metadata rejected: {rep}")
+
+    def step(db):
+        pa.decode(plan, *db.args(), out=out, lse=lse)
+
+    print("[bench] timing decode", file=sys.stderr, flush=True)
+    wall_ms, launch_ms = time_calls(step, sets, args.steps, args.warmup)
+    alg = decode_bytes(base)
+    value = alg / (wall_ms * 1e-3) / 1e9
+    achieved = alg / (launch_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_decode", "batch": 32, "q_len": 1, "num_q_heads": 16, "num_kv_heads": 4,
+                   "head_dim": 128, "page_size": 16, "kv_len": "U{512..4096}", "total_keys": int(np.sum(base.lengths)),
+                   "pool_pages": base.num_pages, "kv_pool_rotation": ROTATIONS, "split_kv": "disabled"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(alg),
+                     "kernel": "decode_kernel", "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_ms": round(launch_ms, 5)},
+    }
+
+    if not args.decode_only:
+        print("[bench] timing prefill", file=sys.stderr, flush=True)
+        pb = workloads.chunked_prefill(canary=False)
+        pdb = DeviceBatch(pb, device)
+        pplan = pa.Plan(32, 8, max_batch=4, max_q_len=512, max_pages_per_row=256, rms_eps=pb.eps)
+        pout = torch.empty_like(pdb.q)
+        plse = torch.empty(pout.shape[:3], dtype=torch.float32, device=device)
+        ws = torch.empty(pa.prefill_workspace_size(pplan, 4, 512, pb.nnz), dtype=torch.uint8, device=device)
+
+        def pstep(db):
+            pa.prefill(pplan, *db.args(), out=pout, lse=plse, workspace=ws)
+
+        psteps = max(20, args.steps // 4)
+        p_wall, p_launch = time_calls(pstep, [pdb], psteps, args.warmup)
+        flops = prefill_flops(pb)
+        result["prefill"] = {
+            "workload": "chunked_prefill", "batch": 4, "q_len": 512, "prefixes": [0, 1024, 2048, 3584],
+            "num_q_heads": 32, "num_kv_heads": 8, "steps": psteps, "ms_per_call": round(p_wall, 5),
+            "value": round(flops / (p_wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(flops / (p_launch * 1e-3) / 1e12, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (p_launch * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": "prologue_kernel + attend_kernel (whole call)",
+                         "algorithmic_flops_per_call": flops, "avg_call_ms": round(p_launch, 5)},
+        }
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = cpu_baseline_decode(base, decode_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

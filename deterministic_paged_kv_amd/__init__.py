@@ -1,0 +1,20 @@
+"""Deterministic, batch-invariant paged-KV GQA attention for AMD MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``include/pa.h`` (``libpa.so``, built in-tree by ``build.py``).  This package is
+the thin Python binding over it: :class:`Plan`, :func:`validate_metadata`,
+:func:`decode`, :func:`prefill`.  Importing it does not load the library; the
+first call does, and raises if it is not built.
+"""
+
+from .binding import (  # noqa: F401
+    PA_SPLIT_DISABLED,
+    PagedAttentionError,
+    Plan,
+    decode,
+    load,
+    prefill,
+    prefill_workspace_size,
+    status_string,
+    validate_metadata,
+)

@@ -1,0 +1,296 @@
+// Host side of the C ABI declared in include/pa.h: argument checks, the plan (with its RoPE
+// table), validation and kernel launches.  pa_decode / pa_prefill only check host scalars
+// and enqueue work: no allocation, no synchronisation, no device reads.
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+using namespace pa;
+
+bool plan_ok(pa_plan_t plan) { return plan != nullptr && plan->d_rope != nullptr; }
+
+// The device a plan was made on must be current: its table lives there.
+pa_status check_device(pa_plan_t plan) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  return dev == plan->device ? PA_OK : PA_ERR_INVALID_ARGUMENT;
+}
+
+// cos/sin of the RoPE angles: frequency i of position p has angle (p / scale) * theta^(-2i/D),
+// formed and evaluated in float64 and rounded once to float32 ("WS2 PR7 Fused Attention
+// Backend Alignment", section "FlashInfer RoPE Fusion": Llama RoPE, theta 1e6, scale 1.0,
+// rotary_dim = head_dim).  Row p holds cos[0..63] then sin[0..63].
+std::vector<float> rope_table(int rows, double theta, double scale) {
+  std::vector<double> inv_freq(kHalfDim);
+  for (int i = 0; i < kHalfDim; ++i) inv_freq[i] = std::pow(theta, -(2.0 * i) / kHeadDim);
+  std::vector<float> t((size_t)rows * kHeadDim);
+  for (int p = 0; p < rows; ++p) {
+    const double pos = (double)p / scale;
+    float* row = t.data() + (size_t)p * kHeadDim;
+    for (int i = 0; i < kHalfDim; ++i) {
+      const double a = pos * inv_freq[i];
+      row[i] = (float)std::cos(a);
+      row[kHalfDim + i] = (float)std::sin(a);
+    }
+  }
+  return t;
+}
+
+// Host-scalar checks shared by pa_decode and pa_prefill.
+pa_status check_launch(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
+                       const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                       const int32_t* query_position_ids, const void* q, const void* k_cache,
+                       const void* v_cache, const void* out, const float* lse) {
+  if (!plan_ok(plan)) return PA_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || q_len < 1 || num_pages < 1 || num_indices < 0) return PA_ERR_INVALID_ARGUMENT;
+  if (batch > plan->max_batch || q_len > plan->max_q_len) return PA_ERR_CAPACITY;
+  if (batch == 0) return PA_OK;
+  if (!kv_indptr || !kv_last_page_len || !query_position_ids || !q || !k_cache || !v_cache || !out || !lse)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_indices > 0 && !kv_indices) return PA_ERR_INVALID_ARGUMENT;
+  return check_device(plan);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY";
+    case PA_ERR_HEAD_RATIO: return "PA_ERR_HEAD_RATIO";
+    case PA_ERR_INDPTR: return "PA_ERR_INDPTR";
+    case PA_ERR_PAGE_OOB: return "PA_ERR_PAGE_OOB";
+    case PA_ERR_DUPLICATE_PAGE: return "PA_ERR_DUPLICATE_PAGE";
+    case PA_ERR_LAST_PAGE_LEN: return "PA_ERR_LAST_PAGE_LEN";
+    case PA_ERR_KEY_POSITION: return "PA_ERR_KEY_POSITION";
+    case PA_ERR_QUERY_POSITION: return "PA_ERR_QUERY_POSITION";
+    case PA_ERR_CACHE_POSITION: return "PA_ERR_CACHE_POSITION";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                  int32_t max_batch, int32_t max_q_len, int32_t max_pages_per_row, float rope_theta,
+                  float rope_scale, float rms_eps, int32_t split_policy, pa_plan_t* plan_out) {
+  if (!plan_out) return PA_ERR_INVALID_ARGUMENT;
+  if (num_q_heads < 1 || num_kv_heads < 1 || max_batch < 1 || max_q_len < 1 || max_pages_per_row < 1)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!(rms_eps > 0.0f) || !std::isfinite(rms_eps)) return PA_ERR_INVALID_ARGUMENT;
+  if (head_dim != kHeadDim || page_size != kPageSize) return PA_ERR_UNSUPPORTED;
+  if (rope_theta != 1.0e6f || rope_scale != 1.0f) return PA_ERR_UNSUPPORTED;
+  if (split_policy != PA_SPLIT_DISABLED) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_HEAD_RATIO;
+  // positions stay int32 and the table below fits in memory
+  if ((long long)max_pages_per_row * kPageSize + 1 > (1LL << 24)) return PA_ERR_CAPACITY;
+
+  pa_plan_s* p = new (std::nothrow) pa_plan_s();
+  if (!p) return PA_ERR_HIP;
+  p->num_q_heads = num_q_heads;
+  p->num_kv_heads = num_kv_heads;
+  p->group = num_q_heads / num_kv_heads;
+  p->max_batch = max_batch;
+  p->max_q_len = max_q_len;
+  p->max_pages_per_row = max_pages_per_row;
+  p->table_rows = max_pages_per_row * kPageSize + 1;
+  p->rope_theta = rope_theta;
+  p->rope_scale = rope_scale;
+  p->rms_eps = rms_eps;
+  p->split_policy = split_policy;
+  p->d_rope = nullptr;
+  if (hipGetDevice(&p->device) != hipSuccess) { delete p; return PA_ERR_HIP; }
+  const std::vector<float> table = rope_table(p->table_rows, (double)rope_theta, (double)rope_scale);
+  const size_t bytes = table.size() * sizeof(float);
+  if (hipMalloc(&p->d_rope, bytes) != hipSuccess) { delete p; return PA_ERR_HIP; }
+  if (hipMemcpy(p->d_rope, table.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p->d_rope);
+    delete p;
+    return PA_ERR_HIP;
+  }
+  *plan_out = p;
+  return PA_OK;
+}
+
+pa_status pa_plan_destroy(pa_plan_t plan) {
+  if (!plan) return PA_OK;
+  pa_status st = PA_OK;
+  if (plan->d_rope && hipFree(plan->d_rope) != hipSuccess) st = PA_ERR_HIP;
+  delete plan;
+  return st;
+}
+
+pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
+                               int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
+                               const int32_t* kv_last_page_len, const int32_t* cache_position,
+                               const int32_t* query_position_ids, const int32_t* key_position_ids,
+                               void* stream, pa_validation_report* report) {
+  pa_validation_report rep = {PA_OK, -1, -1, -1};
+  auto finish = [&](pa_status st) {
+    rep.code = st;
+    if (report) *report = rep;
+    return st;
+  };
+  if (!plan_ok(plan)) return finish(PA_ERR_INVALID_ARGUMENT);
+  if (batch < 0 || q_len < 1 || num_pages < 1 || num_indices < 0) return finish(PA_ERR_INVALID_ARGUMENT);
+  if (batch > plan->max_batch || q_len > plan->max_q_len) return finish(PA_ERR_CAPACITY);
+  if (!kv_indptr || !kv_last_page_len || !cache_position || !query_position_ids || !key_position_ids ||
+      (num_indices > 0 && !kv_indices))
+    return finish(PA_ERR_INVALID_ARGUMENT);
+  if (check_device(plan) != PA_OK) return finish(PA_ERR_INVALID_ARGUMENT);
+  hipStream_t s = (hipStream_t)stream;
+
+  void* scratch = nullptr;
+  const size_t bytes = sizeof(unsigned long long) + (size_t)num_pages * sizeof(int32_t);
+  if (hipMalloc(&scratch, bytes) != hipSuccess) return finish(PA_ERR_HIP);
+  ValidateParams vp;
+  vp.batch = batch;
+  vp.q_len = q_len;
+  vp.num_pages = num_pages;
+  vp.num_indices = num_indices;
+  vp.max_pages_per_row = plan->max_pages_per_row;
+  vp.indptr = kv_indptr;
+  vp.indices = kv_indices;
+  vp.last_page_len = kv_last_page_len;
+  vp.cache_position = cache_position;
+  vp.qpos = query_position_ids;
+  vp.kpos = key_position_ids;
+  vp.report = (unsigned long long*)scratch;
+  vp.page_count = (int32_t*)((char*)scratch + sizeof(unsigned long long));
+  unsigned long long key = ~0ull;
+  hipError_t e = launch_validate(vp, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&key, vp.report, sizeof(key), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  pa_status st = PA_OK;
+  if (e != hipSuccess) {
+    st = PA_ERR_HIP;
+  } else if (key != ~0ull) {
+    static const pa_status by_rank[] = {PA_OK, PA_ERR_INDPTR, PA_ERR_CAPACITY, PA_ERR_PAGE_OOB,
+                                        PA_ERR_DUPLICATE_PAGE, PA_ERR_LAST_PAGE_LEN, PA_ERR_KEY_POSITION,
+                                        PA_ERR_QUERY_POSITION, PA_ERR_CACHE_POSITION};
+    const unsigned rank = (unsigned)(key >> 40);
+    const long long index = (long long)(key & ((1ull << 40) - 1));
+    st = rank < sizeof(by_rank) / sizeof(by_rank[0]) ? by_rank[rank] : PA_ERR_HIP;
+    rep.index = index;
+    // the row and the offending value, read back for the report
+    const int32_t* src = nullptr;
+    switch (st) {
+      case PA_ERR_INDPTR: src = kv_indptr; rep.row = (int32_t)std::max(0LL, index - 1); break;
+      case PA_ERR_CAPACITY: case PA_ERR_LAST_PAGE_LEN: src = kv_last_page_len; rep.row = (int32_t)index; break;
+      case PA_ERR_PAGE_OOB: case PA_ERR_DUPLICATE_PAGE: src = kv_indices; break;
+      case PA_ERR_KEY_POSITION: src = key_position_ids; break;
+      case PA_ERR_QUERY_POSITION: src = query_position_ids; rep.row = (int32_t)(index / q_len); break;
+      case PA_ERR_CACHE_POSITION: src = cache_position; rep.row = (int32_t)(index / q_len); break;
+      default: break;
+    }
+    if (st == PA_ERR_CAPACITY) {
+      int32_t pr[2];
+      if (hipMemcpy(pr, kv_indptr + index, sizeof(pr), hipMemcpyDeviceToHost) == hipSuccess)
+        rep.value = pr[1] - pr[0];
+    } else if (src) {
+      int32_t v = 0;
+      if (hipMemcpy(&v, src + index, sizeof(v), hipMemcpyDeviceToHost) == hipSuccess) rep.value = v;
+    }
+    if (st == PA_ERR_PAGE_OOB || st == PA_ERR_DUPLICATE_PAGE || st == PA_ERR_KEY_POSITION) {
+      // row owning the element: indptr is valid here (indptr violations rank first)
+      std::vector<int32_t> indptr(batch + 1);
+      if (hipMemcpy(indptr.data(), kv_indptr, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost) == hipSuccess) {
+        const long long page_elem = st == PA_ERR_KEY_POSITION ? index / kPageSize : index;
+        const auto it = std::upper_bound(indptr.begin(), indptr.end(), (int32_t)page_elem);
+        rep.row = (int32_t)(it - indptr.begin()) - 1;
+      }
+    }
+  }
+  if (hipFree(scratch) != hipSuccess && st == PA_OK) st = PA_ERR_HIP;
+  return finish(st);
+}
+
+pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
+                    const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                    const int32_t* query_position_ids, const void* q, const void* k_cache, const void* v_cache,
+                    const float* q_norm_weight, const float* k_norm_weight, void* out, float* lse,
+                    void* stream) {
+  pa_status st = check_launch(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices,
+                              kv_last_page_len, query_position_ids, q, k_cache, v_cache, out, lse);
+  if (st != PA_OK || batch == 0) return st;
+  if (q_len != 1) return PA_ERR_INVALID_ARGUMENT;
+  DecodeParams p;
+  p.batch = batch;
+  p.num_q_heads = plan->num_q_heads;
+  p.num_kv_heads = plan->num_kv_heads;
+  p.group = plan->group;
+  p.num_pages = num_pages;
+  p.num_indices = num_indices;
+  p.max_pages_per_row = plan->max_pages_per_row;
+  p.table_rows = plan->table_rows;
+  p.indptr = kv_indptr;
+  p.indices = kv_indices;
+  p.last_page_len = kv_last_page_len;
+  p.qpos = query_position_ids;
+  p.q = (const uint16_t*)q;
+  p.k_cache = (const uint16_t*)k_cache;
+  p.v_cache = (const uint16_t*)v_cache;
+  p.q_norm = q_norm_weight;
+  p.k_norm = k_norm_weight;
+  p.out = (uint16_t*)out;
+  p.lse = lse;
+  p.rope = plan->d_rope;
+  p.eps = plan->rms_eps;
+  return launch_decode(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_indices,
+                                    size_t* bytes) {
+  if (!plan_ok(plan) || !bytes || batch < 0 || q_len < 1 || num_indices < 0) return PA_ERR_INVALID_ARGUMENT;
+  if (batch > plan->max_batch || q_len > plan->max_q_len) return PA_ERR_CAPACITY;
+  *bytes = prefill_workspace_bytes(plan->num_q_heads, plan->num_kv_heads, batch, q_len, num_indices);
+  return PA_OK;
+}
+
+pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
+                     const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                     const int32_t* query_position_ids, const void* q, const void* k_cache, const void* v_cache,
+                     const float* q_norm_weight, const float* k_norm_weight, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = check_launch(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices,
+                              kv_last_page_len, query_position_ids, q, k_cache, v_cache, out, lse);
+  if (st != PA_OK || batch == 0) return st;
+  const size_t need = prefill_workspace_bytes(plan->num_q_heads, plan->num_kv_heads, batch, q_len, num_indices);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  PrefillParams p;
+  p.batch = batch;
+  p.q_len = q_len;
+  p.num_q_heads = plan->num_q_heads;
+  p.num_kv_heads = plan->num_kv_heads;
+  p.group = plan->group;
+  p.num_pages = num_pages;
+  p.num_indices = num_indices;
+  p.max_pages_per_row = plan->max_pages_per_row;
+  p.table_rows = plan->table_rows;
+  p.indptr = kv_indptr;
+  p.indices = kv_indices;
+  p.last_page_len = kv_last_page_len;
+  p.qpos = query_position_ids;
+  p.q = (const uint16_t*)q;
+  p.k_cache = (const uint16_t*)k_cache;
+  p.v_cache = (const uint16_t*)v_cache;
+  p.q_norm = q_norm_weight;
+  p.k_norm = k_norm_weight;
+  p.out = (uint16_t*)out;
+  p.lse = lse;
+  p.rope = plan->d_rope;
+  p.eps = plan->rms_eps;
+  p.workspace = workspace;
+  return launch_prefill(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) deterministic paged-KV GQA attention library.
+ *
+ * The library computes, for every row b, query head h and query i,
+ *
+ *   q^  = bf16( RoPE( RMSNorm(q) * w_q , query_position_ids[b][i] ) )
+ *   k^j = bf16( RoPE( RMSNorm(k_j) * w_k , j ) )            j = logical key index of row b
+ *   s_j = (q^ . k^j) / sqrt(head_dim)                        for keys with j <= query position
+ *   lse = log( sum_j exp(s_j) )                              natural log, FP32
+ *   out = bf16( sum_j exp(s_j - lse) * v_j )
+ *
+ * with FP32 accumulation and a reduction order that depends only on the row's own
+ * length: never on the batch it runs in, on the plan's capacity ("plan width") or on
+ * where its pages sit in the pool.  Sources (web pages, cited by title and section):
+ *
+ *   [PR279]  "[WS2][PR7][Attention] Add FlashInfer RoPE-fused paged attention scaffold",
+ *            section "Scope" (boundary table: logical K/V order materialised before
+ *            arithmetic, Split-KV disabled, FP32 attention-domain LSE, GQA packing from
+ *            the head layout, same post-RoPE boundary on both sides, Q/K RMSNorm).
+ *   [PR7]    "WS2 PR7 Fused Attention Backend Alignment", sections "Original PR7
+ *            Requirements" (LSE shaped [B, Hq, Sq]; metadata validated before execution),
+ *            "Current Implementation" (validation steps; out [B, Hq, Sq, D]),
+ *            "FlashInfer RoPE Fusion" (Llama rotate-half RoPE, theta 1e6, scale 1.0,
+ *            rotary_dim = head_dim; pre-RoPE Q and K cache; cache_position ==
+ *            query_position_ids; trailing contiguous query positions),
+ *            "Split-KV Policy" (disabled / fixed:<N> / auto, auto rejected).
+ *   [PR162]  "flashinfer_fa2 backend for NVIDIA Ada (SM89)", sections "Summary" (BF16,
+ *            page size 16, head_dim 128, NHD), "Design notes" (CSR indptr / compact
+ *            indices / last_page_len; Split-KV disabled so a row's result does not depend
+ *            on plan width or batch), "Code audit" (empty rows have last_page_len 1;
+ *            unsupported head ratios and row-count mismatches are rejected).
+ *   [XCFG]   "WS2 Attention Cross-Configuration Integration", sections "H100 Attention
+ *            input and projection boundary" (order: Q/K RMSNorm, then RoPE) and "Fail
+ *            closed, never substitute" (FP32 accumulation, downcast only at the final
+ *            write, unsupported requests are errors).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are HIP device addresses of caller-owned buffers; the library
+ *     keeps no pointer after a call returns.  `stream` is a hipStream_t (NULL = the
+ *     default stream).
+ *   - BF16 tensors are raw 16-bit patterns.  All tensors are dense, row-major, with the
+ *     layouts stated below.
+ *   - Errors are negative pa_status codes; nothing falls back to another algorithm.
+ *   - pa_decode / pa_prefill never allocate, never synchronise and never read device
+ *     memory from the host, so they may be recorded into a HIP graph.  They check host
+ *     scalars only.  The kernels additionally bounds-check every page index, row length
+ *     and position they read; a row whose metadata is out of range gets NaN in out and
+ *     lse (the launch still succeeds).  Call pa_validate_metadata first to get a precise
+ *     error instead.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = -1,  /* null pointer, non-positive size, bad plan handle          */
+  PA_ERR_UNSUPPORTED = -2,       /* head_dim != 128, page_size != 16, theta != 1e6,
+                                    rope_scale != 1, unknown or "auto" split policy            */
+  PA_ERR_CAPACITY = -3,          /* batch, q_len or pages per row beyond the plan            */
+  PA_ERR_HEAD_RATIO = -4,        /* Hq not a positive multiple of Hkv, or Hq/Hkv > 16         */
+  PA_ERR_INDPTR = -5,            /* indptr[0] != 0, decreasing, or indptr[B] != num_indices   */
+  PA_ERR_PAGE_OOB = -6,          /* a page index outside [0, num_pages)                      */
+  PA_ERR_DUPLICATE_PAGE = -7,    /* a physical page used twice in the batch                  */
+  PA_ERR_LAST_PAGE_LEN = -8,     /* outside [1, page_size], or != 1 for a row with no pages  */
+  PA_ERR_KEY_POSITION = -9,      /* key_position_ids not 0, 1, ..., L_b - 1 in logical order */
+  PA_ERR_QUERY_POSITION = -10,   /* query positions not contiguous, negative, or not ending
+                                    at L_b - 1 or L_b                                        */
+  PA_ERR_CACHE_POSITION = -11,   /* cache_position != query_position_ids                     */
+  PA_ERR_WORKSPACE = -12,        /* prefill workspace missing or too small                   */
+  PA_ERR_HIP = -13               /* a HIP runtime call failed                                */
+};
+
+/* Split-KV policy ([PR7] "Split-KV Policy").  Only PA_SPLIT_DISABLED is implemented:
+ * one pass over each row's keys in a fixed order.  PA_SPLIT_FIXED is reserved and
+ * returns PA_ERR_UNSUPPORTED; PA_SPLIT_AUTO is rejected because it makes a row's
+ * reduction depend on the batch. */
+enum { PA_SPLIT_DISABLED = 0, PA_SPLIT_FIXED = 1, PA_SPLIT_AUTO = 2 };
+
+typedef struct pa_plan_s* pa_plan_t;
+
+/* Result of pa_validate_metadata: the first violated rule (rules are checked in the
+ * order of the status codes above, from PA_ERR_INDPTR down) and, within that rule, the
+ * lowest offending element. */
+typedef struct {
+  pa_status code;   /* PA_OK or the violated rule                                   */
+  int32_t row;      /* batch row of the violation, -1 if not row-specific            */
+  int64_t index;    /* element index in the offending array, -1 if not applicable   */
+  int64_t value;    /* the offending value (or the expected one for count checks)    */
+} pa_validation_report;
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/* Create a plan: fixed shapes, capacities and the RoPE cos/sin table.
+ *   num_q_heads, num_kv_heads  Hq, Hkv of one GPU's head share; Hq % Hkv == 0, Hq/Hkv <= 16
+ *                              ([PR279] "Scope": GQA packing fixed from the head layout).
+ *   head_dim, page_size        must be 128 and 16 ([PR162] "Summary").
+ *   max_batch, max_q_len       capacity for B and Sq.
+ *   max_pages_per_row          capacity for pages per row.  Capacity only: it never
+ *                              changes the arithmetic ([PR162] "Design notes").
+ *   rope_theta, rope_scale     must be 1e6 and 1.0; rms_eps > 0 ([PR7] "FlashInfer RoPE
+ *                              Fusion").
+ *   split_policy               PA_SPLIT_DISABLED.
+ * Allocates device memory for the cos/sin table (max_pages_per_row * page_size + 1
+ * positions, 512 bytes each) and synchronises the current device once.  The plan is
+ * immutable afterwards and may serve several streams at once.  *plan_out is written
+ * only on success. */
+pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                  int32_t max_batch, int32_t max_q_len, int32_t max_pages_per_row,
+                  float rope_theta, float rope_scale, float rms_eps, int32_t split_policy,
+                  pa_plan_t* plan_out);
+
+/* Free a plan and its device table.  NULL is accepted.  No call using the plan may be in
+ * flight on any stream. */
+pa_status pa_plan_destroy(pa_plan_t plan);
+
+/* Check the paged-KV metadata on the device before execution ([PR7] "Original PR7
+ * Requirements": page table, cache_position, query_position_ids, key_position_ids and
+ * logical token order are validated before execution; "Current Implementation": page
+ * bounds, logical order, key positions, duplicate pages, non-canonical inactive rows,
+ * cache_position == query_position_ids, trailing query positions; [PR162] "Code audit":
+ * empty rows carry last_page_len 1).
+ *   batch, q_len               B and Sq (host scalars, checked against the plan).
+ *   num_pages                  pages in the K/V pool.
+ *   num_indices                nnz, the length of kv_indices.
+ *   kv_indptr        int32 [B+1]       row b owns kv_indices[kv_indptr[b] .. kv_indptr[b+1]).
+ *   kv_indices       int32 [nnz]       physical page ids, logical page order.
+ *   kv_last_page_len int32 [B]         keys in each row's last page.
+ *   cache_position, query_position_ids int32 [B, Sq].
+ *   key_position_ids int32 [nnz * 16]  logical key j of row b at kv_indptr[b] * 16 + j;
+ *                                      entries past a row's length are ignored.
+ * Launches validation kernels on `stream`, copies a small report back and synchronises
+ * `stream`; allocates and frees a scratch buffer of num_pages * 4 bytes.  Returns the
+ * report's code (PA_OK if every rule holds); `report` (optional) receives the details. */
+pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
+                               int32_t num_indices, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                               const int32_t* cache_position, const int32_t* query_position_ids,
+                               const int32_t* key_position_ids, void* stream,
+                               pa_validation_report* report);
+
+/* Paged decode (Sq = 1): one fused pass per (row, KV head) that gathers the row's pages in
+ * logical order, applies RMSNorm + RoPE + BF16 rounding to q and to every key, and runs
+ * the FP32 online softmax and PV product with no Split-KV ([PR279] "Scope"; [PR7]
+ * "FlashInfer RoPE Fusion", "Split-KV Policy"; [PR162] "Design notes").
+ *   q                bf16 [B, Hq, 1, 128]   pre-norm, pre-RoPE.
+ *   k_cache, v_cache bf16 [num_pages, 16, Hkv, 128] (NHD); K pre-norm, pre-RoPE.
+ *   q_norm_weight, k_norm_weight  fp32 [128], or NULL to skip that RMSNorm.
+ *   query_position_ids int32 [B, 1]; key positions are the logical indices 0..L_b-1.
+ *   out              bf16 [B, Hq, 1, 128]   written.
+ *   lse              fp32 [B, Hq, 1]        written; natural log of the sum of
+ *                                           exp(scaled scores) ([PR7] "Original PR7
+ *                                           Requirements").  Rows with no keys get
+ *                                           out = 0 and lse = -inf.
+ * Asynchronous on `stream`; requires q_len == 1 and batch <= plan capacity. */
+pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
+                    int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
+                    const int32_t* kv_last_page_len, const int32_t* query_position_ids,
+                    const void* q, const void* k_cache, const void* v_cache,
+                    const float* q_norm_weight, const float* k_norm_weight,
+                    void* out, float* lse, void* stream);
+
+/* Workspace bytes pa_prefill needs for these sizes (host arithmetic only). */
+pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len,
+                                    int32_t num_indices, size_t* bytes);
+
+/* Chunked paged prefill: Sq >= 1 trailing queries per row attend causally (key j visible
+ * to the query at position p iff j <= p, on logical positions) to the row's cached keys,
+ * which include the chunk's own keys ([PR7] "Current Implementation", "FlashInfer RoPE
+ * Fusion").  Same arguments and layouts as pa_decode with Sq = q_len, plus a caller-owned
+ * device workspace of at least pa_prefill_workspace_size() bytes that holds the
+ * normalised, rotated BF16 q^ and k^ between the two kernels of the call.  Asynchronous
+ * on `stream`.  Concurrent calls need separate workspaces. */
+pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
+                     int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
+                     const int32_t* kv_last_page_len, const int32_t* query_position_ids,
+                     const void* q, const void* k_cache, const void* v_cache,
+                     const float* q_norm_weight, const float* k_norm_weight,
+                     void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every symbol include/pa.h declares, and rejects bad host
+arguments before touching the GPU.  CPU only: nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from deterministic_paged_kv_amd import binding
+
+    return binding.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pa_plan", "pa_plan_destroy", "pa_validate_metadata", "pa_decode", "pa_prefill",
+                     "pa_prefill_workspace_size", "pa_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    from deterministic_paged_kv_amd import binding
+
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in binding.SIGNATURES, name
+
+
+def test_status_strings(lib):
+    from deterministic_paged_kv_amd import binding
+
+    for code, name in binding.STATUS.items():
+        assert lib.pa_status_string(code).decode() == name
+    assert lib.pa_status_string(12345).decode() == "PA_ERR_UNKNOWN"
+
+
+def _plan(lib, hq=16, hkv=4, d=128, ps=16, mb=1, mq=1, mp=1, theta=1e6, scale=1.0, eps=1e-6, split=0):
+    h = ctypes.c_void_p()
+    st = lib.pa_plan(hq, hkv, d, ps, mb, mq, mp, theta, scale, eps, split, ctypes.byref(h))
+    assert h.value is None  # written only on success; none of these cases succeed
+    return st
+
+
+def test_plan_fails_closed_on_host_arguments(lib):
+    assert _plan(lib, d=64) == -2
+    assert _plan(lib, ps=32) == -2
+    assert _plan(lib, theta=1e4) == -2
+    assert _plan(lib, scale=2.0) == -2
+    assert _plan(lib, split=1) == -2          # fixed split: reserved
+    assert _plan(lib, split=2) == -2          # auto split: rejected
+    assert _plan(lib, hq=16, hkv=3) == -4     # head ratio
+    assert _plan(lib, hq=34, hkv=2) == -4     # group of 17 > 16
+    assert _plan(lib, hq=0) == -1
+    assert _plan(lib, mb=0) == -1
+    assert _plan(lib, eps=0.0) == -1
+    assert _plan(lib, mp=1 << 21) == -3       # positions past 2^24
+    assert lib.pa_plan(16, 4, 128, 16, 1, 1, 1, 1e6, 1.0, 1e-6, 0, None) == -1
+
+
+def test_calls_without_a_plan_fail_closed(lib):
+    null = None
+    assert lib.pa_decode(null, 1, 1, 1, 0, *([null] * 11), null) == -1
+    assert lib.pa_prefill(null, 1, 1, 1, 0, *([null] * 12), 0, null) == -1
+    from deterministic_paged_kv_amd import binding
+
+    rep = binding.ValidationReport()
+    assert lib.pa_validate_metadata(null, 1, 1, 1, 0, *([null] * 7), ctypes.byref(rep)) == -1
+    assert rep.code == -1
+    n = ctypes.c_size_t()
+    assert lib.pa_prefill_workspace_size(null, 1, 1, 0, ctypes.byref(n)) == -1
+    assert lib.pa_plan_destroy(null) == 0
+
+
+def test_product_path_does_not_import_the_oracle():
+    import subprocess
+    import sys
+
+    code = ("import sys, deterministic_paged_kv_amd as d; d.load(); "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "deterministic_paged_kv_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f

@@ -1,0 +1,131 @@
+"""pa_decode on the GPU against the CPU oracle, and its bitwise invariances."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _paged import DeviceBatch, assert_parity, make_plan, run
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_ref(b, rows=None, q_heads=None):
+    args, kwargs = b.oracle_args()
+    return oracle.paged_attention(*args, rows=rows, q_heads=q_heads, **kwargs)
+
+
+def check_full(b, label, plan=None):
+    db = DeviceBatch(b)
+    plan = plan or make_plan(b)
+    out, lse = run("decode", plan, db)
+    ref_out, ref_lse = oracle_ref(b)
+    assert_parity(out, lse, ref_out, ref_lse, label)
+    return out, lse
+
+
+def test_tiny_decode_parity(gpu):
+    """B=2, Hq=8, Hkv=2, 128 keys per row, pages drawn from a 64-page pool; NaN canaries elsewhere."""
+    check_full(workloads.tiny_decode(), "tiny decode")
+
+
+def test_qwen3_8b_decode_parity_sampled(gpu):
+    """Full Qwen3-8B per-GPU shape (B=32, Hq=16, Hkv=4, L ~ U[512, 4096]); oracle on sampled rows."""
+    b = workloads.qwen3_8b_decode()
+    db = DeviceBatch(b)
+    plan = make_plan(b, max_pages_per_row=256)
+    out, lse = run("decode", plan, db)
+    rows = [0, 5, 17, 31, int(np.argmax(b.lengths)), int(np.argmin(b.lengths))]
+    ref_out, ref_lse = oracle_ref(b, rows=rows)
+    assert_parity(out[rows], lse[rows], ref_out, ref_lse, "qwen3-8b decode rows %s" % rows)
+    # every row finite
+    assert np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("lengths", [
+    [0, 1, 15, 16, 17, 33, 130, 255],
+    [2, 0, 0, 31],
+    [4096, 3],
+])
+def test_decode_ragged_and_empty_rows(gpu, lengths):
+    b = workloads.make_batch(11, lengths, q_len=1, num_q_heads=8, num_kv_heads=2,
+                             num_pages=max(64, 2 * sum((L + 15) // 16 for L in lengths)))
+    check_full(b, f"ragged {lengths}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (16, 2), (32, 2), (32, 8)])
+def test_decode_group_sizes(gpu, hq, hkv):
+    b = workloads.make_batch(12, [77, 300, 16], q_len=1, num_q_heads=hq, num_kv_heads=hkv, num_pages=128)
+    check_full(b, f"Hq={hq} Hkv={hkv}")
+
+
+def test_decode_without_norm(gpu):
+    b = workloads.make_batch(13, [100, 257], q_len=1, num_q_heads=8, num_kv_heads=2, num_pages=64, norm=False)
+    check_full(b, "no RMSNorm")
+
+
+def test_decode_query_at_last_key(gpu):
+    """Query position L-1 (the query's own key is the last cached key)."""
+    b = workloads.make_batch(14, [50, 129, 1], q_len=1, num_q_heads=8, num_kv_heads=2, num_pages=64)
+    b.query_position_ids[:] = (b.lengths - 1)[:, None]
+    b.cache_position[:] = b.query_position_ids
+    check_full(b, "query at L-1")
+
+
+def test_decode_bitwise_repeat_and_page_permutation(gpu):
+    b = workloads.make_batch(15, [700, 1500, 33, 2048], q_len=1, num_q_heads=16, num_kv_heads=4, num_pages=512)
+    plan = make_plan(b)
+    db = DeviceBatch(b)
+    first = run("decode", plan, db)
+    for _ in range(5):
+        again = run("decode", plan, db)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1].view(np.uint32), again[1].view(np.uint32))
+    perm = run("decode", plan, DeviceBatch(workloads.permute_pages(b, 5)))
+    assert np.array_equal(first[0], perm[0])
+    assert np.array_equal(first[1].view(np.uint32), perm[1].view(np.uint32))
+
+
+def test_batch_and_plan_width_invariance(gpu):
+    """The 1,500-token row (Hq=32, Hkv=8): alone under 128- and 256-page plans, as row 3 of a batch of
+    8 under 512- and 1024-page plans, and alone with its pages permuted: bitwise equal out and LSE,
+    each run repeated 10 times; and within tolerance of the oracle."""
+    alone = workloads.invariance_batch(alone=True)
+    full = workloads.invariance_batch(alone=False)
+    r = workloads.INVARIANCE_ROW_INDEX
+    results = []
+    db_alone = DeviceBatch(alone)
+    db_full = DeviceBatch(full)
+    db_perm = DeviceBatch(workloads.permute_pages(alone, 77))
+    for width in (128, 256):
+        plan = make_plan(alone, max_pages_per_row=width)
+        for _ in range(10):
+            o, l = run("decode", plan, db_alone)
+            results.append((f"alone w={width}", o[0], l[0]))
+        for _ in range(2):
+            o, l = run("decode", plan, db_perm)
+            results.append((f"permuted w={width}", o[0], l[0]))
+    for width in (512, 1024):
+        plan = make_plan(full, max_pages_per_row=width, max_batch=8)
+        for _ in range(10):
+            o, l = run("decode", plan, db_full)
+            results.append((f"batch8 w={width}", o[r], l[r]))
+    ref_label, ref_o, ref_l = results[0]
+    for label, o, l in results[1:]:
+        assert np.array_equal(o, ref_o), f"out differs: {label} vs {ref_label}"
+        assert np.array_equal(l.view(np.uint32), ref_l.view(np.uint32)), f"lse differs: {label} vs {ref_label}"
+    ref_out, ref_lse = oracle_ref(alone)
+    assert_parity(ref_o[None], ref_l[None], ref_out, ref_lse, "1500-token row")
+
+
+@pytest.mark.parametrize("batch,length", [(1, 131072), (2, 32768)])
+def test_long_context_decode_sampled(gpu, batch, length):
+    """Long-context low-batch decode (Hq=32, Hkv=8): oracle on one row and two heads per KV group edge."""
+    pages = batch * length // 16
+    b = workloads.long_decode(batch, length, num_pages=pages + 512)
+    db = DeviceBatch(b)
+    plan = make_plan(b, max_pages_per_row=length // 16)
+    out, lse = run("decode", plan, db)
+    heads = [0, 3, 31]
+    ref_out, ref_lse = oracle_ref(b, rows=[batch - 1], q_heads=heads)
+    assert_parity(out[[batch - 1]][:, heads], lse[[batch - 1]][:, heads], ref_out, ref_lse,
+                  f"long decode B={batch} L={length}")
