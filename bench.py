@@ -216,8 +216,14 @@ def main():
     def step(db):
         pa.decode(plan, *db.args(), out=out, lse=lse)
 
+    ws = pa.decode_workspace(plan, 32, device=device)
+
+    def step_multi(db):
+        pa.decode(plan, *db.args(), out=out, lse=lse, workspace=ws)
+
     print("[bench] timing decode", file=sys.stderr, flush=True)
     wall_ms, launch_ms = time_calls(step, sets, args.steps, args.warmup)
+    mc_wall_ms, mc_launch_ms = time_calls(step_multi, sets, args.steps, args.warmup)
     alg = decode_bytes(base)
     value = alg / (wall_ms * 1e-3) / 1e9
     achieved = alg / (launch_ms * 1e-3) / 1e9
@@ -239,8 +245,14 @@ def main():
                    "pool_pages": base.num_pages, "kv_pool_rotation": ROTATIONS, "split_kv": "disabled"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(alg),
-                     "kernel": "decode_kernel", "algorithmic_bytes_per_launch": alg,
+                     "kernel": "decode_unit_kernel", "algorithmic_bytes_per_launch": alg,
                      "avg_launch_ms": round(launch_ms, 5)},
+        # the same reduction tree with each of a row's 8 page streams on its own compute unit:
+        # bit-identical results (tested), opt-in through a workspace
+        "decode_multi_cu": {"value": round(alg / (mc_wall_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                            "ms_per_step": round(mc_wall_ms, 5), "kernel": "decode_stream_kernel",
+                            "avg_launch_ms": round(mc_launch_ms, 5),
+                            "frac": round(alg / (mc_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
 
     if not args.decode_only:

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     PagedAttentionError,
     Plan,
     decode,
+    decode_workspace,
+    decode_workspace_size,
     load,
     prefill,
     prefill_workspace_size,

@@ -34,7 +34,8 @@ SIGNATURES = {
     "pa_plan_destroy": (_i32, [_p]),
     "pa_validate_metadata": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                                     ctypes.POINTER(ValidationReport)]),
-    "pa_decode": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "pa_decode": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "pa_decode_workspace_size": (_i32, [_p, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill_workspace_size": (_i32, [_p, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
 }
@@ -186,9 +187,25 @@ def validate_metadata(plan: Plan, *, batch: int, q_len: int, num_pages: int, kv_
             "index": int(rep.index), "value": int(rep.value)}
 
 
+def decode_workspace_size(plan: Plan, batch: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().pa_decode_workspace_size(plan.handle, batch, ctypes.byref(n)), "pa_decode_workspace_size")
+    return int(n.value)
+
+
+def decode_workspace(plan: Plan, batch: int, device="cuda"):
+    """A zeroed workspace for pa_decode's multi-compute-unit schedule (reusable across calls)."""
+    import torch
+
+    return torch.zeros(decode_workspace_size(plan, batch), dtype=torch.uint8, device=device)
+
+
 def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, query_position_ids,
-           q_norm_weight=None, k_norm_weight=None, out=None, lse=None, stream=None):
-    """pa_decode.  q [B, Hq, 1, 128] bf16; returns (out [B, Hq, 1, 128] bf16, lse [B, Hq, 1] fp32)."""
+           q_norm_weight=None, k_norm_weight=None, out=None, lse=None, workspace=None, stream=None):
+    """pa_decode.  q [B, Hq, 1, 128] bf16; returns (out [B, Hq, 1, 128] bf16, lse [B, Hq, 1] fp32).
+
+    workspace: None for the one-workgroup-per-(row, KV head) schedule, or a zeroed uint8 device
+    tensor from decode_workspace() for the multi-compute-unit schedule (same bits)."""
     import torch
 
     B, Sq, num_pages, nnz = _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len,
@@ -203,10 +220,14 @@ def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16, shape=q.shape)
     _need(lse, "lse", torch.float32, shape=q.shape[:3])
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws_bytes = int(workspace.numel())
     _check(load().pa_decode(plan.handle, B, Sq, num_pages, nnz, _ptr(kv_indptr), _ptr(kv_indices),
                             _ptr(kv_last_page_len), _ptr(query_position_ids), _ptr(q), _ptr(k_cache),
                             _ptr(v_cache), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(out), _ptr(lse),
-                            _stream(stream)), "pa_decode")
+                            _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
     return out, lse
 
 

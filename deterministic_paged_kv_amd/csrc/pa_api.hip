@@ -218,11 +218,13 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
                     const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
                     const int32_t* query_position_ids, const void* q, const void* k_cache, const void* v_cache,
                     const float* q_norm_weight, const float* k_norm_weight, void* out, float* lse,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_launch(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices,
                               kv_last_page_len, query_position_ids, q, k_cache, v_cache, out, lse);
   if (st != PA_OK || batch == 0) return st;
   if (q_len != 1) return PA_ERR_INVALID_ARGUMENT;
+  if (workspace && workspace_bytes < decode_workspace_bytes(batch, plan->num_kv_heads, plan->group))
+    return PA_ERR_WORKSPACE;
   DecodeParams p;
   p.batch = batch;
   p.num_q_heads = plan->num_q_heads;
@@ -245,7 +247,14 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
   p.lse = lse;
   p.rope = plan->d_rope;
   p.eps = plan->rms_eps;
-  return launch_decode(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return launch_decode(p, workspace, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_workspace_size(pa_plan_t plan, int32_t batch, size_t* bytes) {
+  if (!plan_ok(plan) || !bytes || batch < 0) return PA_ERR_INVALID_ARGUMENT;
+  if (batch > plan->max_batch) return PA_ERR_CAPACITY;
+  *bytes = decode_workspace_bytes(batch, plan->num_kv_heads, plan->group);
+  return PA_OK;
 }
 
 pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_indices,

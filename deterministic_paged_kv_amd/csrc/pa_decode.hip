@@ -1,4 +1,5 @@
-// Paged decode: one workgroup per (row, KV head), no Split-KV.
+// Paged decode, no Split-KV: a fixed reduction tree per (row, KV head), run by one
+// workgroup, or by one wavefront per stream on separate compute units with identical bits.
 //
 // What it computes: for the G = Hq/Hkv query heads of one GQA group, softmax attention of
 // the single query against every key of the row, with the Q/K prologue (RMSNorm, RoPE,
@@ -9,15 +10,23 @@
 // NHD) and "Design notes" (CSR metadata; with Split-KV disabled a row's result does not
 // depend on the plan width or the batch).
 //
-// Reduction order.  The workgroup's W wavefronts take the row's pages round-robin (wave w
-// takes logical pages w, w+W, w+2W, ...).  Each wave runs an FP32 online softmax over its
-// pages in ascending order, one page (16 keys) per step: S^T = K^ Q^T by bf16 MFMA with FP32
-// accumulation, a page max and sum per head taken in a fixed order (4 keys in registers, then
-// a 2-step lane butterfly), and O^T += V^T P^T by bf16 MFMA into FP32 with P split into two
-// bf16 parts (hi + lo), so the probabilities keep about 16 significant bits.  The W wave states are
-// then combined in wave order 0..W-1 through LDS.  Every choice depends only on the row's own
-// length, so the bits of a row are the same whatever batch it is in, whatever the plan width
-// and wherever its pages sit.
+// Reduction tree.  The row's pages are dealt to 8 streams: stream s takes logical pages
+// s, s+8, s+16, ...  Each stream runs an FP32 online softmax over its pages in ascending
+// order, one page (16 keys) per step: S^T = K^ Q^T by bf16 MFMA with FP32 accumulation, a
+// page max and sum per head taken in a fixed order (4 keys in registers, then a 2-step lane
+// exchange), and O^T += V^T P^T by bf16 MFMA into FP32 with P split into two bf16 parts
+// (hi + lo), so the probabilities keep about 16 significant bits.  The 8 stream states are
+// then combined in stream order 0..7.  The tree depends only on the row's own length, so the
+// bits of a row are the same whatever batch it is in, whatever the plan width and wherever
+// its pages sit.
+//
+// Two schedules run this same tree with the same device code (floating-point contraction is
+// pinned off in it, so both compile to the same arithmetic):
+//  * one workgroup of 8 wavefronts per (row, KV head), stream s on wavefront s, states
+//    combined through LDS (no workspace);
+//  * one single-wavefront workgroup per (row, KV head, stream), states written to a caller
+//    workspace, and the last workgroup of each (row, KV head) to finish (per-unit counter)
+//    combines them.  This spreads a long row over 8 compute units; the bits are identical.
 //
 // Memory layout.  k_cache/v_cache are NHD [page][slot][Hkv][128] bf16: one KV head of one
 // page is 16 rows of 256 B at a stride of Hkv * 256 B.  A lane (r = lane % 16, g = lane / 16)
@@ -31,206 +40,396 @@ namespace pa {
 
 namespace {
 
-constexpr int kDecodeWaves = 8;
-constexpr int kDecodeThreads = kDecodeWaves * 64;
-// V staging rows are padded by 16 bytes so that the transposed reads (one key row per lane
-// group g) fall on different LDS banks.
+constexpr int kStreams = 8;                  // streams of the reduction tree
+constexpr int kDecodeThreads = kStreams * 64;
+// V staging rows are padded by 16 bytes to spread the transposed reads over the LDS banks.
 constexpr int kVRow = kHeadDim + 8;
-
-struct DecodeSmem {
-  union {
-    uint16_t v[kDecodeWaves][kPageSize][kVRow];   // per-wave V page, [key][dim]
-    float acc[kDecodeWaves][4][kHeadDim];          // per-wave outputs of 4 heads (merge)
-  } u;
-  float m[kDecodeWaves][kMaxGroup];
-  float l[kDecodeWaves][kMaxGroup];
-  int poison[kDecodeWaves];
-};
+typedef uint16_t VSlot[kPageSize][kVRow];
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeParams P) {
-  __shared__ DecodeSmem sm;
-  const int unit = blockIdx.x;
-  const int b = unit / P.num_kv_heads;
-  const int hk = unit % P.num_kv_heads;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+// Row geometry from the CSR block table, with the bounds checks every kernel applies.
+struct RowInfo {
+  int p0, n, L, qp;
+  bool bad;
+  size_t head0;  // index of the group's first query head in [B * Hq]
+};
+
+__device__ __forceinline__ RowInfo row_info(const DecodeParams& P, int b, int hk) {
+  RowInfo ri;
+  ri.p0 = P.indptr[b];
+  const int p1 = P.indptr[b + 1];
+  ri.n = p1 - ri.p0;
+  const int lpl = P.last_page_len[b];
+  ri.qp = P.qpos[b];
+  ri.bad = ri.p0 < 0 || ri.n < 0 || p1 > P.num_indices || ri.n > P.max_pages_per_row || ri.qp < 0 ||
+           ri.qp >= P.table_rows || (ri.n > 0 && (lpl < 1 || lpl > kPageSize));
+  ri.L = (ri.n > 0 && !ri.bad) ? (ri.n - 1) * kPageSize + lpl : 0;
+  ri.head0 = (size_t)b * P.num_q_heads + (size_t)hk * P.group;
+  return ri;
+}
+
+// Output of a row with no keys (0, -inf) or with out-of-range metadata (NaN, NaN).
+__device__ __forceinline__ void write_degenerate(const DecodeParams& P, const RowInfo& ri, int tid, int nthreads) {
+  for (int i = tid; i < P.group * kHeadDim; i += nthreads) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    P.out[(ri.head0 + h) * kHeadDim + d] = ri.bad ? (uint16_t)0x7FC0 : (uint16_t)0;
+    if (d == 0) P.lse[ri.head0 + h] = ri.bad ? __builtin_nanf("") : -__builtin_inff();
+  }
+}
+
+// One page of one KV head as this lane holds it: key row r (dims 32*kb + 8*g ..) of K and V.
+struct PageIn {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+__device__ __forceinline__ void issue_page(PageIn& in, const DecodeParams& P, int phys, int hk, int r, int g) {
+  const size_t row_off = (((size_t)phys * kPageSize + r) * P.num_kv_heads + hk) * kHeadDim + 8 * g;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) in.k[kb] = ldg16(P.k_cache + row_off + 32 * kb);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) in.v[kb] = ldg16(P.v_cache + row_off + 32 * kb);
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Softmax state of one stream: running max and sum of head r (in every lane with that r),
+// and O^T (lane (r, g) holds dims 16*nb + 4g + i of head r).
+struct StreamState {
+  float m, l;
+  f32x4 acc[8];
+  int poison;
+};
+struct Scored {
+  i16x4 p_hi, p_lo;  // P^T of the page as two bf16 parts (hi + lo)
+  float alpha;       // rescale of the accumulator before this page's P.V
+};
+
+// Scores of page pg: stage V in LDS, run the K prologue, S^T = K^ Q^T, and advance the
+// running max and sum.  Lane (r, g) holds keys 4g+i of head r.
+__device__ __forceinline__ Scored score_page(const PageIn& in, float4 cs[8], const float* cs_next, int pg,
+                                             StreamState& st, const bf16x8 qop[4], const float* kw, bool knorm,
+                                             float eps, int L, int qp, int r, int g, VSlot& sv) {
+#pragma clang fp contract(off)
+  // keys at or past `live_end` are invisible (past the row, or after the query): only a row's
+  // last pages have any, so the masking sits behind a wave-uniform test
+  const int live_end = min(L, qp + 1);
+  const bool tail = pg * kPageSize + kPageSize > live_end;
+  if (!tail) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<uint4*>(&sv[r][32 * kb + 8 * g]) = in.v[kb];
+  } else {
+    const bool vlive = pg * kPageSize + r < L;  // value rows past the row's end are zero
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      *reinterpret_cast<uint4*>(&sv[r][32 * kb + 8 * g]) = vlive ? in.v[kb] : make_uint4(0, 0, 0, 0);
+  }
+
+  bf16x8 kop[4];
+  prologue_operand_lds_w(in.k, kw, knorm, eps, cs, g, kop);
+  load_cos_sin(cs_next, g, cs);  // the next page's cos/sin go in flight as soon as these are used
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], qop[kb], s, 0, 0, 0);
+
+  float t[4];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t[i] = s[i] * kScoreScaleLog2;
+    if (tail) {
+      const int j = pg * kPageSize + 4 * g + i;  // logical key index = key position
+      t[i] = j < live_end ? t[i] : -__builtin_inff();
+    }
+    mx = fmaxf(mx, t[i]);
+  }
+  mx = pair32_max(pair16_max(mx));
+  const float m_new = fmaxf(st.m, mx);
+  const bool any = m_new != -__builtin_inff();
+  Scored sc;
+  sc.alpha = any ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
+  float pr[4];
+  float ps = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pr[i] = any ? __builtin_amdgcn_exp2f(t[i] - m_new) : 0.0f;
+    ps = ps + pr[i];
+  }
+  ps = pair32_sum(pair16_sum(ps));
+  st.l = __builtin_fmaf(st.l, sc.alpha, ps);
+  st.m = m_new;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 hi = (__bf16)pr[i];
+    sc.p_hi[i] = __builtin_bit_cast(short, hi);
+    sc.p_lo[i] = __builtin_bit_cast(short, (__bf16)(pr[i] - (float)hi));
+  }
+  return sc;
+}
+
+// acc = acc * alpha + P.V for a scored page whose V sits in `sv`.
+__device__ __forceinline__ void pv_page(const Scored& sc, StreamState& st, int r, int g, VSlot& sv) {
+#pragma clang fp contract(off)
+  // rescale only when some head's max moved: multiplying by exactly 1 changes nothing
+  if (__builtin_amdgcn_ballot_w64(sc.alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) st.acc[nb] = st.acc[nb] * sc.alpha;
+  }
+  // V^T operand by transposed LDS reads: in each 16-lane group g, lane j points at keys
+  // 4g + j/4, dims 16*nb + 4*(j%4) .. +3; lane r then receives keys 4g .. 4g+3 of dim 16*nb + r.
+  const int jr = 4 * g + (r >> 2);
+  const int jc = 4 * (r & 3);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sv[jr][16 * nb + jc]));
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, sc.p_hi, st.acc[nb], 0, 0, 0);
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, sc.p_lo, st.acc[nb], 0, 0, 0);
+  }
+}
+
+// Stream s of one (row, KV head) unit on one wavefront: pages s, s+8, s+16, ...
+// sv: this wavefront's V staging slot; kw: the K norm weights in LDS (or 1.0 without norm).
+__device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo& ri, int hk, int s, int lane,
+                                           VSlot& sv, const float* kw, StreamState& st) {
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = P.group;
-  const int Hkv = P.num_kv_heads;
-
-  // ---- row geometry (CSR block table) and bounds checks -------------------------------
-  const int p0 = P.indptr[b];
-  const int p1 = P.indptr[b + 1];
-  const int n = p1 - p0;
-  const int lpl = P.last_page_len[b];
-  const int qp = P.qpos[b];
-  const bool bad = p0 < 0 || n < 0 || p1 > P.num_indices || n > P.max_pages_per_row || qp < 0 ||
-                   qp >= P.table_rows || (n > 0 && (lpl < 1 || lpl > kPageSize));
-  const int L = (n > 0 && !bad) ? (n - 1) * kPageSize + lpl : 0;
-  const size_t head0 = (size_t)b * P.num_q_heads + (size_t)hk * G;  // first head of the group
-  if (bad || L == 0) {
-    for (int i = tid; i < G * kHeadDim; i += kDecodeThreads) {
-      const int h = i / kHeadDim, d = i % kHeadDim;
-      P.out[(head0 + h) * kHeadDim + d] = bad ? (uint16_t)0x7FC0 : (uint16_t)0;
-      if (d == 0) P.lse[head0 + h] = bad ? __builtin_nanf("") : -__builtin_inff();
-    }
-    return;
-  }
-
+  const int n = ri.n, L = ri.L, qp = ri.qp, p0 = ri.p0;
   const bool qnorm = P.q_norm != nullptr;
   const bool knorm = P.k_norm != nullptr;
 
-  // ---- q^ of the group's heads in the operand layout (vector r = head r < G) -----------
+  // The stream's first two pages go in flight first.  Pages past the row's end are still
+  // loaded (from the row's last page), so every iteration issues the same loads; their data
+  // is never used.
+  st.poison = 0;
+  auto phys_of = [&](int pg) {
+    int phys = load_uniform(P.indices, p0 + min(pg, n - 1));
+    if (phys < 0 || phys >= P.num_pages) { st.poison |= pg < n; phys = 0; }
+    return phys;
+  };
+  int pgA = s, pgB = s + kStreams;
+  PageIn inA, inB;
+  issue_page(inA, P, phys_of(pgA), hk, r, g);
+  issue_page(inB, P, phys_of(pgB), hk, r, g);
+  // table row of page pg's key r (pages past the end read the last page's rows)
+  auto rope_row = [&](int pg) { return P.rope + (size_t)(min(pg, n - 1) * kPageSize + r) * kHeadDim; };
+  float4 cs[8];  // cos/sin of the next page to score
+  load_cos_sin(rope_row(pgA), g, cs);
+  int physA = phys_of(pgA + 2 * kStreams), physB = phys_of(pgB + 2 * kStreams);
+
+  // q^ of the group's heads in the operand layout (vector r = head r < G)
   bf16x8 qop[4];
   {
     float w[32];
     uint4 raw[4];
+    float4 qcs[8];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       raw[kb] = make_uint4(0, 0, 0, 0);
-      if (r < G) raw[kb] = ldg16(P.q + (head0 + r) * kHeadDim + 32 * kb + 8 * g);
+      if (r < G) raw[kb] = ldg16(P.q + (ri.head0 + r) * kHeadDim + 32 * kb + 8 * g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
     }
-    prologue_operand(raw, w, qnorm, P.eps, P.rope + (size_t)qp * kHeadDim, g, qop);
-  }
-  float kw[32];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kw[kb * 8 + e] = knorm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
-
-  // ---- per-wave online softmax over pages w, w+W, ... ---------------------------------
-  // S^T tile (MFMA C of K^ . Q^T): lane (r, g) holds keys 4g+i (i = 0..3) of head r.  The
-  // same registers, rounded to bf16, are the B operand (P^T) of O^T += V^T . P^T, whose C
-  // layout gives lane (r, g) dims 16*nb + 4g + i of head r.  m, l of head r live in every
-  // lane with that r.
-  float m_run = -__builtin_inff(), l_run = 0.0f;
-  f32x4 acc[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int poison = 0;
-
-  for (int pg = wave; pg < n; pg += kDecodeWaves) {
-    int phys = P.indices[p0 + pg];
-    if (phys < 0 || phys >= P.num_pages) { poison = 1; phys = 0; }
-    const size_t row_off = (((size_t)phys * kPageSize + r) * Hkv + hk) * kHeadDim + 8 * g;
-    uint4 kraw[4], vraw[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      kraw[kb] = ldg16(P.k_cache + row_off + 32 * kb);
-      vraw[kb] = ldg16(P.v_cache + row_off + 32 * kb);
-    }
-    // stage V for the transposed read; rows past the row's end are zero
-    const bool vlive = pg * kPageSize + r < L;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      *reinterpret_cast<uint4*>(&sm.u.v[wave][r][32 * kb + 8 * g]) = vlive ? vraw[kb] : make_uint4(0, 0, 0, 0);
-
-    bf16x8 kop[4];
-    prologue_operand(kraw, kw, knorm, P.eps, P.rope + (size_t)(pg * kPageSize + r) * kHeadDim, g, kop);
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], qop[kb], s, 0, 0, 0);
-
-    float t[4];
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = pg * kPageSize + 4 * g + i;  // logical key index = key position
-      t[i] = (j < L && j <= qp) ? s[i] * kScoreScaleLog2 : -__builtin_inff();
-      mx = fmaxf(mx, t[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const bool any = m_new != -__builtin_inff();
-    const float alpha = any ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-    float pr[4];
-    float ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[i] = any ? __builtin_amdgcn_exp2f(t[i] - m_new) : 0.0f;
-      ps += pr[i];
-    }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    // P^T as two bf16 parts, hi + lo, so the P.V product keeps ~16 bits of each probability
-    i16x4 pb_hi, pb_lo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 hi = (__bf16)pr[i];
-      pb_hi[i] = __builtin_bit_cast(short, hi);
-      pb_lo[i] = __builtin_bit_cast(short, (__bf16)(pr[i] - (float)hi));
-    }
-
-    wave_lds_sync();
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      i16x4 va;  // V^T rows: dim 16*nb + r, keys 4g .. 4g+3
-#pragma unroll
-      for (int e = 0; e < 4; ++e) va[e] = (short)sm.u.v[wave][4 * g + e][16 * nb + r];
-      acc[nb] = acc[nb] * alpha;
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, acc[nb], 0, 0, 0);
-    }
-    wave_lds_sync();
+    load_cos_sin(P.rope + (size_t)qp * kHeadDim, g, qcs);
+    prologue_operand(raw, w, qnorm, P.eps, qcs, qop);
   }
 
-  // ---- combine the W wave states in wave order -----------------------------------------
-  if (g == 0 && r < G) { sm.m[wave][r] = m_run; sm.l[wave][r] = l_run; }
-  if (lane == 0) sm.poison[wave] = poison;
+  st.m = -__builtin_inff();
+  st.l = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Pages alternate between two register buffers: while one page is scored and accumulated,
+  // the next two are in flight.  Each page is scored and then accumulated before the next.
+  for (; pgA < n;) {
+    const Scored sa = score_page(inA, cs, rope_row(pgB), pgA, st, qop, kw, knorm, P.eps, L, qp, r, g, sv);
+    pgA += 2 * kStreams;
+    issue_page(inA, P, physA, hk, r, g);
+    physA = phys_of(pgA + 2 * kStreams);
+    wave_lds_sync();
+    pv_page(sa, st, r, g, sv);
+    wave_lds_sync();
+    if (pgB < n) {
+      const Scored sb = score_page(inB, cs, rope_row(pgA), pgB, st, qop, kw, knorm, P.eps, L, qp, r, g, sv);
+      wave_lds_sync();
+      pv_page(sb, st, r, g, sv);
+      wave_lds_sync();
+    }
+    pgB += 2 * kStreams;
+    issue_page(inB, P, physB, hk, r, g);
+    physB = phys_of(pgB + 2 * kStreams);
+  }
+}
+
+// Combine the kStreams states of head h at dim d in stream order and write out (and lse at
+// d == 0).  m(w), l(w), acc(w) read stream w's values.
+template <class M, class Lf, class A>
+__device__ __forceinline__ void combine_one(const DecodeParams& P, const RowInfo& ri, int h, int d, bool poison,
+                                            M m, Lf l, A acc) {
+#pragma clang fp contract(off)
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < kStreams; ++w) mx = fmaxf(mx, m(w));
+  float num = 0.0f, den = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kStreams; ++w) {
+    const float mw = m(w);
+    const float sc = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - mx);
+    num = __builtin_fmaf(acc(w), sc, num);
+    den = __builtin_fmaf(l(w), sc, den);
+  }
+  float o = num / den;
+  float lse = (mx + __builtin_log2f(den)) * kLn2;
+  if (poison) { o = __builtin_nanf(""); lse = __builtin_nanf(""); }
+  P.out[(ri.head0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
+  if (d == 0) P.lse[ri.head0 + h] = lse;
+}
+
+// ---------------------------------------------------------------------------------------
+// Schedule 1: one workgroup per unit, stream s on wavefront s, combine through LDS.
+// ---------------------------------------------------------------------------------------
+struct UnitSmem {
+  union {
+    VSlot v[kStreams];                     // per-wave V page
+    float acc[kStreams][4][kHeadDim];      // per-stream outputs of 4 heads (combine)
+  } u;
+  float m[kStreams][kMaxGroup];
+  float l[kStreams][kMaxGroup];
+  float kw[kHeadDim];  // K RMSNorm weights
+  int poison[kStreams];
+};
+
+__global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const DecodeParams P) {
+  __shared__ UnitSmem sm;
+  const int unit = blockIdx.x;
+  const int b = unit / P.num_kv_heads;
+  const int hk = unit % P.num_kv_heads;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int G = P.group;
+  const RowInfo ri = row_info(P, b, hk);
+  if (ri.bad || ri.L == 0) {
+    write_degenerate(P, ri, tid, kDecodeThreads);
+    return;
+  }
+  for (int i = tid; i < kHeadDim; i += kDecodeThreads) sm.kw[i] = P.k_norm != nullptr ? P.k_norm[i] : 1.0f;
   __syncthreads();
-  int any_poison = 0;
-#pragma unroll
-  for (int w = 0; w < kDecodeWaves; ++w) any_poison |= sm.poison[w];
 
-  // heads are merged four at a time through LDS
+  StreamState st;
+  run_stream(P, ri, hk, wave, lane, sm.u.v[wave], sm.kw, st);
+
+  if (g == 0 && r < G) { sm.m[wave][r] = st.m; sm.l[wave][r] = st.l; }
+  if (lane == 0) sm.poison[wave] = st.poison;
+  __syncthreads();
+  int poison = 0;
+#pragma unroll
+  for (int w = 0; w < kStreams; ++w) poison |= sm.poison[w];
+  // heads are combined four at a time through LDS
   for (int h0 = 0; h0 < G; h0 += 4) {
     if (r >= h0 && r < h0 + 4) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.u.acc[wave][r - h0][16 * nb + 4 * g + i] = acc[nb][i];
+        for (int i = 0; i < 4; ++i) sm.u.acc[wave][r - h0][16 * nb + 4 * g + i] = st.acc[nb][i];
     }
     __syncthreads();
     const int nh = min(4, G - h0);
     for (int idx = tid; idx < nh * kHeadDim; idx += kDecodeThreads) {
       const int hi = idx / kHeadDim, d = idx % kHeadDim;
       const int h = h0 + hi;
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm.m[w][h]);
-      float num = 0.0f, den = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float mw = sm.m[w][h];
-        const float sc = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        num += sm.u.acc[w][hi][d] * sc;
-        den += sm.l[w][h] * sc;
-      }
-      float o = num / den;
-      float lse = (M + __builtin_log2f(den)) * kLn2;
-      if (any_poison) { o = __builtin_nanf(""); lse = __builtin_nanf(""); }
-      P.out[(head0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
-      if (d == 0) P.lse[head0 + h] = lse;
+      combine_one(P, ri, h, d, poison != 0, [&](int w) { return sm.m[w][h]; }, [&](int w) { return sm.l[w][h]; },
+                  [&](int w) { return sm.u.acc[w][hi][d]; });
     }
     __syncthreads();
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Schedule 2: one single-wavefront workgroup per (unit, stream); states to the workspace;
+// the last workgroup of a unit combines.  Workspace: an int32 counter per unit (zero between
+// calls: the combining workgroup resets it), an int32 poison flag per (unit, stream), then
+// per unit and stream G records of [m, l, 128 accumulators].
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void decode_stream_kernel(const DecodeParams P, int32_t* __restrict__ counters,
+                                                           int32_t* __restrict__ poisons, float* __restrict__ states) {
+  __shared__ VSlot sv;
+  __shared__ float kw[kHeadDim];
+  const int unit = blockIdx.x / kStreams;
+  const int s = blockIdx.x % kStreams;
+  const int b = unit / P.num_kv_heads;
+  const int hk = unit % P.num_kv_heads;
+  const int lane = threadIdx.x;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int G = P.group;
+  const RowInfo ri = row_info(P, b, hk);
+  if (ri.bad || ri.L == 0) {
+    if (s == 0) write_degenerate(P, ri, lane, 64);
+    return;
+  }
+  for (int i = lane; i < kHeadDim; i += 64) kw[i] = P.k_norm != nullptr ? P.k_norm[i] : 1.0f;
+  __syncthreads();
+
+  StreamState st;
+  run_stream(P, ri, hk, s, lane, sv, kw, st);
+
+  const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per stream state
+  float* unit_states = states + (size_t)unit * kStreams * rec;
+  if (r < G) {
+    float* hrec = unit_states + (size_t)s * rec + (size_t)r * (2 + kHeadDim);
+    if (g == 0) { hrec[0] = st.m; hrec[1] = st.l; }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<f32x4*>(hrec + 2 + 16 * nb + 4 * g) = st.acc[nb];
+  }
+  if (lane == 0) poisons[unit * kStreams + s] = st.poison;
+  // publish this stream's state, then count it
+  __threadfence();
+  int ticket = 0;
+  if (lane == 0) ticket = atomicAdd(&counters[unit], 1);
+  ticket = __shfl(ticket, 0);
+  if (ticket != kStreams - 1) return;
+  __threadfence();
+
+  // last stream of the unit: combine in stream order
+  int poison = 0;
+  for (int w = 0; w < kStreams; ++w) poison |= poisons[unit * kStreams + w];
+  for (int idx = lane; idx < G * kHeadDim; idx += 64) {
+    const int h = idx / kHeadDim, d = idx % kHeadDim;
+    const float* base = unit_states + (size_t)h * (2 + kHeadDim);
+    combine_one(P, ri, h, d, poison != 0, [&](int w) { return base[(size_t)w * rec]; },
+                [&](int w) { return base[(size_t)w * rec + 1]; },
+                [&](int w) { return base[(size_t)w * rec + 2 + d]; });
+  }
+  if (lane == 0) counters[unit] = 0;
+}
+
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)p.batch * (unsigned)p.num_kv_heads;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kDecodeThreads), 0, stream, p);
+size_t decode_workspace_bytes(int batch, int num_kv_heads, int group) {
+  const size_t units = (size_t)batch * num_kv_heads;
+  return align256(units * sizeof(int32_t)) + align256(units * kStreams * sizeof(int32_t)) +
+         units * kStreams * group * (2 + kHeadDim) * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t stream) {
+  const unsigned units = (unsigned)p.batch * (unsigned)p.num_kv_heads;
+  if (units == 0) return hipSuccess;
+  if (workspace == nullptr) {
+    hipLaunchKernelGGL(decode_unit_kernel, dim3(units), dim3(kDecodeThreads), 0, stream, p);
+  } else {
+    char* ws = (char*)workspace;
+    int32_t* counters = (int32_t*)ws;
+    ws += align256((size_t)units * sizeof(int32_t));
+    int32_t* poisons = (int32_t*)ws;
+    ws += align256((size_t)units * kStreams * sizeof(int32_t));
+    float* states = (float*)ws;
+    hipLaunchKernelGGL(decode_stream_kernel, dim3(units * kStreams), dim3(64), 0, stream, p, counters, poisons,
+                       states);
+  }
   return hipGetLastError();
 }
 

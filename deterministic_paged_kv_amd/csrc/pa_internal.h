@@ -60,6 +60,41 @@ __device__ __forceinline__ void unpack8(const uint4& raw, float* x) {
   x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
 }
 
+// Exchanges between lanes l and l^16 / l^32 with v_permlane16_swap / v_permlane32_swap
+// (plain VALU operations, no LDS round trip).  Swapping a register with itself leaves the
+// lane's own value in one half of the result and its partner's in the other, so both lanes
+// of a pair combine the same two operands and end with the same value.
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ double pair16_sum(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  return __builtin_bit_cast(double, (uint64_t)lo[0] | ((uint64_t)hi[0] << 32)) +
+         __builtin_bit_cast(double, (uint64_t)lo[1] | ((uint64_t)hi[1] << 32));
+}
+__device__ __forceinline__ double pair32_sum(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  return __builtin_bit_cast(double, (uint64_t)lo[0] | ((uint64_t)hi[0] << 32)) +
+         __builtin_bit_cast(double, (uint64_t)lo[1] | ((uint64_t)hi[1] << 32));
+}
+
 // The Q/K prologue for one head vector held in the operand layout above:
 //   y   = RMSNorm(x) * w     sum of squares exact (float64; every square of a BF16 value is
 //                            exact and the 128-term float64 sum is exact for any realistic
@@ -75,22 +110,24 @@ __device__ __forceinline__ void unpack8(const uint4& raw, float* x) {
 // RoPE Fusion" (Llama rotate-half RoPE, theta 1e6, rotary_dim = head_dim).
 //
 // raw: the lane's 4 blocks of 8 BF16 inputs.  w: the lane's 32 norm weights (block-major),
-// ignored if !norm.  cs: the position's cos/sin row (cos[64] then sin[64]).  All four lanes
-// of a vector must call this together (it exchanges partial sums across lanes l^16, l^32).
+// ignored if !norm.  cs: the lane's 32 cos/sin values for its vector's position, as loaded by
+// load_cos_sin (cos of frequencies 8g..8g+7, 32+8g..32+8g+7, then sin of the same).  All four
+// lanes of a vector must call this together (it exchanges partial sums across lanes l^16, l^32).
 __device__ __forceinline__ void prologue_operand(const uint4 raw[4], const float w[32], bool norm, float eps,
-                                                 const float* __restrict__ cs, int g, bf16x8 out[4]) {
+                                                 const float4 cs[8], bf16x8 out[4]) {
 #pragma clang fp contract(off)
   float x[4][8];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) unpack8(raw[kb], x[kb]);
   if (norm) {
+    // x*x is exact in float64, so fma(x, x, ss) rounds exactly like x*x + ss
     double ss = 0.0;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += (double)x[kb][e] * (double)x[kb][e];
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+      for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)x[kb][e], (double)x[kb][e], ss);
+    ss = pair16_sum(ss);
+    ss = pair32_sum(ss);
     const float ms = (float)(ss * (1.0 / kHeadDim));
     const float t = ms + eps;
     const float inv = (float)(1.0 / __builtin_sqrt((double)t));
@@ -101,9 +138,7 @@ __device__ __forceinline__ void prologue_operand(const uint4 raw[4], const float
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const float4* cp = reinterpret_cast<const float4*>(cs + 32 * kb + 8 * g);
-    const float4* sp = reinterpret_cast<const float4*>(cs + kHalfDim + 32 * kb + 8 * g);
-    const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+    const float4 c0 = cs[2 * kb], c1 = cs[2 * kb + 1], s0 = cs[4 + 2 * kb], s1 = cs[4 + 2 * kb + 1];
     const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
@@ -119,29 +154,73 @@ __device__ __forceinline__ void prologue_operand(const uint4 raw[4], const float
   }
 }
 
+// Same prologue with the norm weights read from LDS (w_lds: the 128 weights) instead of
+// registers.  The arithmetic and its order are identical.
+__device__ __forceinline__ void prologue_operand_lds_w(const uint4 raw[4], const float* w_lds, bool norm, float eps,
+                                                       const float4 cs[8], int g, bf16x8 out[4]) {
+#pragma clang fp contract(off)
+  float x[4][8];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) unpack8(raw[kb], x[kb]);
+  if (norm) {
+    double ss = 0.0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)x[kb][e], (double)x[kb][e], ss);
+    ss = pair16_sum(ss);
+    ss = pair32_sum(ss);
+    const float ms = (float)(ss * (1.0 / kHeadDim));
+    const float t = ms + eps;
+    const float inv = (float)(1.0 / __builtin_sqrt((double)t));
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 w0 = *reinterpret_cast<const float4*>(w_lds + 32 * kb + 8 * g);
+      const float4 w1 = *reinterpret_cast<const float4*>(w_lds + 32 * kb + 8 * g + 4);
+      const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[kb][e] = (x[kb][e] * inv) * w[e];
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const float4 c0 = cs[2 * kb], c1 = cs[2 * kb + 1], s0 = cs[4 + 2 * kb], s1 = cs[4 + 2 * kb + 1];
+    const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y1 = x[kb][e], y2 = x[kb + 2][e];
+      const float a = y1 * c[e];
+      const float b = y2 * s[e];
+      const float cc = y2 * c[e];
+      const float d = y1 * s[e];
+      out[kb][e] = (__bf16)(a - b);
+      out[kb + 2][e] = (__bf16)(cc + d);
+    }
+  }
+}
+
+// The lane's 32 cos/sin values of one position from the table row `row` (cos[64], sin[64]).
+__device__ __forceinline__ void load_cos_sin(const float* __restrict__ row, int g, float4 cs[8]) {
+  const float4* c = reinterpret_cast<const float4*>(row);
+  const float4* s = reinterpret_cast<const float4*>(row + kHalfDim);
+  cs[0] = c[2 * g]; cs[1] = c[2 * g + 1]; cs[2] = c[8 + 2 * g]; cs[3] = c[8 + 2 * g + 1];
+  cs[4] = s[2 * g]; cs[5] = s[2 * g + 1]; cs[6] = s[8 + 2 * g]; cs[7] = s[8 + 2 * g + 1];
+}
+
+// Wave-uniform read of a read-only int32 array through the constant address space, so the
+// compiler issues a scalar load (counted separately from the vector loads in flight).
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, int i) {
+  return ((const_i32_ptr)p)[i];
+}
+
 // Intra-wavefront LDS hand-off: make this lane's LDS writes visible to the other lanes of
 // the same wavefront, and keep the compiler from moving LDS accesses across this point.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Fixed butterfly reductions over the 16 lanes of a row (lanes 16*g .. 16*g+15).  Every lane
-// ends with the same value: at each level both partners add the same two operands.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v = v + __shfl_xor(v, 1);
-  v = v + __shfl_xor(v, 2);
-  v = v + __shfl_xor(v, 4);
-  v = v + __shfl_xor(v, 8);
-  return v;
 }
 
 struct DecodeParams {
@@ -162,7 +241,11 @@ struct DecodeParams {
   float eps;
 };
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// Decode.  workspace == NULL: one workgroup per (row, KV head).  Otherwise (at least
+// decode_workspace_bytes, zero before its first use; every call leaves it zero): one
+// wavefront per (row, KV head, stream) on separate compute units.  Same bits either way.
+size_t decode_workspace_bytes(int batch, int num_kv_heads, int group);
+hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t stream);
 
 struct ValidateParams {
   int32_t batch, q_len, num_pages, num_indices, max_pages_per_row;

@@ -76,7 +76,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrefillParams P, ui
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.q + (size_t)v * kHeadDim + 32 * kb + 8 * g) : zero4;
-      prologue_operand(raw, qw, qnorm, P.eps, P.rope + (size_t)pos * kHeadDim, g, op);
+      float4 cs[8];
+      load_cos_sin(P.rope + (size_t)pos * kHeadDim, g, cs);
+      prologue_operand(raw, qw, qnorm, P.eps, cs, op);
       if (live) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) stg16(qh + (size_t)v * kHeadDim + 32 * kb + 8 * g, bad ? nan4 : as_u4(op[kb]));
@@ -106,7 +108,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrefillParams P, ui
       const size_t src = (((size_t)phys * kPageSize + r) * P.num_kv_heads + hk) * kHeadDim + 8 * g;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.k_cache + src + 32 * kb) : zero4;
-      prologue_operand(raw, kw, knorm, P.eps, P.rope + (size_t)(live ? j : 0) * kHeadDim, g, op);
+      float4 cs[8];
+      load_cos_sin(P.rope + (size_t)(live ? j : 0) * kHeadDim, g, cs);
+      prologue_operand(raw, kw, knorm, P.eps, cs, op);
       uint16_t* dst = kh + ((size_t)hk * P.num_indices * kPageSize + (size_t)gp * kPageSize + r) * kHeadDim + 8 * g;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !page_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));

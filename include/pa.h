@@ -75,7 +75,7 @@ enum {
   PA_ERR_QUERY_POSITION = -10,   /* query positions not contiguous, negative, or not ending
                                     at L_b - 1 or L_b                                        */
   PA_ERR_CACHE_POSITION = -11,   /* cache_position != query_position_ids                     */
-  PA_ERR_WORKSPACE = -12,        /* prefill workspace missing or too small                   */
+  PA_ERR_WORKSPACE = -12,        /* a workspace too small (decode), or missing (prefill)      */
   PA_ERR_HIP = -13               /* a HIP runtime call failed                                */
 };
 
@@ -87,9 +87,10 @@ enum { PA_SPLIT_DISABLED = 0, PA_SPLIT_FIXED = 1, PA_SPLIT_AUTO = 2 };
 
 typedef struct pa_plan_s* pa_plan_t;
 
-/* Result of pa_validate_metadata: the first violated rule (rules are checked in the
- * order of the status codes above, from PA_ERR_INDPTR down) and, within that rule, the
- * lowest offending element. */
+/* Result of pa_validate_metadata: the first violated rule, in the order PA_ERR_INDPTR,
+ * PA_ERR_CAPACITY (pages per row), PA_ERR_PAGE_OOB, PA_ERR_DUPLICATE_PAGE,
+ * PA_ERR_LAST_PAGE_LEN, PA_ERR_KEY_POSITION, PA_ERR_QUERY_POSITION, PA_ERR_CACHE_POSITION,
+ * and within that rule the lowest offending element. */
 typedef struct {
   pa_status code;   /* PA_OK or the violated rule                                   */
   int32_t row;      /* batch row of the violation, -1 if not row-specific            */
@@ -148,9 +149,9 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
                                const int32_t* key_position_ids, void* stream,
                                pa_validation_report* report);
 
-/* Paged decode (Sq = 1): one fused pass per (row, KV head) that gathers the row's pages in
- * logical order, applies RMSNorm + RoPE + BF16 rounding to q and to every key, and runs
- * the FP32 online softmax and PV product with no Split-KV ([PR279] "Scope"; [PR7]
+/* Paged decode (Sq = 1): the G = Hq/Hkv query heads of each (row, KV head) against every key
+ * of the row, with the page gather, the RMSNorm + RoPE + BF16 prologue of q and of every key,
+ * an FP32 online softmax and the P.V product fused, and no Split-KV ([PR279] "Scope"; [PR7]
  * "FlashInfer RoPE Fusion", "Split-KV Policy"; [PR162] "Design notes").
  *   q                bf16 [B, Hq, 1, 128]   pre-norm, pre-RoPE.
  *   k_cache, v_cache bf16 [num_pages, 16, Hkv, 128] (NHD); K pre-norm, pre-RoPE.
@@ -161,13 +162,26 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
  *                                           exp(scaled scores) ([PR7] "Original PR7
  *                                           Requirements").  Rows with no keys get
  *                                           out = 0 and lse = -inf.
+ *   workspace        NULL, or device memory of at least pa_decode_workspace_size() bytes.
+ * Reduction order: each (row, KV head)'s pages are dealt to 8 streams (stream s takes pages
+ * s, s+8, s+16, ...), each stream is an online softmax over its pages in ascending order,
+ * and the 8 stream states are combined in stream order.  The order depends only on the row
+ * itself.  With workspace == NULL one workgroup runs all 8 streams; with a workspace each
+ * stream runs on its own compute unit and the last to finish combines them, which spreads a
+ * long row over 8 compute units.  Both give bit-identical results.  The workspace must be
+ * zero before its first use; every call leaves it zero again.  Calls that overlap in time
+ * need separate workspaces.
  * Asynchronous on `stream`; requires q_len == 1 and batch <= plan capacity. */
 pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
                     int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
                     const int32_t* kv_last_page_len, const int32_t* query_position_ids,
                     const void* q, const void* k_cache, const void* v_cache,
                     const float* q_norm_weight, const float* k_norm_weight,
-                    void* out, float* lse, void* stream);
+                    void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of pa_decode's multi-compute-unit schedule for `batch` rows (host
+ * arithmetic only). */
+pa_status pa_decode_workspace_size(pa_plan_t plan, int32_t batch, size_t* bytes);
 
 /* Workspace bytes pa_prefill needs for these sizes (host arithmetic only). */
 pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len,

@@ -62,6 +62,11 @@ def run(kind, plan, db, **kw):
     return to_numpy(out, lse)
 
 
+def same_bits(a, b):
+    """Bitwise equality of two (out bits, lse) results."""
+    return np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
 def bf16_to_f64(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 

@@ -27,7 +27,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("pa_plan", "pa_plan_destroy", "pa_validate_metadata", "pa_decode", "pa_prefill",
-                     "pa_prefill_workspace_size", "pa_status_string"):
+                     "pa_decode_workspace_size", "pa_prefill_workspace_size", "pa_status_string"):
         assert required in names
 
 
@@ -72,7 +72,8 @@ def test_plan_fails_closed_on_host_arguments(lib):
 
 def test_calls_without_a_plan_fail_closed(lib):
     null = None
-    assert lib.pa_decode(null, 1, 1, 1, 0, *([null] * 11), null) == -1
+    assert lib.pa_decode(null, 1, 1, 1, 0, *([null] * 12), 0, null) == -1
+    assert lib.pa_decode_workspace_size(null, 1, ctypes.byref(ctypes.c_size_t())) == -1
     assert lib.pa_prefill(null, 1, 1, 1, 0, *([null] * 12), 0, null) == -1
     from deterministic_paged_kv_amd import binding
 

@@ -5,7 +5,8 @@ import pytest
 
 import oracle
 import workloads
-from _paged import DeviceBatch, assert_parity, make_plan, run
+import deterministic_paged_kv_amd as pa
+from _paged import DeviceBatch, assert_parity, make_plan, run, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -129,3 +130,30 @@ def test_long_context_decode_sampled(gpu, batch, length):
     ref_out, ref_lse = oracle_ref(b, rows=[batch - 1], q_heads=heads)
     assert_parity(out[[batch - 1]][:, heads], lse[[batch - 1]][:, heads], ref_out, ref_lse,
                   f"long decode B={batch} L={length}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "qwen3_8b", "batch8", "groups16"])
+def test_multi_cu_schedule_is_bit_identical(gpu, name):
+    """One wavefront per stream on separate compute units gives the same bits as one workgroup
+    per (row, KV head); the workspace is left zeroed, so it is reused across calls."""
+    if name == "tiny":
+        b = workloads.tiny_decode()
+    elif name == "ragged":
+        b = workloads.make_batch(41, [0, 1, 15, 16, 17, 33, 130, 255], q_len=1, num_q_heads=8, num_kv_heads=2,
+                                 num_pages=128)
+    elif name == "qwen3_8b":
+        b = workloads.qwen3_8b_decode()
+    elif name == "batch8":
+        b = workloads.invariance_batch(alone=False)
+    else:
+        b = workloads.make_batch(42, [900, 77], q_len=1, num_q_heads=32, num_kv_heads=2, num_pages=128)
+    plan = make_plan(b, max_pages_per_row=max(256, int(np.max(np.diff(b.kv_indptr)))))
+    db = DeviceBatch(b)
+    unit = run("decode", plan, db)
+    ws = pa.decode_workspace(plan, b.batch)
+    for _ in range(3):
+        multi = run("decode", plan, db, workspace=ws)
+        assert same_bits(unit, multi), name
+    # counters are zero again after every call
+    units = b.batch * b.num_kv_heads
+    assert int(ws[:4 * units].count_nonzero()) == 0
