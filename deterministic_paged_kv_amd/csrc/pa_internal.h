@@ -282,10 +282,10 @@ struct PrefillParams {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Prefill workspace: q^ [B][Hq][Sq][128] bf16, then k^ [Hkv][nnz * 16][128] bf16.
+// Prefill workspace: k^ [Hkv][nnz * 16][128] bf16.
 inline size_t prefill_workspace_bytes(int hq, int hkv, int batch, int q_len, int num_indices) {
-  return align256((size_t)batch * hq * q_len * kHeadDim * 2) +
-         align256((size_t)hkv * num_indices * kPageSize * kHeadDim * 2);
+  (void)hq; (void)batch; (void)q_len;
+  return align256((size_t)hkv * num_indices * kPageSize * kHeadDim * 2);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

@@ -7,17 +7,19 @@
 // K/V order before arithmetic, Split-KV disabled, FP32 LSE, same post-RoPE boundary).
 //
 // Two kernels per call.
-//  1. prologue_kernel: every query vector and every cached key (per KV head) goes once through
-//     the shared Q/K prologue (RMSNorm, RoPE, BF16).  q^ is written in q's own layout
-//     [B][Hq][Sq][128]; k^ is written in logical order, [Hkv][nnz * 16][128], key j of row b at
-//     (kv_indptr[b] * 16 + j); slots past a row's length are written as zeros.
-//  2. attend_kernel: one workgroup per (query block of 32, row, KV head, group of up to 4
-//     query heads); wavefront w handles one query head of the KV head's GQA group, so those
-//     heads share each staged V tile.  Key tiles
-//     of 64 (4 pages) are visited in ascending order up to the block's last visible key; per
-//     tile S^T = K^ Q^T (bf16 MFMA, FP32 accumulation), causal mask on logical positions
-//     (key j visible to a query at position p iff j <= p), FP32 online softmax with a fixed
-//     reduction order, O^T += V^T P^T (P rounded to bf16 for the MFMA, FP32 accumulation).
+//  1. key_prologue_kernel: every cached key of every KV head goes once through the shared
+//     Q/K prologue (RMSNorm, RoPE, BF16); k^ is written in logical order to the workspace,
+//     [Hkv][nnz * 16][128], key j of row b at (kv_indptr[b] * 16 + j); slots past a row's
+//     length are written as zeros.
+//  2. attend_kernel: one workgroup per (block of 32 queries, row, KV head, group of up to 4
+//     query heads); wavefront w handles one query head of the KV head's GQA group and runs
+//     the prologue of its own queries.  Key tiles of 32 (2 pages) are visited in ascending
+//     order up to the block's last visible key; the workgroup stages each tile's k^ and V in
+//     LDS once for all its heads, with the next tile's loads in flight while the current one
+//     is used.  Per tile: S^T = K^ Q^T (bf16 MFMA, FP32 accumulation), causal mask on logical
+//     positions (key j visible to a query at position p iff j <= p) on tiles that cross the
+//     diagonal, FP32 online softmax with a fixed reduction order, O^T += V^T P^T (P rounded
+//     to bf16 for the MFMA, FP32 accumulation).
 //  The tiling is a constant of the library, so each row's reduction order depends only on
 //  the row itself, never on the batch or the plan width.
 #include "pa_internal.h"
@@ -26,108 +28,134 @@ namespace pa {
 
 namespace {
 
-constexpr int kQBlock = 32;   // queries per wavefront (two 16-row MFMA tiles)
-constexpr int kKTile = 64;    // keys per tile (4 pages)
-constexpr int kVRow = kHeadDim + 8;
+constexpr int kQBlock = 32;          // queries per wavefront (two 16-row MFMA tiles)
+constexpr int kQT = kQBlock / 16;
+constexpr int kKT = 32;              // keys per tile (2 pages)
+constexpr int kRow = kHeadDim + 8;   // LDS row, padded by 16 bytes
+constexpr int kAttendThreads = 256;
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(uint16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
-
 __device__ __forceinline__ uint4 as_u4(const bf16x8& v) { return __builtin_bit_cast(uint4, v); }
 
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 // ---------------------------------------------------------------------------------------
-// 1. prologue
+// 1. k^ for every cached key
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prologue_kernel(const PrefillParams P, uint16_t* __restrict__ qh,
-                                                       uint16_t* __restrict__ kh) {
+__global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int nq = P.batch * P.num_q_heads * P.q_len;
-  const int q_tiles = (nq + 15) / 16;
   const int k_tiles = P.num_indices * P.num_kv_heads;
   const int waves = gridDim.x * (blockDim.x >> 6);
-  const bool qnorm = P.q_norm != nullptr;
   const bool knorm = P.k_norm != nullptr;
-  float qw[32], kw[32];
+  float kw[32];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qw[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
-      kw[kb * 8 + e] = knorm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
-    }
+    for (int e = 0; e < 8; ++e) kw[kb * 8 + e] = knorm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
   const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
-  for (int task = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); task < q_tiles + k_tiles; task += waves) {
-    uint4 raw[4];
-    bf16x8 op[4];
-    if (task < q_tiles) {
-      const int v = task * 16 + r;  // flattened (b, h, i)
-      const bool live = v < nq;
-      int pos = 0;
-      bool bad = false;
-      if (live) {
-        const int b = v / (P.num_q_heads * P.q_len);
-        const int i = v % P.q_len;
-        pos = P.qpos[(size_t)b * P.q_len + i];
-        if (pos < 0 || pos >= P.table_rows) { bad = true; pos = 0; }
-      }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.q + (size_t)v * kHeadDim + 32 * kb + 8 * g) : zero4;
-      float4 cs[8];
-      load_cos_sin(P.rope + (size_t)pos * kHeadDim, g, cs);
-      prologue_operand(raw, qw, qnorm, P.eps, cs, op);
-      if (live) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) stg16(qh + (size_t)v * kHeadDim + 32 * kb + 8 * g, bad ? nan4 : as_u4(op[kb]));
-      }
-    } else {
-      const int kt = task - q_tiles;
-      const int hk = kt / P.num_indices;
-      const int gp = kt % P.num_indices;  // page slot in kv_indices
-      // row owning this page slot: last b with indptr[b] <= gp
-      int lo = 0, hi = P.batch;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (P.indptr[mid] <= gp) lo = mid; else hi = mid;
-      }
-      const int b = lo;
-      const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
-      const int n = p1 - p0, pr = gp - p0;
-      const int lpl = P.last_page_len[b];
-      const bool row_ok = p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && pr >= 0 &&
-                          pr < n && lpl >= 1 && lpl <= kPageSize;
-      const int L = row_ok ? (n - 1) * kPageSize + lpl : 0;
-      const int j = pr * kPageSize + r;  // logical key index = key position
-      const bool live = row_ok && j < L;
-      int phys = P.indices[gp];
-      const bool page_ok = phys >= 0 && phys < P.num_pages;
-      if (!page_ok) phys = 0;
-      const size_t src = (((size_t)phys * kPageSize + r) * P.num_kv_heads + hk) * kHeadDim + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.k_cache + src + 32 * kb) : zero4;
-      float4 cs[8];
-      load_cos_sin(P.rope + (size_t)(live ? j : 0) * kHeadDim, g, cs);
-      prologue_operand(raw, kw, knorm, P.eps, cs, op);
-      uint16_t* dst = kh + ((size_t)hk * P.num_indices * kPageSize + (size_t)gp * kPageSize + r) * kHeadDim + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !page_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
+  for (int kt = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); kt < k_tiles; kt += waves) {
+    const int hk = kt / P.num_indices;
+    const int gp = kt % P.num_indices;  // page slot in kv_indices
+    // row owning this page slot: last b with indptr[b] <= gp
+    int lo = 0, hi = P.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.indptr[mid] <= gp) lo = mid; else hi = mid;
     }
+    const int b = lo;
+    const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
+    const int n = p1 - p0, pr = gp - p0;
+    const int lpl = P.last_page_len[b];
+    const bool row_ok = p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && pr >= 0 &&
+                        pr < n && lpl >= 1 && lpl <= kPageSize;
+    const int L = row_ok ? (n - 1) * kPageSize + lpl : 0;
+    const int j = pr * kPageSize + r;  // logical key index = key position
+    const bool live = row_ok && j < L;
+    int phys = P.indices[gp];
+    const bool page_ok = phys >= 0 && phys < P.num_pages;
+    if (!page_ok) phys = 0;
+    const size_t src = (((size_t)phys * kPageSize + r) * P.num_kv_heads + hk) * kHeadDim + 8 * g;
+    uint4 raw[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.k_cache + src + 32 * kb) : zero4;
+    float4 cs[8];
+    load_cos_sin(P.rope + (size_t)(live ? j : 0) * kHeadDim, g, cs);
+    bf16x8 op[4];
+    prologue_operand(raw, kw, knorm, P.eps, cs, op);
+    uint16_t* dst = kh + ((size_t)hk * P.num_indices * kPageSize + (size_t)gp * kPageSize + r) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !page_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. causal attention over the prepared q^ / k^ and the paged V
+// 2. causal attention: q^ made here, k^ from the workspace, V from the pages
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attend_kernel(const PrefillParams P, const uint16_t* __restrict__ qh,
-                                                      const uint16_t* __restrict__ kh) {
-  __shared__ uint16_t sv[kKTile][kVRow];
-  __shared__ int s_poison;
+struct AttendSmem {
+  uint16_t k[2][kKT][kRow];
+  uint16_t v[2][kKT][kRow];
+};
+
+// The tile's share of one thread: k^ and V rows rt and rt + 16 of the tile (rt = tid / 16), 16
+// bytes each at column chunk tid % 16.  Keys past the row's end read the row's last key, so
+// every load is in bounds and finite (their scores are masked and their probabilities are 0).
+struct TileRegs {
+  uint4 k[2];
+  uint4 v[2];
+};
+
+// Physical pages of tile kt's two halves (wave-uniform scalar loads), bounds-checked.
+struct TilePages {
+  int phys[2];
+};
+
+__device__ __forceinline__ TilePages tile_pages(const PrefillParams& P, int p0, int L, int kt, int& poison) {
+  TilePages tp;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int pg = min(kt * kKT + 16 * u, L - 1) / kPageSize;  // the 16 rows of half u lie in one page
+    int phys = load_uniform(P.indices, p0 + pg);
+    if (phys < 0 || phys >= P.num_pages) { poison = 1; phys = 0; }
+    tp.phys[u] = phys;
+  }
+  return tp;
+}
+
+__device__ __forceinline__ void load_tile(TileRegs& tr, const PrefillParams& P, const uint16_t* kh_row0,
+                                          const TilePages& tp, int L, int hk, int kt, int tid) {
+  const int rt = tid >> 4;
+  const int col = tid & 15;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = min(kt * kKT + 16 * u + rt, L - 1);  // logical key (clamped)
+    tr.k[u] = ldg16(kh_row0 + (size_t)j * kHeadDim + col * 8);
+    tr.v[u] = ldg16(P.v_cache + (((size_t)tp.phys[u] * kPageSize + (j % kPageSize)) * P.num_kv_heads + hk) * kHeadDim +
+                    col * 8);
+  }
+}
+
+__device__ __forceinline__ void store_tile(const TileRegs& tr, AttendSmem& sm, int buf, int tid) {
+  const int rt = tid >> 4;
+  const int col = tid & 15;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    *reinterpret_cast<uint4*>(&sm.k[buf][16 * u + rt][col * 8]) = tr.k[u];
+    *reinterpret_cast<uint4*>(&sm.v[buf][16 * u + rt][col * 8]) = tr.v[u];
+  }
+}
+
+__global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillParams P,
+                                                                const uint16_t* __restrict__ kh) {
+  __shared__ AttendSmem sm;
   const int G = P.group;
   const int Hkv = P.num_kv_heads;
-  const int nqb = (P.q_len + kQBlock - 1) / kQBlock;
+  const int Sq = P.q_len;
+  const int nqb = (Sq + kQBlock - 1) / kQBlock;
   // longest work first: the last query blocks of every row see the most keys
   const int nhg = (G + 3) / 4;
   const int per_qb = P.batch * Hkv * nhg;
@@ -138,15 +166,13 @@ __global__ __launch_bounds__(256) void attend_kernel(const PrefillParams P, cons
   const int b = rest / Hkv;
   const int hk = rest % Hkv;
   const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int gi = hg * 4 + wave;          // head within the GQA group
-  const bool head_live = gi < G;         // trailing waves of a partial group only help stage V
+  const int gi = hg * 4 + wave;       // head within the GQA group
+  const bool head_live = gi < G;      // trailing waves of a partial group only help stage tiles
   const int h = hk * G + (head_live ? gi : 0);
-  const int Sq = P.q_len;
 
   const int p0 = P.indptr[b];
   const int p1 = P.indptr[b + 1];
@@ -156,133 +182,182 @@ __global__ __launch_bounds__(256) void attend_kernel(const PrefillParams P, cons
                    (n > 0 && (lpl < 1 || lpl > kPageSize));
   const int L = (n > 0 && !bad) ? (n - 1) * kPageSize + lpl : 0;
 
-  // positions of this lane's two queries (-1: past the chunk, sees nothing)
-  int qp[2];
-  int i_of[2];
+  // positions of this lane's queries (-1: past the chunk, sees nothing)
+  int qp[kQT];
+  int i_of[kQT];
+  int poison = bad;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kQT; ++t) {
     const int i = qb * kQBlock + 16 * t + r;
     i_of[t] = i;
     qp[t] = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
+    if (qp[t] >= P.table_rows) { poison = 1; qp[t] = -1; }
   }
-  // last key any query of the block can see
-  int qmax = max(qp[0], qp[1]);
-  qmax = max(qmax, __shfl_xor(qmax, 1));
-  qmax = max(qmax, __shfl_xor(qmax, 2));
-  qmax = max(qmax, __shfl_xor(qmax, 4));
-  qmax = max(qmax, __shfl_xor(qmax, 8));
+  // first and last key positions any query of the block can see
+  int qmax = qp[0], qmin = qp[0] < 0 ? INT32_MAX : qp[0];
+#pragma unroll
+  for (int t = 1; t < kQT; ++t) {
+    qmax = max(qmax, qp[t]);
+    if (qp[t] >= 0) qmin = min(qmin, qp[t]);
+  }
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) {
+    qmax = max(qmax, __shfl_xor(qmax, sh));
+    qmin = min(qmin, __shfl_xor(qmin, sh));
+  }
+  // identical in every lane after the exchange: make them wave-uniform (scalar)
+  qmax = __builtin_amdgcn_readfirstlane(qmax);
+  qmin = __builtin_amdgcn_readfirstlane(qmin);
   const int kend = min(L, qmax + 1);
-  const int ntiles = kend > 0 ? (kend + kKTile - 1) / kKTile : 0;
+  const int ntiles = kend > 0 ? (kend + kKT - 1) / kKT : 0;
+  // tiles ending at or before this key need no mask: every key is < L and <= every query
+  const int free_end = min(L, qmin == INT32_MAX ? 0 : qmin + 1);
 
-  if (tid == 0) s_poison = 0;
-
-  bf16x8 qop[2][4];
+  // q^ of this wavefront's queries, in the operand layout (vector r = query 16t + r)
+  bf16x8 qop[kQT][4];
+  {
+    const bool qnorm = P.q_norm != nullptr;
+    float w[32];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const size_t off = (((size_t)b * P.num_q_heads + h) * Sq + i_of[t]) * kHeadDim + 32 * kb + 8 * g;
-      qop[t][kb] = __builtin_bit_cast(bf16x8, (head_live && i_of[t] < Sq) ? ldg16(qh + off) : make_uint4(0, 0, 0, 0));
+      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      uint4 raw[4];
+      const bool live = head_live && i_of[t] < Sq;
+      const size_t off = (((size_t)b * P.num_q_heads + h) * Sq + (live ? i_of[t] : 0)) * kHeadDim + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.q + off + 32 * kb) : make_uint4(0, 0, 0, 0);
+      float4 cs[8];
+      load_cos_sin(P.rope + (size_t)max(qp[t], 0) * kHeadDim, g, cs);
+      prologue_operand(raw, w, qnorm, P.eps, cs, qop[t]);
     }
+  }
 
-  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l_run[2] = {0.0f, 0.0f};
-  f32x4 acc[2][8];
+  float m_run[kQT], l_run[kQT];
+  f32x4 acc[kQT][8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < kQT; ++t) {
+    m_run[t] = -__builtin_inff();
+    l_run[t] = 0.0f;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const size_t kh_head = (size_t)hk * P.num_indices * kPageSize;
+  }
+  const uint16_t* kh_row0 = kh + ((size_t)hk * P.num_indices + p0) * kPageSize * kHeadDim;  // key 0 of the row
+  const int jr = 4 * g + (r >> 2);  // transposed-read row within a 16-key subtile
+  const int jc = 4 * (r & 3);
+
+  // Tiles kt+1 .. kt+3 are in flight (a ring of three register sets) while tile kt is used
+  // from LDS; tile kt+1 goes to the other LDS buffer at the end of the step.  The page indices
+  // of a tile are loaded one step before its data.
+  constexpr int kRing = 3;
+  TileRegs ring[kRing];
+  TilePages pages_next{{0, 0}};
+  if (ntiles > 0) {
+    load_tile(ring[0], P, kh_row0, tile_pages(P, p0, L, 0, poison), L, hk, 0, tid);
+#pragma unroll
+    for (int u = 1; u < kRing; ++u)
+      if (u < ntiles) load_tile(ring[u], P, kh_row0, tile_pages(P, p0, L, u, poison), L, hk, u, tid);
+    if (kRing < ntiles) pages_next = tile_pages(P, p0, L, kRing, poison);
+    store_tile(ring[0], sm, 0, tid);
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // stage the V tile [64 keys][128 dims] from the pages (zeros past the row's end)
-    for (int s = tid; s < kKTile * 16; s += nthreads) {
-      const int row = s >> 4, col = s & 15;
-      const int j = kt * kKTile + row;
-      const int pr = j / kPageSize;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < L) {
-        int phys = P.indices[p0 + pr];
-        if (phys < 0 || phys >= P.num_pages) { s_poison = 1; phys = 0; }
-        v = ldg16(P.v_cache + (((size_t)phys * kPageSize + (j % kPageSize)) * Hkv + hk) * kHeadDim + col * 8);
-      }
-      *reinterpret_cast<uint4*>(&sv[row][col * 8]) = v;
+  auto step = [&](const int kt, TileRegs& done, TileRegs& following) {
+    // `done`: the registers of tile kt (already in LDS), free to take tile kt+kRing;
+    // `following`: the registers of tile kt+1
+    const int buf = kt & 1;
+    if (kt + kRing < ntiles) {
+      load_tile(done, P, kh_row0, pages_next, L, hk, kt + kRing, tid);
+      if (kt + kRing + 1 < ntiles) pages_next = tile_pages(P, p0, L, kt + kRing + 1, poison);
     }
-    __syncthreads();
-
-    f32x4 sc[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int pr = kt * 4 + ks;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sc[t][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (pr < n && head_live) {
-        bf16x8 ka[4];
-        const uint16_t* src = kh + (kh_head + (size_t)(p0 + pr) * kPageSize + r) * kHeadDim + 8 * g;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ka[kb] = __builtin_bit_cast(bf16x8, ldg16(src + 32 * kb));
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
+    if (head_live) {
+        // S^T = K^ Q^T for the tile's two 16-key subtiles
+        f32x4 sc[kQT][2];
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 ka[4];
+  #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
-            sc[t][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], sc[t][ks], 0, 0, 0);
-      }
-    }
-
-    i16x4 pb[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float tv[4][4];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = kt * kKTile + 16 * ks + 4 * g + i;
-          tv[ks][i] = (j < L && j <= qp[t]) ? sc[t][ks][i] * kScoreScaleLog2 : -__builtin_inff();
-          mx = fmaxf(mx, tv[ks][i]);
+            ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
+  #pragma unroll
+          for (int t = 0; t < kQT; ++t) {
+            sc[t][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+              sc[t][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], sc[t][ks], 0, 0, 0);
+          }
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[t], mx);
-      const bool any = m_new != -__builtin_inff();
-      const float alpha = any ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.0f;
-      float ps = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = any ? __builtin_amdgcn_exp2f(tv[ks][i] - m_new) : 0.0f;
-          ps += p;
-          pb[t][ks][i] = __builtin_bit_cast(short, (__bf16)p);
+        const bool masked = (kt + 1) * kKT > free_end;
+        i16x4 pb[kQT][2];
+  #pragma unroll
+        for (int t = 0; t < kQT; ++t) {
+          // the row max is taken on raw scores (the scale is positive), the scale is folded into
+          // the exponent: p = exp2(s * c - m) with one fused multiply-add
+          float sv_[2][4];
+          float mx = -__builtin_inff();
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float v = sc[t][ks][i];
+              if (masked) {
+                const int j = kt * kKT + 16 * ks + 4 * g + i;
+                v = (j < L && j <= qp[t]) ? v : -__builtin_inff();
+              }
+              sv_[ks][i] = v;
+              mx = fmaxf(mx, v);
+            }
+          mx = pair32_max(pair16_max(mx));
+          const float m_new = fmaxf(m_run[t], mx * kScoreScaleLog2);
+          const bool any = m_new != -__builtin_inff();
+          const float alpha = any ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.0f;
+          float ps = 0.0f;
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float p = any ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv_[ks][i], kScoreScaleLog2, -m_new)) : 0.0f;
+              ps += p;
+              pb[t][ks][i] = __builtin_bit_cast(short, (__bf16)p);
+            }
+          ps = pair32_sum(pair16_sum(ps));
+          l_run[t] = __builtin_fmaf(l_run[t], alpha, ps);
+          m_run[t] = m_new;
+          if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+  #pragma unroll
+            for (int nb = 0; nb < 8; ++nb) acc[t][nb] = acc[t][nb] * alpha;
+          }
         }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run[t] = l_run[t] * alpha + ps;
-      m_run[t] = m_new;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) acc[t][nb] = acc[t][nb] * alpha;
-    }
-
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (kt * 4 + ks >= n || !head_live) continue;
-        i16x4 va;  // V^T rows: dim 16*nb + r, keys 16*ks + 4g .. +3
-#pragma unroll
-        for (int e = 0; e < 4; ++e) va[e] = (short)sv[16 * ks + 4 * g + e][16 * nb + r];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[t][ks], acc[t][nb], 0, 0, 0);
+        // O^T += V^T P^T; V^T by transposed LDS reads
+  #pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const i16x4 va =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][16 * ks + jr][16 * nb + jc]));
+  #pragma unroll
+            for (int t = 0; t < kQT; ++t)
+              acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[t][ks], acc[t][nb], 0, 0, 0);
+          }
+        }
       }
-    }
+    if (kt + 1 < ntiles) store_tile(following, sm, buf ^ 1, tid);
     __syncthreads();
+  };
+  for (int kt = 0; kt < ntiles; kt += kRing) {
+    step(kt, ring[0], ring[1]);
+    if (kt + 1 >= ntiles) break;
+    step(kt + 1, ring[1], ring[2]);
+    if (kt + 2 >= ntiles) break;
+    step(kt + 2, ring[2], ring[0]);
   }
 
-  const bool poison = bad || s_poison != 0;
+  // any out-of-range page index seen by any thread poisons the whole block's output
+  const bool out_poison = __syncthreads_or(poison) != 0;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kQT; ++t) {
     const int i = i_of[t];
     if (i >= Sq || !head_live) continue;
     const size_t row = ((size_t)b * P.num_q_heads + h) * Sq + i;
@@ -293,14 +368,14 @@ __global__ __launch_bounds__(256) void attend_kernel(const PrefillParams P, cons
       uint2 w;
       float o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = poison ? __builtin_nanf("") : acc[t][nb][e] * inv;
+      for (int e = 0; e < 4; ++e) o[e] = out_poison ? __builtin_nanf("") : acc[t][nb][e] * inv;
       w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[1]) << 16);
       w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[3]) << 16);
       *reinterpret_cast<uint2*>(P.out + row * kHeadDim + 16 * nb + 4 * g) = w;
     }
     if (g == 0) {
       float lse = empty ? -__builtin_inff() : (m_run[t] + __builtin_log2f(l_run[t])) * kLn2;
-      if (poison) lse = __builtin_nanf("");
+      if (out_poison) lse = __builtin_nanf("");
       P.lse[row] = lse;
     }
   }
@@ -309,17 +384,16 @@ __global__ __launch_bounds__(256) void attend_kernel(const PrefillParams P, cons
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  uint16_t* qh = (uint16_t*)p.workspace;
-  uint16_t* kh = (uint16_t*)((char*)p.workspace + align256((size_t)p.batch * p.num_q_heads * p.q_len * kHeadDim * 2));
-  const long long tasks = ((long long)p.batch * p.num_q_heads * p.q_len + 15) / 16 +
-                          (long long)p.num_indices * p.num_kv_heads;
-  const unsigned pro_blocks = (unsigned)std::min<long long>(std::max<long long>((tasks + 3) / 4, 1), 8192);
-  hipLaunchKernelGGL(prologue_kernel, dim3(pro_blocks), dim3(256), 0, stream, p, qh, kh);
+  uint16_t* kh = (uint16_t*)p.workspace;
+  const long long tasks = (long long)p.num_indices * p.num_kv_heads;
+  if (tasks > 0) {
+    const unsigned pro_blocks = (unsigned)std::min<long long>((tasks + 3) / 4, 8192);
+    hipLaunchKernelGGL(key_prologue_kernel, dim3(pro_blocks), dim3(256), 0, stream, p, kh);
+  }
   const unsigned nqb = (unsigned)((p.q_len + kQBlock - 1) / kQBlock);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
   const unsigned grid = nqb * (unsigned)p.batch * (unsigned)p.num_kv_heads * nhg;
-  const unsigned threads = 64u * (unsigned)std::min(p.group, 4);
-  if (grid > 0) hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(threads), 0, stream, p, qh, kh);
+  if (grid > 0) hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh);
   return hipGetLastError();
 }
 
