@@ -180,6 +180,7 @@ def main():
     ap.add_argument("--profile-copy", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="skip prefill and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the chunked prefill")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -222,8 +223,9 @@ def main():
         pa.decode(plan, *db.args(), out=out, lse=lse, workspace=ws)
 
     print("[bench] timing decode", file=sys.stderr, flush=True)
-    wall_ms, launch_ms = time_calls(step, sets, args.steps, args.warmup)
-    mc_wall_ms, mc_launch_ms = time_calls(step_multi, sets, args.steps, args.warmup)
+    dsteps = 2 if args.prefill_only else args.steps
+    wall_ms, launch_ms = time_calls(step, sets, dsteps, 0 if args.prefill_only else args.warmup)
+    mc_wall_ms, mc_launch_ms = time_calls(step_multi, sets, dsteps, 0 if args.prefill_only else args.warmup)
     alg = decode_bytes(base)
     value = alg / (wall_ms * 1e-3) / 1e9
     achieved = alg / (launch_ms * 1e-3) / 1e9

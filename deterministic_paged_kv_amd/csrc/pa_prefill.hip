@@ -19,7 +19,9 @@
 //     is used.  Per tile: S^T = K^ Q^T (bf16 MFMA, FP32 accumulation), causal mask on logical
 //     positions (key j visible to a query at position p iff j <= p) on tiles that cross the
 //     diagonal, FP32 online softmax with a fixed reduction order, O^T += V^T P^T (P rounded
-//     to bf16 for the MFMA, FP32 accumulation).
+//     to bf16 for the MFMA, FP32 accumulation).  The softmax reference of a query follows its
+//     running maximum lazily (moved only when exceeded by more than 2^8 in probability), which
+//     leaves out = sum(p v) / sum(p) and the LSE unchanged up to rounding.
 //  The tiling is a constant of the library, so each row's reduction order depends only on
 //  the row itself, never on the batch or the plan width.
 #include "pa_internal.h"
@@ -33,12 +35,20 @@ constexpr int kQT = kQBlock / 16;
 constexpr int kKT = 32;              // keys per tile (2 pages)
 constexpr int kRow = kHeadDim + 8;   // LDS row, padded by 16 bytes
 constexpr int kAttendThreads = 256;
+// A query's softmax reference is moved only when a tile's scaled score exceeds it by more
+// than this (log2 domain), so probabilities stay below 2^8 and rescaling is rare.
+constexpr float kLazyMax = 8.0f;
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(uint16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 __device__ __forceinline__ uint4 as_u4(const bf16x8& v) { return __builtin_bit_cast(uint4, v); }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i16x8 concat4(const i16x4& a, const i16x4& b) {
+  return i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
 // ---------------------------------------------------------------------------------------
 // 1. k^ for every cached key
@@ -235,12 +245,16 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
     }
   }
 
-  float m_run[kQT], l_run[kQT];
+  // Per query: reference m (log2 domain, scaled), m_neg = -m (0 while m is -inf), and this
+  // lane's partial sum of p over its own key slots (the four lanes of a query are summed once,
+  // in a fixed order, at the end).
+  float m_run[kQT], m_neg[kQT], l_part[kQT];
   f32x4 acc[kQT][8];
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
     m_run[t] = -__builtin_inff();
-    l_run[t] = 0.0f;
+    m_neg[t] = 0.0f;
+    l_part[t] = 0.0f;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -293,8 +307,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
         i16x4 pb[kQT][2];
   #pragma unroll
         for (int t = 0; t < kQT; ++t) {
-          // the row max is taken on raw scores (the scale is positive), the scale is folded into
-          // the exponent: p = exp2(s * c - m) with one fused multiply-add
+          // Raw scores (the scale c is positive, so maxima commute with it); masked keys -inf.
           float sv_[2][4];
           float mx = -__builtin_inff();
   #pragma unroll
@@ -309,38 +322,44 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
               sv_[ks][i] = v;
               mx = fmaxf(mx, v);
             }
-          mx = pair32_max(pair16_max(mx));
-          const float m_new = fmaxf(m_run[t], mx * kScoreScaleLog2);
-          const bool any = m_new != -__builtin_inff();
-          const float alpha = any ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.0f;
-          float ps = 0.0f;
+          // The reference m of a query moves only when the tile's largest scaled score exceeds it
+          // by more than kLazyMax; the test is exact per query (a lane's own keys are a subset of
+          // the query's), so the full reduction runs only when some query of the wave moves.
+          if (__builtin_amdgcn_ballot_w64(mx * kScoreScaleLog2 > m_run[t] + kLazyMax) != 0) {
+            const float rowmax = pair32_max(pair16_max(mx)) * kScoreScaleLog2;
+            if (rowmax > m_run[t] + kLazyMax) {
+              const float alpha = m_run[t] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run[t] - rowmax);
+              m_run[t] = rowmax;
+              m_neg[t] = -rowmax;
+              l_part[t] *= alpha;
+  #pragma unroll
+              for (int nb = 0; nb < 8; ++nb) acc[t][nb] = acc[t][nb] * alpha;
+            }
+          }
+          // p = 2^(s c - m) <= 2^kLazyMax; 0 for masked keys (and while m is still -inf, m_neg = 0)
   #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
   #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float p = any ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv_[ks][i], kScoreScaleLog2, -m_new)) : 0.0f;
-              ps += p;
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv_[ks][i], kScoreScaleLog2, m_neg[t]));
+              l_part[t] += p;
               pb[t][ks][i] = __builtin_bit_cast(short, (__bf16)p);
             }
-          ps = pair32_sum(pair16_sum(ps));
-          l_run[t] = __builtin_fmaf(l_run[t], alpha, ps);
-          m_run[t] = m_new;
-          if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-  #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) acc[t][nb] = acc[t][nb] * alpha;
-          }
         }
-        // O^T += V^T P^T; V^T by transposed LDS reads
+        // O^T += V^T P^T over the tile's 32 keys in one K=32 MFMA per (query tile, column block):
+        // k-slot 8g+e holds key 4g+e for e < 4 and key 16+4g+(e-4) for e >= 4, in both operands.
+        // V^T comes from two transposed LDS reads (one per 16-key subtile).
+        bf16x8 pk[kQT];
+  #pragma unroll
+        for (int t = 0; t < kQT; ++t) pk[t] = __builtin_bit_cast(bf16x8, concat4(pb[t][0], pb[t][1]));
   #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][jr][16 * nb + jc]));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][16 + jr][16 * nb + jc]));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, concat4(v0, v1));
   #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const i16x4 va =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][16 * ks + jr][16 * nb + jc]));
-  #pragma unroll
-            for (int t = 0; t < kQT; ++t)
-              acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[t][ks], acc[t][nb], 0, 0, 0);
-          }
+          for (int t = 0; t < kQT; ++t)
+            acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t], acc[t][nb], 0, 0, 0);
         }
       }
     if (kt + 1 < ntiles) store_tile(following, sm, buf ^ 1, tid);
@@ -356,6 +375,9 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
 
   // any out-of-range page index seen by any thread poisons the whole block's output
   const bool out_poison = __syncthreads_or(poison) != 0;
+  float l_run[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) l_run[t] = pair32_sum(pair16_sum(l_part[t]));
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
     const int i = i_of[t];
