@@ -18,10 +18,13 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # no packed FP32 instructions anywhere in the library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in ordinary VGPRs: the kernels rescale them on the VALU
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
+# MFMA accumulators in ordinary VGPRs: the kernels rescale them on the VALU
+EXTRA = {
+    "pa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _run(cmd):
@@ -35,7 +38,7 @@ def build_library(verbose: bool = False) -> str:
     """Compile every source and link libpa.so next to this file; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[HIPCC, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for r in ex.map(_run, cmds):
             if verbose and r.stderr:
