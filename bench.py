@@ -17,6 +17,9 @@ causally visible pairs) per call.  The CPU oracle is timed on a bounded sample o
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
        python bench.py --profile-copy     # plain copy of a known size, for counter scaling
+       python bench.py --ingest-counters FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
+           # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results of the decode run and of the copy
+           # -> profiles/decode_qwen3_8b_counters.json (HBM bytes per decode launch)
 """
 
 import argparse
@@ -133,29 +136,47 @@ def time_calls(fn, sets, steps, warmup):
     return wall_ms, launch_ms
 
 
-def cpu_baseline_decode(base, alg_bytes_fn):
-    """The CPU oracle on the first rows of the same decode batch, single thread."""
-    import numpy as np
+def host_cores() -> int:
+    """Cores this process may run on (the CPU share of the machine), capped at 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _time_oracle(b, min_seconds, max_reps):
+    """Median wall time of oracle.paged_attention on batch b, repeated until min_seconds of CPU
+    work have been spent (at least 3 runs, at most max_reps)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
-    import workloads
 
-    rows = list(range(4))
-    sub = workloads.PagedBatch(**{**base.__dict__})
-    sub_bytes = 0
-    with threadpool_limits(limits=1):
-        args, kwargs = base.oracle_args()
-        t0 = time.perf_counter()
-        oracle.paged_attention(*args, rows=rows, **kwargs)
-        dt = time.perf_counter() - t0
-    D = 128
-    L = base.lengths[rows]
-    sub_bytes = int(np.sum(L)) * base.num_kv_heads * D * 4 + len(rows) * base.num_q_heads * (D * 4 + 4)
-    del sub
-    return {"value": round(sub_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"rows {rows[0]}..{rows[-1]} of the B=32 decode batch (all 16 heads, "
-                      f"{int(np.sum(L))} keys), {dt:.1f} s, numpy with BLAS limited to 1 thread"}
+    cores = host_cores()
+    args, kwargs = b.oracle_args()
+    times = []
+    with threadpool_limits(limits=cores):
+        while len(times) < 3 or (sum(times) < min_seconds and len(times) < max_reps):
+            t0 = time.perf_counter()
+            oracle.paged_attention(*args, **kwargs)
+            times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2], len(times), sum(times), cores
+
+
+def cpu_baseline_decode(base, alg_bytes):
+    """The CPU oracle (float64 numpy) on the whole decode batch, ~10 s of repeated runs."""
+    dt, reps, total, cores = _time_oracle(base, 10.0, 40)
+    return {"value": round(alg_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole B=32 decode batch (all rows and heads): median of {reps} runs "
+                      f"({dt:.2f} s each, {total:.1f} s in all), float64 numpy with {cores} BLAS threads"}
+
+
+def cpu_baseline_prefill(b, flops):
+    """The CPU oracle on the whole chunked-prefill batch, ~10 s of repeated runs."""
+    dt, reps, total, cores = _time_oracle(b, 10.0, 20)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole chunked-prefill batch: median of {reps} runs ({dt:.2f} s each, "
+                      f"{total:.1f} s in all), float64 numpy with {cores} BLAS threads"}
 
 
 def profile_copy():
@@ -172,6 +193,51 @@ def profile_copy():
     print(json.dumps({"copy_bytes": n}))
 
 
+def _counter_mean(path, counter, kernel_substr):
+    """Mean per-dispatch value of one counter over the dispatches whose kernel name contains
+    kernel_substr, from a rocprofv3 counter_collection.csv."""
+    import csv
+
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr!r} in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for a plain 1 GiB copy (which moves exactly 1 GiB each way)."""
+    import workloads
+
+    copy_bytes = 1 << 30
+    cf, _ = _counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    fk, nf = _counter_mean(fetch_csv, "FETCH_SIZE", "decode_unit_kernel")
+    wk, nw = _counter_mean(write_csv, "WRITE_SIZE", "decode_unit_kernel")
+    fetch = fk * 1024.0 * f_scale
+    write = wk * 1024.0 * w_scale
+    alg = decode_bytes(workloads.qwen3_8b_decode(canary=False))
+    doc = {
+        "kernel": "decode_unit_kernel", "workload": "qwen3_8b_decode",
+        "source_hash": source_hash(DECODE_SOURCES),
+        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "dispatches": [nf, nw],
+        "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "hbm_bytes_per_launch": int(round(fetch + write)),
+        "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": round((fetch + write) / alg, 4),
+    }
+    out = os.path.join(ROOT, "profiles", "decode_qwen3_8b_counters.json")
+    with open(out, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(doc))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,7 +247,11 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="skip prefill and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the chunked prefill")
+    ap.add_argument("--ingest-counters", nargs=4, metavar="CSV")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               f"multi-GPU path: rows and heads shard across GPUs with no exchange, see the design notes.",
@@ -283,8 +353,9 @@ def main():
                          "algorithmic_flops_per_call": flops, "avg_call_ms": round(p_launch, 5)},
         }
         if not args.no_cpu_baseline:
-            print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-            result["cpu_baseline"] = cpu_baseline_decode(base, decode_bytes)
+            print("[bench] timing the CPU oracle (decode, then prefill)", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = cpu_baseline_decode(base, alg)
+            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pb, flops)
     print(json.dumps(result), flush=True)
 
 
