@@ -194,10 +194,11 @@ def decode_workspace_size(plan: Plan, batch: int) -> int:
 
 
 def decode_workspace(plan: Plan, batch: int, device="cuda"):
-    """A zeroed workspace for pa_decode's multi-compute-unit schedule (reusable across calls)."""
+    """A workspace for pa_decode's multi-compute-unit schedule (needs no initialisation and
+    can be reused by calls that do not overlap in time)."""
     import torch
 
-    return torch.zeros(decode_workspace_size(plan, batch), dtype=torch.uint8, device=device)
+    return torch.empty(decode_workspace_size(plan, batch), dtype=torch.uint8, device=device)
 
 
 def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, query_position_ids,

@@ -24,20 +24,32 @@ pa_status check_device(pa_plan_t plan) {
 // cos/sin of the RoPE angles: frequency i of position p has angle (p / scale) * theta^(-2i/D),
 // formed and evaluated in float64 and rounded once to float32 ("WS2 PR7 Fused Attention
 // Backend Alignment", section "FlashInfer RoPE Fusion": Llama RoPE, theta 1e6, scale 1.0,
-// rotary_dim = head_dim).  Row p holds cos[0..63] then sin[0..63].
+// rotary_dim = head_dim).
+//
+// Layout (the order in which the kernels' lanes use the values): positions come in blocks of
+// 16; block B holds [e = 0..7][lane = 0..63][4 floats], where lane = r + 16 g serves position
+// 16 B + r for lane group g, and float c of entry e is
+//   e = 0..3: cos of frequency f(e, g) + c,  e = 4..7: sin of frequency f(e - 4, g) + c,
+//   f(q, g) = 8 g + 4 q (q = 0, 1),  32 + 8 g + 4 (q - 2) (q = 2, 3),
+// i.e. a lane's 32 values are the cos and sin of its frequencies 8g..8g+7 and 32+8g..32+8g+7,
+// the partners of its head dimensions 32 kb + 8 g + 0..7 in the rotate-half pairing.
 std::vector<float> rope_table(int rows, double theta, double scale) {
   std::vector<double> inv_freq(kHalfDim);
   for (int i = 0; i < kHalfDim; ++i) inv_freq[i] = std::pow(theta, -(2.0 * i) / kHeadDim);
-  std::vector<float> t((size_t)rows * kHeadDim);
-  for (int p = 0; p < rows; ++p) {
-    const double pos = (double)p / scale;
-    float* row = t.data() + (size_t)p * kHeadDim;
-    for (int i = 0; i < kHalfDim; ++i) {
-      const double a = pos * inv_freq[i];
-      row[i] = (float)std::cos(a);
-      row[kHalfDim + i] = (float)std::sin(a);
-    }
-  }
+  const int blocks = (rows + kPageSize - 1) / kPageSize;
+  std::vector<float> t((size_t)blocks * kRopeBlockFloats);
+  for (int blk = 0; blk < blocks; ++blk)
+    for (int e = 0; e < 8; ++e)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int r = lane & 15, g = lane >> 4, q = e & 3;
+        const double pos = (double)(blk * kPageSize + r) / scale;
+        const int f0 = q < 2 ? 8 * g + 4 * q : 32 + 8 * g + 4 * (q - 2);
+        float* dst = t.data() + (size_t)blk * kRopeBlockFloats + ((size_t)e * 64 + lane) * 4;
+        for (int c = 0; c < 4; ++c) {
+          const double a = pos * inv_freq[f0 + c];
+          dst[c] = (float)(e < 4 ? std::cos(a) : std::sin(a));
+        }
+      }
   return t;
 }
 

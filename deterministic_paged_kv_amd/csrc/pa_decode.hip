@@ -25,8 +25,8 @@
 //  * one workgroup of 8 wavefronts per (row, KV head), stream s on wavefront s, states
 //    combined through LDS (no workspace);
 //  * one single-wavefront workgroup per (row, KV head, stream), states written to a caller
-//    workspace, and the last workgroup of each (row, KV head) to finish (per-unit counter)
-//    combines them.  This spreads a long row over 8 compute units; the bits are identical.
+//    workspace, and a second kernel that combines each unit's states in stream order.  This
+//    spreads a long row over 8 compute units; the bits are identical.
 //
 // Memory layout.  k_cache/v_cache are NHD [page][slot][Hkv][128] bf16: one KV head of one
 // page is 16 rows of 256 B at a stride of Hkv * 256 B.  A lane (r = lane % 16, g = lane / 16)
@@ -42,6 +42,11 @@ namespace {
 
 constexpr int kStreams = 8;                  // streams of the reduction tree
 constexpr int kDecodeThreads = kStreams * 64;
+// pages in flight per wavefront: the unit schedule runs 2 wavefronts per SIMD, the
+// multi-CU schedule one or two with the register file to itself
+constexpr int kUnitRing = 2;
+constexpr int kStreamRing = 4;
+constexpr int kStreamCsRing = 2;
 // V staging rows are padded by 16 bytes to spread the transposed reads over the LDS banks.
 constexpr int kVRow = kHeadDim + 8;
 typedef uint16_t VSlot[kPageSize][kVRow];
@@ -93,6 +98,7 @@ __device__ __forceinline__ void issue_page(PageIn& in, const DecodeParams& P, in
 }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 // Softmax state of one stream: running max and sum of head r (in every lane with that r),
 // and O^T (lane (r, g) holds dims 16*nb + 4g + i of head r).
@@ -108,9 +114,9 @@ struct Scored {
 
 // Scores of page pg: stage V in LDS, run the K prologue, S^T = K^ Q^T, and advance the
 // running max and sum.  Lane (r, g) holds keys 4g+i of head r.
-__device__ __forceinline__ Scored score_page(const PageIn& in, float4 cs[8], const float* cs_next, int pg,
-                                             StreamState& st, const bf16x8 qop[4], const float* kw, bool knorm,
-                                             float eps, int L, int qp, int r, int g, VSlot& sv) {
+__device__ __forceinline__ Scored score_page(const PageIn& in, const float4 cs[8], int pg, StreamState& st,
+                                             const bf16x8 qop[4], const float* kw, bool knorm, float eps, int L,
+                                             int qp, int r, int g, VSlot& sv) {
 #pragma clang fp contract(off)
   // keys at or past `live_end` are invisible (past the row, or after the query): only a row's
   // last pages have any, so the masking sits behind a wave-uniform test
@@ -128,7 +134,6 @@ __device__ __forceinline__ Scored score_page(const PageIn& in, float4 cs[8], con
 
   bf16x8 kop[4];
   prologue_operand_lds_w(in.k, kw, knorm, eps, cs, g, kop);
-  load_cos_sin(cs_next, g, cs);  // the next page's cos/sin go in flight as soon as these are used
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], qop[kb], s, 0, 0, 0);
@@ -178,45 +183,71 @@ __device__ __forceinline__ void pv_page(const Scored& sc, StreamState& st, int r
   }
   // V^T operand by transposed LDS reads: in each 16-lane group g, lane j points at keys
   // 4g + j/4, dims 16*nb + 4*(j%4) .. +3; lane r then receives keys 4g .. 4g+3 of dim 16*nb + r.
+  // One K=32 MFMA takes both parts of P: k-slots 8g..8g+3 pair V rows 4g..4g+3 with P_hi,
+  // k-slots 8g+4..8g+7 pair the same rows with P_lo.
   const int jr = 4 * g + (r >> 2);
   const int jc = 4 * (r & 3);
+  const bf16x8 pb = __builtin_bit_cast(
+      bf16x8, i16x8{sc.p_hi[0], sc.p_hi[1], sc.p_hi[2], sc.p_hi[3], sc.p_lo[0], sc.p_lo[1], sc.p_lo[2], sc.p_lo[3]});
+  // all eight reads in flight before the first MFMA consumes one
+  i16x4 va[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) va[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sv[jr][16 * nb + jc]));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sv[jr][16 * nb + jc]));
-    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, sc.p_hi, st.acc[nb], 0, 0, 0);
-    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, sc.p_lo, st.acc[nb], 0, 0, 0);
+    const bf16x8 vv =
+        __builtin_bit_cast(bf16x8, i16x8{va[nb][0], va[nb][1], va[nb][2], va[nb][3], va[nb][0], va[nb][1], va[nb][2], va[nb][3]});
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, st.acc[nb], 0, 0, 0);
   }
 }
 
 // Stream s of one (row, KV head) unit on one wavefront: pages s, s+8, s+16, ...
 // sv: this wavefront's V staging slot; kw: the K norm weights in LDS (or 1.0 without norm).
+// R pages of K and V are in flight: page t of the stream (t = 0, 1, ...) sits in ring slot
+// t % R, and once it is scored the slot is refilled with page t + R.  The cos/sin rows of the
+// keys (mostly cache hits, read by every KV head) run RC pages ahead in a ring of their own.
+// The physical page numbers come 64 at a time in one vector load (lane l: the stream's page
+// 64 blk + l) and are taken out with readlane, so they never wait behind other loads.
+// Pages past the row's end are loaded from the row's last page (their data is never used),
+// so every step issues the same loads.
+template <int R, int RC>
 __device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo& ri, int hk, int s, int lane,
                                            VSlot& sv, const float* kw, StreamState& st) {
+  static_assert(R % RC == 0, "the cos/sin ring must divide the K/V ring");
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = P.group;
   const int n = ri.n, L = ri.L, qp = ri.qp, p0 = ri.p0;
   const bool qnorm = P.q_norm != nullptr;
   const bool knorm = P.k_norm != nullptr;
+  const int steps = (n - s + kStreams - 1) / kStreams;  // pages of this stream (n > s or 0)
 
-  // The stream's first two pages go in flight first.  Pages past the row's end are still
-  // loaded (from the row's last page), so every iteration issues the same loads; their data
-  // is never used.
   st.poison = 0;
-  auto phys_of = [&](int pg) {
-    int phys = load_uniform(P.indices, p0 + min(pg, n - 1));
-    if (phys < 0 || phys >= P.num_pages) { st.poison |= pg < n; phys = 0; }
+  // lane l's page slot for block blk: the stream's page 64 blk + l, clamped to the row
+  auto index_block = [&](int blk) {
+    const int pg = min(s + (64 * blk + lane) * kStreams, n - 1);
+    return P.indices[p0 + pg];
+  };
+  int vcur = index_block(0);
+  int vnext = index_block(1);
+  int cur_blk = 0;
+  auto phys_at = [&](int t) {  // physical page of the stream's page t (t within blocks cur_blk, +1)
+    const int a = __builtin_amdgcn_readlane(vcur, t & 63);
+    const int c = __builtin_amdgcn_readlane(vnext, t & 63);
+    int phys = (t >> 6) == cur_blk ? a : c;
+    if (phys < 0 || phys >= P.num_pages) { st.poison |= t < steps; phys = 0; }
     return phys;
   };
-  int pgA = s, pgB = s + kStreams;
-  PageIn inA, inB;
-  issue_page(inA, P, phys_of(pgA), hk, r, g);
-  issue_page(inB, P, phys_of(pgB), hk, r, g);
-  // table row of page pg's key r (pages past the end read the last page's rows)
-  auto rope_row = [&](int pg) { return P.rope + (size_t)(min(pg, n - 1) * kPageSize + r) * kHeadDim; };
-  float4 cs[8];  // cos/sin of the next page to score
-  load_cos_sin(rope_row(pgA), g, cs);
-  int physA = phys_of(pgA + 2 * kStreams), physB = phys_of(pgB + 2 * kStreams);
+  // position of key r of the stream's page t (pages past the end read the last page's)
+  auto key_pos = [&](int t) { return min(s + t * kStreams, n - 1) * kPageSize + r; };
+
+  PageIn in[R];
+  float4 cs[RC][8];
+#pragma unroll
+  for (int k = 0; k < R; ++k) issue_page(in[k], P, phys_at(k), hk, r, g);
+#pragma unroll
+  for (int c = 0; c < RC; ++c) load_cos_sin(P.rope, key_pos(c), g, cs[c]);
 
   // q^ of the group's heads in the operand layout (vector r = head r < G)
   bf16x8 qop[4];
@@ -231,7 +262,7 @@ __device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo&
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
     }
-    load_cos_sin(P.rope + (size_t)qp * kHeadDim, g, qcs);
+    load_cos_sin(P.rope, qp, g, qcs);
     prologue_operand(raw, w, qnorm, P.eps, qcs, qop);
   }
 
@@ -240,25 +271,27 @@ __device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo&
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Pages alternate between two register buffers: while one page is scored and accumulated,
-  // the next two are in flight.  Each page is scored and then accumulated before the next.
-  for (; pgA < n;) {
-    const Scored sa = score_page(inA, cs, rope_row(pgB), pgA, st, qop, kw, knorm, P.eps, L, qp, r, g, sv);
-    pgA += 2 * kStreams;
-    issue_page(inA, P, physA, hk, r, g);
-    physA = phys_of(pgA + 2 * kStreams);
-    wave_lds_sync();
-    pv_page(sa, st, r, g, sv);
-    wave_lds_sync();
-    if (pgB < n) {
-      const Scored sb = score_page(inB, cs, rope_row(pgA), pgB, st, qop, kw, knorm, P.eps, L, qp, r, g, sv);
+  for (int t0 = 0; t0 < steps; t0 += R) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int t = t0 + k;
+      if (t >= steps) continue;  // (not break: an early exit from the unrolled body costs registers)
+      const int c = k % RC;
+      const Scored sc = score_page(in[k], cs[c], s + t * kStreams, st, qop, kw, knorm, P.eps, L, qp, r, g, sv);
+      load_cos_sin(P.rope, key_pos(t + RC), g, cs[c]);
+      // refill the slot with page t + R; a new block of page numbers is due when t + R
+      // enters the next one
+      const int u = t + R;
+      if ((u & 63) == 0 && (u >> 6) != cur_blk) {
+        vcur = vnext;
+        cur_blk = u >> 6;
+        vnext = index_block(cur_blk + 1);
+      }
+      issue_page(in[k], P, phys_at(u), hk, r, g);
       wave_lds_sync();
-      pv_page(sb, st, r, g, sv);
+      pv_page(sc, st, r, g, sv);
       wave_lds_sync();
     }
-    pgB += 2 * kStreams;
-    issue_page(inB, P, physB, hk, r, g);
-    physB = phys_of(pgB + 2 * kStreams);
   }
 }
 
@@ -320,7 +353,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
   __syncthreads();
 
   StreamState st;
-  run_stream(P, ri, hk, wave, lane, sm.u.v[wave], sm.kw, st);
+  run_stream<kUnitRing, 1>(P, ri, hk, wave, lane, sm.u.v[wave], sm.kw, st);
 
   if (g == 0 && r < G) { sm.m[wave][r] = st.m; sm.l[wave][r] = st.l; }
   if (lane == 0) sm.poison[wave] = st.poison;
@@ -349,13 +382,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
 }
 
 // ---------------------------------------------------------------------------------------
-// Schedule 2: one single-wavefront workgroup per (unit, stream); states to the workspace;
-// the last workgroup of a unit combines.  Workspace: an int32 counter per unit (zero between
-// calls: the combining workgroup resets it), an int32 poison flag per (unit, stream), then
-// per unit and stream G records of [m, l, 128 accumulators].
+// Schedule 2: one single-wavefront workgroup per (unit, stream) writes its stream state to
+// the workspace; a second kernel combines each unit's states in stream order.  The kernel
+// boundary makes the states visible, so neither kernel needs a device-wide fence.
+// Workspace: an int32 poison flag per (unit, stream), then per unit and stream G records of
+// [m, l, 128 accumulators].
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void decode_stream_kernel(const DecodeParams P, int32_t* __restrict__ counters,
-                                                           int32_t* __restrict__ poisons, float* __restrict__ states) {
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_stream_kernel(
+    const DecodeParams P, int32_t* __restrict__ poisons, float* __restrict__ states) {
   __shared__ VSlot sv;
   __shared__ float kw[kHeadDim];
   const int unit = blockIdx.x / kStreams;
@@ -367,52 +403,54 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const DecodeParams P,
   const int g = lane >> 4;
   const int G = P.group;
   const RowInfo ri = row_info(P, b, hk);
-  if (ri.bad || ri.L == 0) {
-    if (s == 0) write_degenerate(P, ri, lane, 64);
-    return;
-  }
+  if (ri.bad || ri.L == 0) return;  // the combine kernel writes these rows
   for (int i = lane; i < kHeadDim; i += 64) kw[i] = P.k_norm != nullptr ? P.k_norm[i] : 1.0f;
   __syncthreads();
 
   StreamState st;
-  run_stream(P, ri, hk, s, lane, sv, kw, st);
+  run_stream<kStreamRing, kStreamCsRing>(P, ri, hk, s, lane, sv, kw, st);
 
   const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per stream state
-  float* unit_states = states + (size_t)unit * kStreams * rec;
   if (r < G) {
-    float* hrec = unit_states + (size_t)s * rec + (size_t)r * (2 + kHeadDim);
+    float* hrec = states + ((size_t)unit * kStreams + s) * rec + (size_t)r * (2 + kHeadDim);
     if (g == 0) { hrec[0] = st.m; hrec[1] = st.l; }
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<f32x4*>(hrec + 2 + 16 * nb + 4 * g) = st.acc[nb];
   }
   if (lane == 0) poisons[unit * kStreams + s] = st.poison;
-  // publish this stream's state, then count it
-  __threadfence();
-  int ticket = 0;
-  if (lane == 0) ticket = atomicAdd(&counters[unit], 1);
-  ticket = __shfl(ticket, 0);
-  if (ticket != kStreams - 1) return;
-  __threadfence();
+}
 
-  // last stream of the unit: combine in stream order
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeParams P,
+                                                                         const int32_t* __restrict__ poisons,
+                                                                         const float* __restrict__ states) {
+  const int unit = blockIdx.x;
+  const int b = unit / P.num_kv_heads;
+  const int hk = unit % P.num_kv_heads;
+  const int G = P.group;
+  const RowInfo ri = row_info(P, b, hk);
+  if (ri.bad || ri.L == 0) {
+    write_degenerate(P, ri, threadIdx.x, kCombineThreads);
+    return;
+  }
   int poison = 0;
+#pragma unroll
   for (int w = 0; w < kStreams; ++w) poison |= poisons[unit * kStreams + w];
-  for (int idx = lane; idx < G * kHeadDim; idx += 64) {
+  const size_t rec = (size_t)G * (2 + kHeadDim);
+  const float* unit_states = states + (size_t)unit * kStreams * rec;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kCombineThreads) {
     const int h = idx / kHeadDim, d = idx % kHeadDim;
     const float* base = unit_states + (size_t)h * (2 + kHeadDim);
     combine_one(P, ri, h, d, poison != 0, [&](int w) { return base[(size_t)w * rec]; },
                 [&](int w) { return base[(size_t)w * rec + 1]; },
                 [&](int w) { return base[(size_t)w * rec + 2 + d]; });
   }
-  if (lane == 0) counters[unit] = 0;
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int batch, int num_kv_heads, int group) {
   const size_t units = (size_t)batch * num_kv_heads;
-  return align256(units * sizeof(int32_t)) + align256(units * kStreams * sizeof(int32_t)) +
-         units * kStreams * group * (2 + kHeadDim) * sizeof(float);
+  return align256(units * kStreams * sizeof(int32_t)) + units * kStreams * group * (2 + kHeadDim) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t stream) {
@@ -422,13 +460,12 @@ hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t str
     hipLaunchKernelGGL(decode_unit_kernel, dim3(units), dim3(kDecodeThreads), 0, stream, p);
   } else {
     char* ws = (char*)workspace;
-    int32_t* counters = (int32_t*)ws;
-    ws += align256((size_t)units * sizeof(int32_t));
     int32_t* poisons = (int32_t*)ws;
     ws += align256((size_t)units * kStreams * sizeof(int32_t));
     float* states = (float*)ws;
-    hipLaunchKernelGGL(decode_stream_kernel, dim3(units * kStreams), dim3(64), 0, stream, p, counters, poisons,
-                       states);
+    hipLaunchKernelGGL(decode_stream_kernel, dim3(units * kStreams), dim3(64), 0, stream, p, poisons, states);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(units), dim3(kCombineThreads), 0, stream, p,
+                       (const int32_t*)poisons, (const float*)states);
   }
   return hipGetLastError();
 }

@@ -13,7 +13,8 @@ namespace pa {
 constexpr int kHeadDim = 128;
 constexpr int kPageSize = 16;
 constexpr int kHalfDim = kHeadDim / 2;
-constexpr int kMaxGroup = 16;  // query heads per KV head: the 16 rows of one MFMA tile
+constexpr int kMaxGroup = 16;
+constexpr int kRopeBlockFloats = 8 * 64 * 4;  // one block of 16 positions of the RoPE table  // query heads per KV head: the 16 rows of one MFMA tile
 
 // 1/sqrt(128) * log2(e), rounded once to FP32: scores are kept in the base-2 domain so the
 // softmax uses the hardware exp2; the LSE is converted back with ln(2) at the end.
@@ -173,10 +174,17 @@ __device__ __forceinline__ void prologue_operand_lds_w(const uint4 raw[4], const
     const float ms = (float)(ss * (1.0 / kHeadDim));
     const float t = ms + eps;
     const float inv = (float)(1.0 / __builtin_sqrt((double)t));
+    // the eight weight reads go out together (the LDS latency is paid once)
+    float4 wv[8];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const float4 w0 = *reinterpret_cast<const float4*>(w_lds + 32 * kb + 8 * g);
-      const float4 w1 = *reinterpret_cast<const float4*>(w_lds + 32 * kb + 8 * g + 4);
+      wv[2 * kb] = *reinterpret_cast<const float4*>(w_lds + 32 * kb + 8 * g);
+      wv[2 * kb + 1] = *reinterpret_cast<const float4*>(w_lds + 32 * kb + 8 * g + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 w0 = wv[2 * kb], w1 = wv[2 * kb + 1];
       const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[kb][e] = (x[kb][e] * inv) * w[e];
@@ -200,12 +208,15 @@ __device__ __forceinline__ void prologue_operand_lds_w(const uint4 raw[4], const
   }
 }
 
-// The lane's 32 cos/sin values of one position from the table row `row` (cos[64], sin[64]).
-__device__ __forceinline__ void load_cos_sin(const float* __restrict__ row, int g, float4 cs[8]) {
-  const float4* c = reinterpret_cast<const float4*>(row);
-  const float4* s = reinterpret_cast<const float4*>(row + kHalfDim);
-  cs[0] = c[2 * g]; cs[1] = c[2 * g + 1]; cs[2] = c[8 + 2 * g]; cs[3] = c[8 + 2 * g + 1];
-  cs[4] = s[2 * g]; cs[5] = s[2 * g + 1]; cs[6] = s[8 + 2 * g]; cs[7] = s[8 + 2 * g + 1];
+// The lane's 32 cos/sin values for position `pos` from the RoPE table (blocks of 16
+// positions in lane order, built at plan time): cs[0..3] the cos of frequencies
+// 8g..8g+7, 32+8g..32+8g+7, cs[4..7] their sin.  When the 16 lanes r of a group read the 16
+// positions of one block (pos = 16 B + r), each load is 1 KB of contiguous memory.
+__device__ __forceinline__ void load_cos_sin(const float* __restrict__ rope, int pos, int g, float4 cs[8]) {
+  const float4* blk = reinterpret_cast<const float4*>(rope + (size_t)(pos >> 4) * kRopeBlockFloats);
+  const int lane = (pos & 15) + 16 * g;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cs[e] = blk[e * 64 + lane];
 }
 
 // Wave-uniform read of a read-only int32 array through the constant address space, so the
@@ -242,8 +253,8 @@ struct DecodeParams {
 };
 
 // Decode.  workspace == NULL: one workgroup per (row, KV head).  Otherwise (at least
-// decode_workspace_bytes, zero before its first use; every call leaves it zero): one
-// wavefront per (row, KV head, stream) on separate compute units.  Same bits either way.
+// decode_workspace_bytes, any contents): one wavefront per (row, KV head, stream) on
+// separate compute units, then a combining kernel.  Same bits either way.
 size_t decode_workspace_bytes(int batch, int num_kv_heads, int group);
 hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t stream);
 

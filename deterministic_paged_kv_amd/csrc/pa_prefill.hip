@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.k_cache + src + 32 * kb) : zero4;
     float4 cs[8];
-    load_cos_sin(P.rope + (size_t)(live ? j : 0) * kHeadDim, g, cs);
+    load_cos_sin(P.rope, live ? j : 0, g, cs);
     bf16x8 op[4];
     prologue_operand(raw, kw, knorm, P.eps, cs, op);
     uint16_t* dst = kh + ((size_t)hk * P.num_indices * kPageSize + (size_t)gp * kPageSize + r) * kHeadDim + 8 * g;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.q + off + 32 * kb) : make_uint4(0, 0, 0, 0);
       float4 cs[8];
-      load_cos_sin(P.rope + (size_t)max(qp[t], 0) * kHeadDim, g, cs);
+      load_cos_sin(P.rope, max(qp[t], 0), g, cs);
       prologue_operand(raw, w, qnorm, P.eps, cs, qop[t]);
     }
   }

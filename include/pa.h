@@ -167,10 +167,10 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
  * s, s+8, s+16, ...), each stream is an online softmax over its pages in ascending order,
  * and the 8 stream states are combined in stream order.  The order depends only on the row
  * itself.  With workspace == NULL one workgroup runs all 8 streams; with a workspace each
- * stream runs on its own compute unit and the last to finish combines them, which spreads a
- * long row over 8 compute units.  Both give bit-identical results.  The workspace must be
- * zero before its first use; every call leaves it zero again.  Calls that overlap in time
- * need separate workspaces.
+ * stream runs on its own compute unit and writes its state there, and a second kernel
+ * combines the states, which spreads a long row over 8 compute units.  Both give
+ * bit-identical results.  The workspace needs no initialisation (every call writes what it
+ * reads).  Calls that overlap in time need separate workspaces.
  * Asynchronous on `stream`; requires q_len == 1 and batch <= plan capacity. */
 pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
                     int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,

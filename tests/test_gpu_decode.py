@@ -134,8 +134,9 @@ def test_long_context_decode_sampled(gpu, batch, length):
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "qwen3_8b", "batch8", "groups16"])
 def test_multi_cu_schedule_is_bit_identical(gpu, name):
-    """One wavefront per stream on separate compute units gives the same bits as one workgroup
-    per (row, KV head); the workspace is left zeroed, so it is reused across calls."""
+    """One wavefront per stream on separate compute units, then a combining kernel, gives the
+    same bits as one workgroup per (row, KV head); the workspace needs no initialisation (it is
+    filled with NaN bytes before every call)."""
     if name == "tiny":
         b = workloads.tiny_decode()
     elif name == "ragged":
@@ -152,8 +153,6 @@ def test_multi_cu_schedule_is_bit_identical(gpu, name):
     unit = run("decode", plan, db)
     ws = pa.decode_workspace(plan, b.batch)
     for _ in range(3):
+        ws.fill_(0xFF)
         multi = run("decode", plan, db, workspace=ws)
         assert same_bits(unit, multi), name
-    # counters are zero again after every call
-    units = b.batch * b.num_kv_heads
-    assert int(ws[:4 * units].count_nonzero()) == 0
