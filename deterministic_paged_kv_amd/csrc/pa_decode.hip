@@ -10,23 +10,23 @@
 // NHD) and "Design notes" (CSR metadata; with Split-KV disabled a row's result does not
 // depend on the plan width or the batch).
 //
-// Reduction tree.  The row's pages are dealt to 8 streams: stream s takes logical pages
-// s, s+8, s+16, ...  Each stream runs an FP32 online softmax over its pages in ascending
+// Reduction tree.  The row's pages are dealt to 16 streams: stream s takes logical pages
+// s, s+16, s+32, ...  Each stream runs an FP32 online softmax over its pages in ascending
 // order, one page (16 keys) per step: S^T = K^ Q^T by bf16 MFMA with FP32 accumulation, a
 // page max and sum per head taken in a fixed order (4 keys in registers, then a 2-step lane
 // exchange), and O^T += V^T P^T by bf16 MFMA into FP32 with P split into two bf16 parts
 // (hi + lo), so the probabilities keep about 16 significant bits.  The 8 stream states are
-// then combined in stream order 0..7.  The tree depends only on the row's own length, so the
+// then combined in stream order 0..15.  The tree depends only on the row's own length, so the
 // bits of a row are the same whatever batch it is in, whatever the plan width and wherever
 // its pages sit.
 //
 // Two schedules run this same tree with the same device code (floating-point contraction is
 // pinned off in it, so both compile to the same arithmetic):
-//  * one workgroup of 8 wavefronts per (row, KV head), stream s on wavefront s, states
-//    combined through LDS (no workspace);
+//  * one workgroup of 8 wavefronts per (row, KV head), wavefront w walking pages w, w+8, ...
+//    and so running streams w and w+8, states combined through LDS (no workspace);
 //  * one single-wavefront workgroup per (row, KV head, stream), states written to a caller
 //    workspace, and a second kernel that combines each unit's states in stream order.  This
-//    spreads a long row over 8 compute units; the bits are identical.
+//    spreads a long row over 16 compute units; the bits are identical.
 //
 // Memory layout.  k_cache/v_cache are NHD [page][slot][Hkv][128] bf16: one KV head of one
 // page is 16 rows of 256 B at a stride of Hkv * 256 B.  A lane (r = lane % 16, g = lane / 16)
@@ -40,13 +40,14 @@ namespace pa {
 
 namespace {
 
-constexpr int kStreams = 8;                  // streams of the reduction tree
-constexpr int kDecodeThreads = kStreams * 64;
+constexpr int kStreams = 16;                 // streams of the reduction tree
+constexpr int kUnitWaves = 8;                // wavefronts of the one-workgroup schedule
+constexpr int kDecodeThreads = kUnitWaves * 64;
 // pages in flight per wavefront: the unit schedule runs 2 wavefronts per SIMD, the
 // multi-CU schedule one or two with the register file to itself
 constexpr int kUnitRing = 2;
-constexpr int kStreamRing = 4;
-constexpr int kStreamCsRing = 2;
+constexpr int kStreamRing = 2;
+constexpr int kStreamCsRing = 1;
 // V staging rows are padded by 16 bytes to spread the transposed reads over the LDS banks.
 constexpr int kVRow = kHeadDim + 8;
 typedef uint16_t VSlot[kPageSize][kVRow];
@@ -114,8 +115,33 @@ struct Scored {
 
 // Scores of page pg: stage V in LDS, run the K prologue, S^T = K^ Q^T, and advance the
 // running max and sum.  Lane (r, g) holds keys 4g+i of head r.
+// K norm weights: read from LDS by every page (the one-workgroup schedule, short of
+// registers), or held in registers.
+struct KwLds {
+  const float* p;
+  __device__ __forceinline__ void prologue(const uint4 raw[4], bool knorm, float eps, const float4 cs[8], int g,
+                                           bf16x8 out[4]) const {
+    prologue_operand_lds_w(raw, p, knorm, eps, cs, g, out);
+  }
+};
+struct KwRegs {
+  float w[32];
+  __device__ __forceinline__ void load(const float* k_norm, int g) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = k_norm != nullptr ? k_norm[32 * kb + 8 * g + e] : 1.0f;
+  }
+  __device__ __forceinline__ void prologue(const uint4 raw[4], bool knorm, float eps, const float4 cs[8], int g,
+                                           bf16x8 out[4]) const {
+    (void)g;
+    prologue_operand(raw, w, knorm, eps, cs, out);
+  }
+};
+
+template <class Kw>
 __device__ __forceinline__ Scored score_page(const PageIn& in, const float4 cs[8], int pg, StreamState& st,
-                                             const bf16x8 qop[4], const float* kw, bool knorm, float eps, int L,
+                                             const bf16x8 qop[4], const Kw& kw, bool knorm, float eps, int L,
                                              int qp, int r, int g, VSlot& sv) {
 #pragma clang fp contract(off)
   // keys at or past `live_end` are invisible (past the row, or after the query): only a row's
@@ -133,7 +159,7 @@ __device__ __forceinline__ Scored score_page(const PageIn& in, const float4 cs[8
   }
 
   bf16x8 kop[4];
-  prologue_operand_lds_w(in.k, kw, knorm, eps, cs, g, kop);
+  kw.prologue(in.k, knorm, eps, cs, g, kop);
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], qop[kb], s, 0, 0, 0);
@@ -202,45 +228,61 @@ __device__ __forceinline__ void pv_page(const Scored& sc, StreamState& st, int r
   }
 }
 
-// Stream s of one (row, KV head) unit on one wavefront: pages s, s+8, s+16, ...
-// sv: this wavefront's V staging slot; kw: the K norm weights in LDS (or 1.0 without norm).
-// R pages of K and V are in flight: page t of the stream (t = 0, 1, ...) sits in ring slot
-// t % R, and once it is scored the slot is refilled with page t + R.  The cos/sin rows of the
-// keys (mostly cache hits, read by every KV head) run RC pages ahead in a ring of their own.
-// The physical page numbers come 64 at a time in one vector load (lane l: the stream's page
-// 64 blk + l) and are taken out with readlane, so they never wait behind other loads.
-// Pages past the row's end are loaded from the row's last page (their data is never used),
-// so every step issues the same loads.
-template <int R, int RC>
-__device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo& ri, int hk, int s, int lane,
-                                           VSlot& sv, const float* kw, StreamState& st) {
-  static_assert(R % RC == 0, "the cos/sin ring must divide the K/V ring");
+// One wavefront's walk over the pages first, first + stride, first + 2 stride, ... of one
+// (row, KV head) unit.  Walk step t feeds state st[t % NS]: with stride = kStreams and NS = 1
+// the wavefront is stream `first`; with stride = kStreams / 2 and NS = 2 it runs streams
+// `first` (even steps) and `first` + kStreams / 2 (odd steps).  Either way each stream sees its
+// own pages in ascending order.
+// R pages of K and V are in flight: walk step t sits in ring slot t % R, and once it is scored
+// the slot is refilled with step t + R.  The cos/sin rows of the keys (mostly cache hits, read
+// by every KV head) run RC steps ahead in a ring of their own.  The physical page numbers come
+// 64 at a time in one vector load (lane l: walk step 64 blk + l) and are taken out with
+// readlane, so they never wait behind other loads.  Steps past the row's end load the row's
+// last page (their data is never used), so every step issues the same loads.
+template <int R, int RC, int NS, class Kw>
+__device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& ri, int hk, int first, int stride,
+                                         int lane, VSlot& sv, const Kw& kw, StreamState (&st)[NS]) {
+  static_assert(R % RC == 0 && R % NS == 0, "the rings and the state cycle must divide the K/V ring");
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = P.group;
   const int n = ri.n, L = ri.L, qp = ri.qp, p0 = ri.p0;
   const bool qnorm = P.q_norm != nullptr;
   const bool knorm = P.k_norm != nullptr;
-  const int steps = (n - s + kStreams - 1) / kStreams;  // pages of this stream (n > s or 0)
+  const int steps = n > first ? (n - first + stride - 1) / stride : 0;
 
-  st.poison = 0;
-  // lane l's page slot for block blk: the stream's page 64 blk + l, clamped to the row
+  // the query's inputs go out first: they depend on nothing loaded here
+  uint4 qraw[4];
+  float qw[32];
+  float4 qcs[8];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    qraw[kb] = make_uint4(0, 0, 0, 0);
+    if (r < G) qraw[kb] = ldg16(P.q + (ri.head0 + r) * kHeadDim + 32 * kb + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qw[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
+  }
+  load_cos_sin(P.rope, qp, g, qcs);
+
+#pragma unroll
+  for (int i = 0; i < NS; ++i) st[i].poison = 0;
+  // lane l's page slot for block blk: walk step 64 blk + l, clamped to the row
   auto index_block = [&](int blk) {
-    const int pg = min(s + (64 * blk + lane) * kStreams, n - 1);
+    const int pg = min(first + (64 * blk + lane) * stride, n - 1);
     return P.indices[p0 + pg];
   };
   int vcur = index_block(0);
   int vnext = index_block(1);
   int cur_blk = 0;
-  auto phys_at = [&](int t) {  // physical page of the stream's page t (t within blocks cur_blk, +1)
+  auto phys_at = [&](int t) {  // physical page of walk step t (t within blocks cur_blk, +1)
     const int a = __builtin_amdgcn_readlane(vcur, t & 63);
     const int c = __builtin_amdgcn_readlane(vnext, t & 63);
     int phys = (t >> 6) == cur_blk ? a : c;
-    if (phys < 0 || phys >= P.num_pages) { st.poison |= t < steps; phys = 0; }
+    if (phys < 0 || phys >= P.num_pages) { st[0].poison |= t < steps; phys = 0; }
     return phys;
   };
-  // position of key r of the stream's page t (pages past the end read the last page's)
-  auto key_pos = [&](int t) { return min(s + t * kStreams, n - 1) * kPageSize + r; };
+  // position of key r of walk step t (steps past the end read the last page's)
+  auto key_pos = [&](int t) { return min(first + t * stride, n - 1) * kPageSize + r; };
 
   PageIn in[R];
   float4 cs[RC][8];
@@ -251,25 +293,15 @@ __device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo&
 
   // q^ of the group's heads in the operand layout (vector r = head r < G)
   bf16x8 qop[4];
-  {
-    float w[32];
-    uint4 raw[4];
-    float4 qcs[8];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      raw[kb] = make_uint4(0, 0, 0, 0);
-      if (r < G) raw[kb] = ldg16(P.q + (ri.head0 + r) * kHeadDim + 32 * kb + 8 * g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
-    }
-    load_cos_sin(P.rope, qp, g, qcs);
-    prologue_operand(raw, w, qnorm, P.eps, qcs, qop);
-  }
+  prologue_operand(qraw, qw, qnorm, P.eps, qcs, qop);
 
-  st.m = -__builtin_inff();
-  st.l = 0.0f;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NS; ++i) {
+    st[i].m = -__builtin_inff();
+    st[i].l = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) st[i].acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   for (int t0 = 0; t0 < steps; t0 += R) {
 #pragma unroll
@@ -277,9 +309,10 @@ __device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo&
       const int t = t0 + k;
       if (t >= steps) continue;  // (not break: an early exit from the unrolled body costs registers)
       const int c = k % RC;
-      const Scored sc = score_page(in[k], cs[c], s + t * kStreams, st, qop, kw, knorm, P.eps, L, qp, r, g, sv);
+      StreamState& sk = st[k % NS];
+      const Scored sc = score_page(in[k], cs[c], first + t * stride, sk, qop, kw, knorm, P.eps, L, qp, r, g, sv);
       load_cos_sin(P.rope, key_pos(t + RC), g, cs[c]);
-      // refill the slot with page t + R; a new block of page numbers is due when t + R
+      // refill the slot with step t + R; a new block of page numbers is due when t + R
       // enters the next one
       const int u = t + R;
       if ((u & 63) == 0 && (u >> 6) != cur_blk) {
@@ -289,7 +322,7 @@ __device__ __forceinline__ void run_stream(const DecodeParams& P, const RowInfo&
       }
       issue_page(in[k], P, phys_at(u), hk, r, g);
       wave_lds_sync();
-      pv_page(sc, st, r, g, sv);
+      pv_page(sc, sk, r, g, sv);
       wave_lds_sync();
     }
   }
@@ -324,7 +357,7 @@ __device__ __forceinline__ void combine_one(const DecodeParams& P, const RowInfo
 // ---------------------------------------------------------------------------------------
 struct UnitSmem {
   union {
-    VSlot v[kStreams];                     // per-wave V page
+    VSlot v[kUnitWaves];                   // per-wave V page
     float acc[kStreams][4][kHeadDim];      // per-stream outputs of 4 heads (combine)
   } u;
   float m[kStreams][kMaxGroup];
@@ -334,6 +367,7 @@ struct UnitSmem {
 };
 
 __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const DecodeParams P) {
+  static_assert(kStreams == 2 * kUnitWaves, "each wavefront of the workgroup runs two streams");
   __shared__ UnitSmem sm;
   const int unit = blockIdx.x;
   const int b = unit / P.num_kv_heads;
@@ -352,11 +386,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
   for (int i = tid; i < kHeadDim; i += kDecodeThreads) sm.kw[i] = P.k_norm != nullptr ? P.k_norm[i] : 1.0f;
   __syncthreads();
 
-  StreamState st;
-  run_stream<kUnitRing, 1>(P, ri, hk, wave, lane, sm.u.v[wave], sm.kw, st);
+  // wavefront w walks pages w, w+8, ...: streams w (even steps) and w+8 (odd steps)
+  StreamState st[2];
+  run_walk<kUnitRing, 1, 2>(P, ri, hk, wave, kUnitWaves, lane, sm.u.v[wave], KwLds{sm.kw}, st);
 
-  if (g == 0 && r < G) { sm.m[wave][r] = st.m; sm.l[wave][r] = st.l; }
-  if (lane == 0) sm.poison[wave] = st.poison;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int sid = wave + i * kUnitWaves;
+    if (g == 0 && r < G) { sm.m[sid][r] = st[i].m; sm.l[sid][r] = st[i].l; }
+    if (lane == 0) sm.poison[sid] = st[i].poison;
+  }
   __syncthreads();
   int poison = 0;
 #pragma unroll
@@ -365,9 +404,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
   for (int h0 = 0; h0 < G; h0 += 4) {
     if (r >= h0 && r < h0 + 4) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.u.acc[wave][r - h0][16 * nb + 4 * g + i] = st.acc[nb][i];
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.u.acc[wave + i * kUnitWaves][r - h0][16 * nb + 4 * g + e] = st[i].acc[nb][e];
     }
     __syncthreads();
     const int nh = min(4, G - h0);
@@ -390,10 +431,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
 // ---------------------------------------------------------------------------------------
 constexpr int kCombineThreads = 256;
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_stream_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const DecodeParams P, int32_t* __restrict__ poisons, float* __restrict__ states) {
   __shared__ VSlot sv;
-  __shared__ float kw[kHeadDim];
   const int unit = blockIdx.x / kStreams;
   const int s = blockIdx.x % kStreams;
   const int b = unit / P.num_kv_heads;
@@ -404,20 +444,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   const int G = P.group;
   const RowInfo ri = row_info(P, b, hk);
   if (ri.bad || ri.L == 0) return;  // the combine kernel writes these rows
-  for (int i = lane; i < kHeadDim; i += 64) kw[i] = P.k_norm != nullptr ? P.k_norm[i] : 1.0f;
-  __syncthreads();
+  KwRegs kw;
+  kw.load(P.k_norm, g);
 
-  StreamState st;
-  run_stream<kStreamRing, kStreamCsRing>(P, ri, hk, s, lane, sv, kw, st);
+  StreamState st[1];
+  run_walk<kStreamRing, kStreamCsRing, 1>(P, ri, hk, s, kStreams, lane, sv, kw, st);
 
   const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per stream state
   if (r < G) {
     float* hrec = states + ((size_t)unit * kStreams + s) * rec + (size_t)r * (2 + kHeadDim);
-    if (g == 0) { hrec[0] = st.m; hrec[1] = st.l; }
+    if (g == 0) { hrec[0] = st[0].m; hrec[1] = st[0].l; }
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<f32x4*>(hrec + 2 + 16 * nb + 4 * g) = st.acc[nb];
+    for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<f32x4*>(hrec + 2 + 16 * nb + 4 * g) = st[0].acc[nb];
   }
-  if (lane == 0) poisons[unit * kStreams + s] = st.poison;
+  if (lane == 0) poisons[unit * kStreams + s] = st[0].poison;
 }
 
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeParams P,

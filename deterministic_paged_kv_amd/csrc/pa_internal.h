@@ -121,12 +121,14 @@ __device__ __forceinline__ void prologue_operand(const uint4 raw[4], const float
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) unpack8(raw[kb], x[kb]);
   if (norm) {
-    // x*x is exact in float64, so fma(x, x, ss) rounds exactly like x*x + ss
-    double ss = 0.0;
+    // x*x is exact in float64 and so is the sum (the terms have 16 significant bits), so the
+    // four partial sums give the same result as any other order
+    double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)x[kb][e], (double)x[kb][e], ss);
+      for (int e = 0; e < 8; ++e) s4[kb] = __builtin_fma((double)x[kb][e], (double)x[kb][e], s4[kb]);
+    double ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     ss = pair16_sum(ss);
     ss = pair32_sum(ss);
     const float ms = (float)(ss * (1.0 / kHeadDim));
@@ -164,11 +166,12 @@ __device__ __forceinline__ void prologue_operand_lds_w(const uint4 raw[4], const
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) unpack8(raw[kb], x[kb]);
   if (norm) {
-    double ss = 0.0;
+    double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)x[kb][e], (double)x[kb][e], ss);
+      for (int e = 0; e < 8; ++e) s4[kb] = __builtin_fma((double)x[kb][e], (double)x[kb][e], s4[kb]);
+    double ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     ss = pair16_sum(ss);
     ss = pair32_sum(ss);
     const float ms = (float)(ss * (1.0 / kHeadDim));

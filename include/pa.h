@@ -163,12 +163,12 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
  *                                           Requirements").  Rows with no keys get
  *                                           out = 0 and lse = -inf.
  *   workspace        NULL, or device memory of at least pa_decode_workspace_size() bytes.
- * Reduction order: each (row, KV head)'s pages are dealt to 8 streams (stream s takes pages
- * s, s+8, s+16, ...), each stream is an online softmax over its pages in ascending order,
- * and the 8 stream states are combined in stream order.  The order depends only on the row
- * itself.  With workspace == NULL one workgroup runs all 8 streams; with a workspace each
+ * Reduction order: each (row, KV head)'s pages are dealt to 16 streams (stream s takes pages
+ * s, s+16, s+32, ...), each stream is an online softmax over its pages in ascending order,
+ * and the 16 stream states are combined in stream order.  The order depends only on the row
+ * itself.  With workspace == NULL one workgroup runs all 16 streams; with a workspace each
  * stream runs on its own compute unit and writes its state there, and a second kernel
- * combines the states, which spreads a long row over 8 compute units.  Both give
+ * combines the states, which spreads a long row over 16 compute units.  Both give
  * bit-identical results.  The workspace needs no initialisation (every call writes what it
  * reads).  Calls that overlap in time need separate workspaces.
  * Asynchronous on `stream`; requires q_len == 1 and batch <= plan capacity. */
