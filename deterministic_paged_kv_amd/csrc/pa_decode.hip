@@ -15,7 +15,7 @@
 // order, one page (16 keys) per step: S^T = K^ Q^T by bf16 MFMA with FP32 accumulation, a
 // page max and sum per head taken in a fixed order (4 keys in registers, then a 2-step lane
 // exchange), and O^T += V^T P^T by bf16 MFMA into FP32 with P split into two bf16 parts
-// (hi + lo), so the probabilities keep about 16 significant bits.  The 8 stream states are
+// (hi + lo), so the probabilities keep about 16 significant bits.  The 16 stream states are
 // then combined in stream order 0..15.  The tree depends only on the row's own length, so the
 // bits of a row are the same whatever batch it is in, whatever the plan width and wherever
 // its pages sit.
@@ -284,16 +284,19 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
   // position of key r of walk step t (steps past the end read the last page's)
   auto key_pos = [&](int t) { return min(first + t * stride, n - 1) * kPageSize + r; };
 
+  // q^ of the group's heads in the operand layout (vector r = head r < G), before any page
+  // load is issued: when every wavefront of the grid starts at once, the query's few bytes
+  // would otherwise queue behind the first pages of all of them
+  bf16x8 qop[4];
+  prologue_operand(qraw, qw, qnorm, P.eps, qcs, qop);
+  __builtin_amdgcn_sched_barrier(0);
+
   PageIn in[R];
   float4 cs[RC][8];
 #pragma unroll
   for (int k = 0; k < R; ++k) issue_page(in[k], P, phys_at(k), hk, r, g);
 #pragma unroll
   for (int c = 0; c < RC; ++c) load_cos_sin(P.rope, key_pos(c), g, cs[c]);
-
-  // q^ of the group's heads in the operand layout (vector r = head r < G)
-  bf16x8 qop[4];
-  prologue_operand(qraw, qw, qnorm, P.eps, qcs, qop);
 
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
