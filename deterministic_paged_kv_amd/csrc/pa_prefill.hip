@@ -268,12 +268,13 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
   constexpr int kRing = 3;
   TileRegs ring[kRing];
   TilePages pages_next{{0, 0}};
+  // Tiles past the block's last one are loaded all the same (their keys and pages are clamped
+  // to the row's last key): every step issues the same loads, so the wait for tile kt+1 never
+  // has to drain the younger loads still in flight.
   if (ntiles > 0) {
-    load_tile(ring[0], P, kh_row0, tile_pages(P, p0, L, 0, poison), L, hk, 0, tid);
 #pragma unroll
-    for (int u = 1; u < kRing; ++u)
-      if (u < ntiles) load_tile(ring[u], P, kh_row0, tile_pages(P, p0, L, u, poison), L, hk, u, tid);
-    if (kRing < ntiles) pages_next = tile_pages(P, p0, L, kRing, poison);
+    for (int u = 0; u < kRing; ++u) load_tile(ring[u], P, kh_row0, tile_pages(P, p0, L, u, poison), L, hk, u, tid);
+    pages_next = tile_pages(P, p0, L, kRing, poison);
     store_tile(ring[0], sm, 0, tid);
   }
   __syncthreads();
@@ -282,10 +283,8 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
     // `done`: the registers of tile kt (already in LDS), free to take tile kt+kRing;
     // `following`: the registers of tile kt+1
     const int buf = kt & 1;
-    if (kt + kRing < ntiles) {
-      load_tile(done, P, kh_row0, pages_next, L, hk, kt + kRing, tid);
-      if (kt + kRing + 1 < ntiles) pages_next = tile_pages(P, p0, L, kt + kRing + 1, poison);
-    }
+    load_tile(done, P, kh_row0, pages_next, L, hk, kt + kRing, tid);
+    pages_next = tile_pages(P, p0, L, kt + kRing + 1, poison);
     if (head_live) {
         // S^T = K^ Q^T for the tile's two 16-key subtiles
         f32x4 sc[kQT][2];
