@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
 // Workspace: an int32 poison flag per (unit, stream), then per unit and stream G records of
 // [m, l, 128 accumulators].
 // ---------------------------------------------------------------------------------------
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 512;
 
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const DecodeParams P, int32_t* __restrict__ poisons, float* __restrict__ states) {
@@ -466,26 +466,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeParams P,
                                                                          const int32_t* __restrict__ poisons,
                                                                          const float* __restrict__ states) {
+  __shared__ float ml[kStreams][kMaxGroup][2];  // m and l of every stream and head
+  __shared__ int poison_any;
   const int unit = blockIdx.x;
   const int b = unit / P.num_kv_heads;
   const int hk = unit % P.num_kv_heads;
   const int G = P.group;
+  const int tid = threadIdx.x;
   const RowInfo ri = row_info(P, b, hk);
   if (ri.bad || ri.L == 0) {
-    write_degenerate(P, ri, threadIdx.x, kCombineThreads);
+    write_degenerate(P, ri, tid, kCombineThreads);
     return;
   }
-  int poison = 0;
-#pragma unroll
-  for (int w = 0; w < kStreams; ++w) poison |= poisons[unit * kStreams + w];
   const size_t rec = (size_t)G * (2 + kHeadDim);
   const float* unit_states = states + (size_t)unit * kStreams * rec;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kCombineThreads) {
-    const int h = idx / kHeadDim, d = idx % kHeadDim;
-    const float* base = unit_states + (size_t)h * (2 + kHeadDim);
-    combine_one(P, ri, h, d, poison != 0, [&](int w) { return base[(size_t)w * rec]; },
-                [&](int w) { return base[(size_t)w * rec + 1]; },
-                [&](int w) { return base[(size_t)w * rec + 2 + d]; });
+  if (tid == 0) poison_any = 0;
+  __syncthreads();
+  // every stream's m, l and poison flag once into LDS, while the accumulators are loaded below
+  if (tid < kStreams * G * 2) {
+    const int w = tid / (2 * G), h = (tid / 2) % G, c = tid & 1;
+    ml[w][h][c] = unit_states[(size_t)w * rec + (size_t)h * (2 + kHeadDim) + c];
+  }
+  if (tid < kStreams && poisons[unit * kStreams + tid] != 0) atomicOr(&poison_any, 1);
+  for (int idx0 = 0; idx0 < G * kHeadDim; idx0 += kCombineThreads) {
+    const int idx = idx0 + tid;
+    const bool live = idx < G * kHeadDim;
+    const int h = live ? idx / kHeadDim : 0, d = idx % kHeadDim;
+    float a[kStreams];
+#pragma unroll
+    for (int w = 0; w < kStreams; ++w) a[w] = live ? unit_states[(size_t)w * rec + (size_t)h * (2 + kHeadDim) + 2 + d] : 0.0f;
+    __syncthreads();
+    if (live)
+      combine_one(P, ri, h, d, poison_any != 0, [&](int w) { return ml[w][h][0]; }, [&](int w) { return ml[w][h][1]; },
+                  [&](int w) { return a[w]; });
   }
 }
 
