@@ -33,7 +33,7 @@ namespace {
 constexpr int kQBlock = 32;          // queries per wavefront (two 16-row MFMA tiles)
 constexpr int kQT = kQBlock / 16;
 constexpr int kKT = 32;              // keys per tile (2 pages)
-constexpr int kRow = kHeadDim + 8;   // LDS row, padded by 16 bytes
+constexpr int kRow = kHeadDim + 16;  // LDS row, padded by 32 bytes (conflict-free transposed reads)
 constexpr int kAttendThreads = 256;
 // A query's softmax reference is moved only when a tile's scaled score exceeds it by more
 // than this (log2 domain), so probabilities stay below 2^8 and rescaling is rare.
