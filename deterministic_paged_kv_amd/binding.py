@@ -205,8 +205,8 @@ def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_
            q_norm_weight=None, k_norm_weight=None, out=None, lse=None, workspace=None, stream=None):
     """pa_decode.  q [B, Hq, 1, 128] bf16; returns (out [B, Hq, 1, 128] bf16, lse [B, Hq, 1] fp32).
 
-    workspace: None for the one-workgroup-per-(row, KV head) schedule, or a zeroed uint8 device
-    tensor from decode_workspace() for the multi-compute-unit schedule (same bits)."""
+    workspace: None for the one-workgroup-per-(row, KV head) schedule, or a uint8 device tensor
+    from decode_workspace() (any contents) for the multi-compute-unit schedule (same bits)."""
     import torch
 
     B, Sq, num_pages, nnz = _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len,
