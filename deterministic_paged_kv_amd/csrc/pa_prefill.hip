@@ -50,6 +50,24 @@ __device__ __forceinline__ i16x8 concat4(const i16x4& a, const i16x4& b) {
   return i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four FP32 values rounded to BF16 (nearest-even) and packed in order (two v_cvt_pk_bf16_f32).
+__device__ __forceinline__ i16x4 pack_bf16(float a, float b, float c, float d) {
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){c, d}, bf16x2));
+  return __builtin_bit_cast(i16x4, make_uint2(lo, hi));
+}
+
+// max of three floats in one v_max3_f32.  The operands are MFMA results or -inf, never
+// signalling NaNs, so the operand quieting that fmaxf would add is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // ---------------------------------------------------------------------------------------
 // 1. k^ for every cached key
 // ---------------------------------------------------------------------------------------
@@ -107,8 +125,8 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
 // 2. causal attention: q^ made here, k^ from the workspace, V from the pages
 // ---------------------------------------------------------------------------------------
 struct AttendSmem {
-  uint16_t k[2][kKT][kRow];
-  uint16_t v[2][kKT][kRow];
+  uint16_t k[3][kKT][kRow];
+  uint16_t v[3][kKT][kRow];
 };
 
 // The tile's share of one thread: k^ and V rows rt and rt + 16 of the tile (rt = tid / 16), 16
@@ -262,115 +280,172 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
   const int jr = 4 * g + (r >> 2);  // transposed-read row within a 16-key subtile
   const int jc = 4 * (r & 3);
 
-  // Tiles kt+1 .. kt+3 are in flight (a ring of three register sets) while tile kt is used
-  // from LDS; tile kt+1 goes to the other LDS buffer at the end of the step.  The page indices
-  // of a tile are loaded one step before its data.
+  // Software pipeline over 32-key tiles: three LDS buffers and a ring of three register sets.
+  // At the start of step kt, tiles kt and kt+1 are in LDS (buffers kt % 3 and (kt+1) % 3),
+  // S(kt) is in registers and tile kt+2 is in flight or in registers.  Step kt:
+  //   A. S(kt+1) = K^(kt+1) Q^T on the matrix cores while the vector unit runs the softmax of
+  //      S(kt) with the current references (straight-line code); a rare fix-up follows when
+  //      some query's reference has to move.
+  //   B. the loads of tile kt+3 are issued, O^T += V(kt)^T P(kt)^T, tile kt+2 goes to LDS
+  //      buffer (kt+2) % 3 (free since the barrier that ended step kt-1), barrier.
+  // Tiles past the block's last one are loaded, stored and multiplied all the same (keys and
+  // pages clamped to the row's last key, so every access is in bounds and finite); their
+  // results are never used.  Page numbers come through vector loads (one per tile, lane u
+  // holding the page of the tile's half u), so no scalar load shares a counter with the LDS
+  // reads.
   constexpr int kRing = 3;
   TileRegs ring[kRing];
-  TilePages pages_next{{0, 0}};
-  // Tiles past the block's last one are loaded all the same (their keys and pages are clamped
-  // to the row's last key): every step issues the same loads, so the wait for tile kt+1 never
-  // has to drain the younger loads still in flight.
-  if (ntiles > 0) {
+  const int32_t* row_idx = P.indices + p0;
+  const size_t page_elems = (size_t)kPageSize * Hkv * kHeadDim;
+  const int rt = tid >> 4;
+  const int col = tid & 15;
+  const uint32_t v_lane_off = (uint32_t)hk * kHeadDim + col * 8;
+  // page numbers of tile t (lane u: page min(2t + u, n - 1)); only called with n >= 1
+  auto page_vec = [&](int t) -> int { return row_idx[min(2 * t + (lane & 1), n - 1)]; };
+  auto load = [&](TileRegs& tr, int t, int pv) {
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) load_tile(ring[u], P, kh_row0, tile_pages(P, p0, L, u, poison), L, hk, u, tid);
-    pages_next = tile_pages(P, p0, L, kRing, poison);
+    for (int u = 0; u < 2; ++u) {
+      int phys = __builtin_amdgcn_readlane(pv, u);
+      if (phys < 0 || phys >= P.num_pages) { poison = 1; phys = 0; }
+      const int j = min(t * kKT + 16 * u + rt, L - 1);  // logical key (clamped)
+      tr.k[u] = ldg16(kh_row0 + (uint32_t)j * kHeadDim + col * 8);
+      tr.v[u] = ldg16(P.v_cache + (size_t)phys * page_elems + ((uint32_t)(j & (kPageSize - 1)) * Hkv * kHeadDim + v_lane_off));
+    }
+  };
+  // S^T = K^ Q^T for the two 16-key subtiles of the tile in LDS buffer `buf`
+  auto scores = [&](int buf, f32x4 (&out)[kQT][2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 ka[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
+#pragma unroll
+      for (int t = 0; t < kQT; ++t) {
+        out[t][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          out[t][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], out[t][ks], 0, 0, 0);
+      }
+    }
+  };
+  // last key position + 1 each query may see (0: none)
+  int lim[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) lim[t] = min(L, qp[t] + 1);
+
+  int pv_next = 0;
+  if (ntiles > 0) {
+    const int pv0 = page_vec(0), pv1 = page_vec(1), pv2 = page_vec(2);
+    load(ring[0], 0, pv0);
+    load(ring[1], 1, pv1);
+    load(ring[2], 2, pv2);
+    pv_next = page_vec(3);
     store_tile(ring[0], sm, 0, tid);
+    store_tile(ring[1], sm, 1, tid);
   }
   __syncthreads();
+  f32x4 sc[kQT][2];
+  if (ntiles > 0) scores(0, sc);
 
-  auto step = [&](const int kt, TileRegs& done, TileRegs& following) {
-    // `done`: the registers of tile kt (already in LDS), free to take tile kt+kRing;
-    // `following`: the registers of tile kt+1
-    const int buf = kt & 1;
-    load_tile(done, P, kh_row0, pages_next, L, hk, kt + kRing, tid);
-    pages_next = tile_pages(P, p0, L, kt + kRing + 1, poison);
-    if (head_live) {
-        // S^T = K^ Q^T for the tile's two 16-key subtiles
-        f32x4 sc[kQT][2];
-  #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 ka[4];
-  #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
-  #pragma unroll
-          for (int t = 0; t < kQT; ++t) {
-            sc[t][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-              sc[t][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], sc[t][ks], 0, 0, 0);
-          }
-        }
-        const bool masked = (kt + 1) * kKT > free_end;
-        i16x4 pb[kQT][2];
-  #pragma unroll
-        for (int t = 0; t < kQT; ++t) {
-          // Raw scores (the scale c is positive, so maxima commute with it); masked keys -inf.
-          float sv_[2][4];
-          float mx = -__builtin_inff();
-  #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-  #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float v = sc[t][ks][i];
-              if (masked) {
-                const int j = kt * kKT + 16 * ks + 4 * g + i;
-                v = (j < L && j <= qp[t]) ? v : -__builtin_inff();
-              }
-              sv_[ks][i] = v;
-              mx = fmaxf(mx, v);
-            }
-          // The reference m of a query moves only when the tile's largest scaled score exceeds it
-          // by more than kLazyMax; the test is exact per query (a lane's own keys are a subset of
-          // the query's), so the full reduction runs only when some query of the wave moves.
-          if (__builtin_amdgcn_ballot_w64(mx * kScoreScaleLog2 > m_run[t] + kLazyMax) != 0) {
-            const float rowmax = pair32_max(pair16_max(mx)) * kScoreScaleLog2;
-            if (rowmax > m_run[t] + kLazyMax) {
-              const float alpha = m_run[t] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run[t] - rowmax);
-              m_run[t] = rowmax;
-              m_neg[t] = -rowmax;
-              l_part[t] *= alpha;
-  #pragma unroll
-              for (int nb = 0; nb < 8; ++nb) acc[t][nb] = acc[t][nb] * alpha;
-            }
-          }
-          // p = 2^(s c - m) <= 2^kLazyMax; 0 for masked keys (and while m is still -inf, m_neg = 0)
-  #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-  #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv_[ks][i], kScoreScaleLog2, m_neg[t]));
-              l_part[t] += p;
-              pb[t][ks][i] = __builtin_bit_cast(short, (__bf16)p);
-            }
-        }
-        // O^T += V^T P^T over the tile's 32 keys in one K=32 MFMA per (query tile, column block):
-        // k-slot 8g+e holds key 4g+e for e < 4 and key 16+4g+(e-4) for e >= 4, in both operands.
-        // V^T comes from two transposed LDS reads (one per 16-key subtile).
-        bf16x8 pk[kQT];
-  #pragma unroll
-        for (int t = 0; t < kQT; ++t) pk[t] = __builtin_bit_cast(bf16x8, concat4(pb[t][0], pb[t][1]));
-  #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][jr][16 * nb + jc]));
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][16 + jr][16 * nb + jc]));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, concat4(v0, v1));
-  #pragma unroll
-          for (int t = 0; t < kQT; ++t)
-            acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t], acc[t][nb], 0, 0, 0);
+  // p = 2^(s c - m) of a query's 8 scores in this lane, their sum (in key order) and BF16 copy
+  auto tile_p = [&](const f32x4 (&s_)[2], float mneg, float& sum, i16x4 (&pbt)[2]) {
+    float p[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[ks][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[ks][i], kScoreScaleLog2, mneg));
+    sum = p[0][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) sum += p[e >> 2][e & 3];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pbt[ks] = pack_bf16(p[ks][0], p[ks][1], p[ks][2], p[ks][3]);
+  };
+  auto step = [&](const int kt, TileRegs& to_load, TileRegs& to_store) {
+    // ---- A: causal mask (tiles that reach past the block's first query), then S(kt+1) and
+    // the softmax of S(kt)
+    if ((kt + 1) * kKT > free_end) {
+#pragma unroll
+      for (int t = 0; t < kQT; ++t) {
+        const int d = lim[t] - kt * kKT - 4 * g;  // key 16 ks + 4 g + i is visible iff 16 ks + i < d
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[t][ks][i] = 16 * ks + i < d ? sc[t][ks][i] : -__builtin_inff();
+      }
+    }
+    f32x4 sn[kQT][2];
+    scores((kt + 1) % 3, sn);
+    float mx[kQT], lp[kQT];
+    i16x4 pb[kQT][2];
+    bool need = false;
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      // raw-score maximum of this lane's keys (the scale c > 0 commutes with max)
+      mx[t] = max3f(max3f(max3f(sc[t][0][0], sc[t][0][1], sc[t][0][2]), max3f(sc[t][0][3], sc[t][1][0], sc[t][1][1]),
+                          sc[t][1][2]),
+                    sc[t][1][3], sc[t][1][3]);
+      need |= mx[t] * kScoreScaleLog2 > m_run[t] + kLazyMax;
+      // p = 2^(s c - m) with the current reference (0 for masked keys, and while m is -inf)
+      tile_p(sc[t], m_neg[t], lp[t], pb[t]);
+    }
+    // Fix-up, rare: a query whose tile maximum exceeds its reference by more than kLazyMax
+    // (the test is exact per query: a lane's keys are a subset of the query's) moves its
+    // reference to the tile's scaled maximum, rescales what it has summed so far, and
+    // recomputes the tile's p.
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int t = 0; t < kQT; ++t) {
+        const float rowmax = pair32_max(pair16_max(mx[t])) * kScoreScaleLog2;
+        if (rowmax > m_run[t] + kLazyMax) {
+          const float alpha = m_run[t] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run[t] - rowmax);
+          m_run[t] = rowmax;
+          m_neg[t] = -rowmax;
+          l_part[t] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) acc[t][nb] = acc[t][nb] * alpha;
+          tile_p(sc[t], m_neg[t], lp[t], pb[t]);
         }
       }
-    if (kt + 1 < ntiles) store_tile(following, sm, buf ^ 1, tid);
+    }
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) l_part[t] += lp[t];
+    // ---- B: loads of tile kt+3, P.V of tile kt, tile kt+2 to LDS
+    const int pv = pv_next;
+    pv_next = page_vec(kt + 4);
+    load(to_load, kt + 3, pv);
+    // O^T += V^T P^T over the tile's 32 keys in one K=32 MFMA per (query tile, column block):
+    // k-slot 8g+e holds key 4g+e for e < 4 and key 16+4g+(e-4) for e >= 4, in both operands.
+    // V^T comes from two transposed LDS reads (one per 16-key subtile).
+    const int buf = kt % 3;
+    bf16x8 pk[kQT];
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) pk[t] = __builtin_bit_cast(bf16x8, concat4(pb[t][0], pb[t][1]));
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][jr][16 * nb + jc]));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][16 + jr][16 * nb + jc]));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, concat4(v0, v1));
+#pragma unroll
+      for (int t = 0; t < kQT; ++t)
+        acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t], acc[t][nb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < kQT; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) sc[t][ks] = sn[t][ks];
+    store_tile(to_store, sm, (kt + 2) % 3, tid);
     __syncthreads();
   };
-  for (int kt = 0; kt < ntiles; kt += kRing) {
-    step(kt, ring[0], ring[1]);
-    if (kt + 1 >= ntiles) break;
-    step(kt + 1, ring[1], ring[2]);
-    if (kt + 2 >= ntiles) break;
-    step(kt + 2, ring[2], ring[0]);
+  // whole rounds of the ring, then the last one or two tiles (no exit from inside a round)
+  int kt = 0;
+  for (; kt + kRing <= ntiles; kt += kRing) {
+    step(kt, ring[0], ring[2]);
+    step(kt + 1, ring[1], ring[0]);
+    step(kt + 2, ring[2], ring[1]);
   }
+  if (kt < ntiles) step(kt, ring[0], ring[2]);
+  if (kt + 1 < ntiles) step(kt + 1, ring[1], ring[0]);
 
   // any out-of-range page index seen by any thread poisons the whole block's output
   const bool out_poison = __syncthreads_or(poison) != 0;
