@@ -121,6 +121,11 @@ pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, i
   p->split_policy = split_policy;
   p->d_rope = nullptr;
   if (hipGetDevice(&p->device) != hipSuccess) { delete p; return PA_ERR_HIP; }
+  if (hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess ||
+      p->num_cus < 1) {
+    delete p;
+    return PA_ERR_HIP;
+  }
   const std::vector<float> table = rope_table(p->table_rows, (double)rope_theta, (double)rope_scale);
   const size_t bytes = table.size() * sizeof(float);
   if (hipMalloc(&p->d_rope, bytes) != hipSuccess) { delete p; return PA_ERR_HIP; }
@@ -310,6 +315,7 @@ pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_p
   p.lse = lse;
   p.rope = plan->d_rope;
   p.eps = plan->rms_eps;
+  p.num_cus = plan->num_cus;
   p.workspace = workspace;
   return launch_prefill(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -30,6 +30,7 @@ struct pa_plan_s {
   float rope_theta, rope_scale, rms_eps;
   int32_t split_policy;
   int device;
+  int32_t num_cus;  // compute units of that device (work placement only, never arithmetic)
   float* d_rope;  // [table_rows][128]: cos of the 64 frequencies, then sin
 };
 
@@ -291,6 +292,7 @@ struct PrefillParams {
   float* lse;
   const float* rope;
   float eps;
+  int32_t num_cus;
   void* workspace;
 };
 

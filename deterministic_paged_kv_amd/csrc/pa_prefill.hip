@@ -129,6 +129,13 @@ struct AttendSmem {
   uint16_t v[3][kKT][kRow];
 };
 
+// Work placement: tiles per unit, and the unit picked.
+constexpr int kMaxRankUnits = 512;
+struct RankSmem {
+  int tiles[kMaxRankUnits];
+  int sel;
+};
+
 // The tile's share of one thread: k^ and V rows rt and rt + 16 of the tile (rt = tid / 16), 16
 // bytes each at column chunk tid % 16.  Keys past the row's end read the row's last key, so
 // every load is in bounds and finite (their scores are masked and their probabilities are 0).
@@ -177,23 +184,78 @@ __device__ __forceinline__ void store_tile(const TileRegs& tr, AttendSmem& sm, i
   }
 }
 
+// Units (row b, query block qb) are numbered u = (nqb - 1 - qb) * batch + b.  The key tiles a
+// unit visits: its row's keys up to the last query's position (the block's last query stands
+// in for the largest position; only the placement of work depends on it).
+__device__ int unit_tiles(const PrefillParams& P, int nqb, int u) {
+  const int b = u % P.batch;
+  const int qb = nqb - 1 - u / P.batch;
+  const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
+  const int n = p1 - p0;
+  const int lpl = P.last_page_len[b];
+  const bool bad = p0 < 0 || n < 0 || p1 > P.num_indices || n > P.max_pages_per_row ||
+                   (n > 0 && (lpl < 1 || lpl > kPageSize));
+  const int L = (n > 0 && !bad) ? (n - 1) * kPageSize + lpl : 0;
+  const int i_last = min(qb * kQBlock + kQBlock - 1, P.q_len - 1);
+  int qlast = P.qpos[(size_t)b * P.q_len + i_last];
+  if (qlast < 0 || qlast >= P.table_rows) qlast = -1;
+  const int kend = min(L, qlast + 1);
+  return kend > 0 ? (kend + kKT - 1) / kKT : 0;
+}
+
+// The unit of rank `target` in the order: more tiles first, then lower unit number.
+// All threads of the workgroup call it; U <= kMaxRankUnits.
+__device__ int unit_of_rank(const PrefillParams& P, int nqb, int U, int target, int tid, RankSmem& rs) {
+  for (int u = tid; u < U; u += kAttendThreads) rs.tiles[u] = unit_tiles(P, nqb, u);
+  __syncthreads();
+  for (int u = tid; u < U; u += kAttendThreads) {
+    const int c = rs.tiles[u];
+    int rank = 0;
+    for (int v = 0; v < U; ++v) {
+      const int cv = rs.tiles[v];
+      rank += (cv > c || (cv == c && v < u)) ? 1 : 0;
+    }
+    if (rank == target) rs.sel = u;
+  }
+  __syncthreads();
+  return rs.sel;
+}
+
 __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillParams P,
                                                                 const uint16_t* __restrict__ kh) {
   __shared__ AttendSmem sm;
+  __shared__ RankSmem sched;
   const int G = P.group;
   const int Hkv = P.num_kv_heads;
   const int Sq = P.q_len;
   const int nqb = (Sq + kQBlock - 1) / kQBlock;
-  // longest work first: the last query blocks of every row see the most keys
   const int nhg = (G + 3) / 4;
-  const int per_qb = P.batch * Hkv * nhg;
-  const int qb = nqb - 1 - (int)(blockIdx.x / per_qb);
-  int rest = blockIdx.x % per_qb;
-  const int hg = rest % nhg;
-  rest /= nhg;
-  const int b = rest / Hkv;
-  const int hk = rest % Hkv;
   const int tid = threadIdx.x;
+  // This workgroup's item: a unit (row b, query block qb) and a head slot (KV head hk, group
+  // of query heads hg).  The order only places work; every item's arithmetic is the same
+  // wherever it runs.
+  const int HH = Hkv * nhg;
+  const int U = P.batch * nqb;
+  const int N = U * HH;
+  int unit, head;
+  if (N > P.num_cus && N <= 2 * P.num_cus && U <= kMaxRankUnits) {
+    // One dispatch round that puts workgroups i and i + num_cus on the same compute unit:
+    // give them the items of ranks k and N-1-k of the longest-first order (ranked by the
+    // number of key tiles each unit visits), so every compute unit holds one long and one
+    // short item.
+    const int rank = (int)blockIdx.x < P.num_cus ? (int)blockIdx.x : N - 1 - ((int)blockIdx.x - P.num_cus);
+    unit = unit_of_rank(P, nqb, U, rank / HH, tid, sched);
+    head = rank % HH;
+  } else {
+    // Otherwise longest first in launch order: the last query blocks of every row see the
+    // most keys.
+    unit = (int)blockIdx.x / HH;
+    head = (int)blockIdx.x % HH;
+  }
+  const int qb = nqb - 1 - unit / P.batch;
+  const int b = unit % P.batch;
+  const int hg = head % nhg;
+  const int hk = head / nhg;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r = lane & 15;
