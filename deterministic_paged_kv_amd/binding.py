@@ -38,6 +38,8 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_i32, [_p, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill_workspace_size": (_i32, [_p, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "pa_build_csr": (_i32, [_i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "pa_width_bucket": (_i32, [_i32, ctypes.POINTER(_i32)]),
 }
 
 STATUS = {
@@ -264,3 +266,38 @@ def prefill(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page
                              _ptr(v_cache), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(out), _ptr(lse),
                              _ptr(workspace), int(workspace.numel()), _stream(stream)), "pa_prefill")
     return out, lse
+
+
+def build_csr(block_table, kv_lens, kv_indptr=None, kv_indices=None, kv_last_page_len=None, stream=None):
+    """pa_build_csr: CSR metadata from a dense block table on the device, without a host sync.
+
+    block_table int32 [B, W] (-1 padded), kv_lens int32 [B].  Returns (kv_indptr [B+1],
+    kv_indices [B*W], kv_last_page_len [B]), int32 device tensors (allocated here unless
+    given).  The indices past kv_indptr[B] are -1; pass num_indices = B*W to decode/prefill."""
+    import torch
+
+    _need(block_table, "block_table", torch.int32, 2)
+    B, W = (int(x) for x in block_table.shape)
+    _need(kv_lens, "kv_lens", torch.int32, shape=(B,))
+    dev = block_table.device
+    if kv_indptr is None:
+        kv_indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if kv_indices is None:
+        kv_indices = torch.empty(max(B * W, 1), dtype=torch.int32, device=dev)
+    if kv_last_page_len is None:
+        kv_last_page_len = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(kv_indptr, "kv_indptr", torch.int32, shape=(B + 1,))
+    _need(kv_indices, "kv_indices", torch.int32, 1)
+    if kv_indices.numel() < B * W:
+        raise ValueError(f"kv_indices holds {kv_indices.numel()} entries, need {B * W}")
+    _need(kv_last_page_len, "kv_last_page_len", torch.int32, shape=(B,))
+    _check(load().pa_build_csr(B, W, _ptr(block_table), _ptr(kv_lens), _ptr(kv_indptr), _ptr(kv_indices),
+                               _ptr(kv_last_page_len), _stream(stream)), "pa_build_csr")
+    return kv_indptr, kv_indices[:B * W], kv_last_page_len
+
+
+def width_bucket(width: int) -> int:
+    """pa_width_bucket: the power-of-two table width to make a plan for."""
+    out = ctypes.c_int32()
+    _check(load().pa_width_bucket(int(width), ctypes.byref(out)), "pa_width_bucket")
+    return int(out.value)

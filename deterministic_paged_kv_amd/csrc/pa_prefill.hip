@@ -144,36 +144,6 @@ struct TileRegs {
   uint4 v[2];
 };
 
-// Physical pages of tile kt's two halves (wave-uniform scalar loads), bounds-checked.
-struct TilePages {
-  int phys[2];
-};
-
-__device__ __forceinline__ TilePages tile_pages(const PrefillParams& P, int p0, int L, int kt, int& poison) {
-  TilePages tp;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int pg = min(kt * kKT + 16 * u, L - 1) / kPageSize;  // the 16 rows of half u lie in one page
-    int phys = load_uniform(P.indices, p0 + pg);
-    if (phys < 0 || phys >= P.num_pages) { poison = 1; phys = 0; }
-    tp.phys[u] = phys;
-  }
-  return tp;
-}
-
-__device__ __forceinline__ void load_tile(TileRegs& tr, const PrefillParams& P, const uint16_t* kh_row0,
-                                          const TilePages& tp, int L, int hk, int kt, int tid) {
-  const int rt = tid >> 4;
-  const int col = tid & 15;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int j = min(kt * kKT + 16 * u + rt, L - 1);  // logical key (clamped)
-    tr.k[u] = ldg16(kh_row0 + (size_t)j * kHeadDim + col * 8);
-    tr.v[u] = ldg16(P.v_cache + (((size_t)tp.phys[u] * kPageSize + (j % kPageSize)) * P.num_kv_heads + hk) * kHeadDim +
-                    col * 8);
-  }
-}
-
 __device__ __forceinline__ void store_tile(const TileRegs& tr, AttendSmem& sm, int buf, int tid) {
   const int rt = tid >> 4;
   const int col = tid & 15;

@@ -192,7 +192,7 @@ pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len
  * which include the chunk's own keys ([PR7] "Current Implementation", "FlashInfer RoPE
  * Fusion").  Same arguments and layouts as pa_decode with Sq = q_len, plus a caller-owned
  * device workspace of at least pa_prefill_workspace_size() bytes that holds the
- * normalised, rotated BF16 q^ and k^ between the two kernels of the call.  Asynchronous
+ * normalised, rotated BF16 k^ of every cached key between the two kernels of the call.  Asynchronous
  * on `stream`.  Concurrent calls need separate workspaces. */
 pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
                      int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -201,6 +201,39 @@ pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_p
                      const float* q_norm_weight, const float* k_norm_weight,
                      void* out, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* Build the CSR block table on the device from a dense one ([PR162] "Design notes": CSR
+ * metadata built once per traversal, fixed-shape and device-only; "Code audit", "Data
+ * flows checked": indptr = running sum of ceil(len / 16), compact indices by a fixed-shape
+ * scatter, rows without keys get last_page_len 1, no host synchronisation).
+ *   batch, width       B >= 0 rows of a table `width` >= 1 pages wide (B * width and
+ *                      width * 16 must fit in int32).
+ *   block_table        int32 [B, width]   row b's physical pages in logical order; entries
+ *                                         past the row's pages are ignored (-1 by
+ *                                         convention).
+ *   kv_lens            int32 [B]          keys in the cache per row (L_b).
+ *   kv_indptr          int32 [B + 1]      written: kv_indptr[b + 1] - kv_indptr[b] =
+ *                                         ceil(L_b / 16).
+ *   kv_indices         int32 [B * width]  written: the first ceil(L_b / 16) table entries of
+ *                                         each row, rows back to back; slots from
+ *                                         kv_indptr[B] on are set to -1.
+ *   kv_last_page_len   int32 [B]          written: L_b - 16 (ceil(L_b / 16) - 1), or 1 for
+ *                                         a row with no keys.
+ * A length outside [0, 16 * width] cannot be represented: that row takes its whole table row
+ * and last_page_len 0, which pa_validate_metadata reports (PA_ERR_LAST_PAGE_LEN) and which
+ * pa_decode / pa_prefill turn into NaN for the row.  The outputs fit the other entry points
+ * directly, with num_indices = B * width (the compact count kv_indptr[B] stays on the
+ * device; pa_validate_metadata needs it exactly).  Two kernels on `stream`, no allocation,
+ * no synchronisation, no memset: capturable in a HIP graph.  Errors: PA_ERR_INVALID_ARGUMENT
+ * for sizes out of range or a NULL pointer (kv_indptr is always written, so it may not be
+ * NULL even for B = 0). */
+pa_status pa_build_csr(int32_t batch, int32_t width, const int32_t* block_table, const int32_t* kv_lens,
+                       int32_t* kv_indptr, int32_t* kv_indices, int32_t* kv_last_page_len, void* stream);
+
+/* The table width a plan should be made for: the smallest power of two >= width ([PR162]
+ * "Design notes": plans keyed by a power-of-two width bucket, so a growing context makes
+ * few plans).  Host arithmetic only; width in [1, 2^30], else PA_ERR_INVALID_ARGUMENT. */
+pa_status pa_width_bucket(int32_t width, int32_t* bucket);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,8 @@ and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
 HIP library: no kernels, headers, helpers, tables or constants.
 
 What it computes, and the passages it follows, are documented function by
-function in :mod:`oracle.definition`.  Every function there is pinned by
+function in :mod:`oracle.definition` (attention) and :mod:`oracle.csr` (the CSR
+block table built from a dense one).  Every function there is pinned by
 ``tests/test_oracle_pins.py`` against closed forms, invariants, library
 routines or brute force on tiny inputs; none is "parity unpinned".
 """
@@ -26,3 +27,4 @@ from .definition import (  # noqa: F401
     attention_fp64,
     paged_attention,
 )
+from .csr import csr_from_block_table  # noqa: F401

@@ -97,3 +97,30 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+
+
+def test_csr_builder_rejects_bad_sizes_before_any_launch(lib):
+    """pa_build_csr checks its host scalars and pointers before it launches anything."""
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its host checks
+    assert lib.pa_build_csr(-1, 4, p, p, p, p, p, None) == -1     # negative batch
+    assert lib.pa_build_csr(2, 0, p, p, p, p, p, None) == -1      # width 0
+    assert lib.pa_build_csr(2, 1 << 28, p, p, p, p, p, None) == -1  # width * 16 overflows int32
+    assert lib.pa_build_csr(1 << 16, 1 << 16, p, p, p, p, p, None) == -1  # B * width overflows int32
+    assert lib.pa_build_csr(2, 4, p, p, None, p, p, None) == -1   # no indptr
+    assert lib.pa_build_csr(2, 4, None, p, p, p, p, None) == -1   # no table for B > 0
+    assert lib.pa_build_csr(2, 4, p, None, p, p, p, None) == -1   # no lengths
+    assert lib.pa_build_csr(2, 4, p, p, p, None, p, None) == -1   # no indices
+    assert lib.pa_build_csr(2, 4, p, p, p, p, None, None) == -1   # no last_page_len
+
+
+def test_width_bucket_is_the_next_power_of_two(lib):
+    """Plans keyed by a power-of-two width ("flashinfer_fa2 backend for NVIDIA Ada (SM89)",
+    "Design notes"): the smallest power of two not below the width."""
+    out = ctypes.c_int32()
+    for w, want in [(1, 1), (2, 2), (3, 4), (16, 16), (17, 32), (40, 64), (4096, 4096), (4097, 8192),
+                    (1 << 30, 1 << 30)]:
+        assert lib.pa_width_bucket(w, ctypes.byref(out)) == 0
+        assert out.value == want, (w, out.value)
+    assert lib.pa_width_bucket(0, ctypes.byref(out)) == -1
+    assert lib.pa_width_bucket((1 << 30) + 1, ctypes.byref(out)) == -1
+    assert lib.pa_width_bucket(8, None) == -1
