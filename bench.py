@@ -118,6 +118,42 @@ def device_rotation(base, i, device):
     return db
 
 
+def long_context_set(batch, length, device, seed=1004):
+    """The long-context low-batch decode shape (Hq=32, Hkv=8, pages scattered over a 40,960-page
+    pool) with K/V/q drawn on the device (seeded); returns (host metadata, device batch)."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from tests._paged import DeviceBatch
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = np.full(batch, length, dtype=np.int64)
+    pool = 40960
+    order = rng.permutation(pool).astype(np.int32)
+    indptr, indices, last, keypos = workloads.csr_from_lengths(lengths, order)
+    meta = types.SimpleNamespace(lengths=lengths, num_kv_heads=8, num_q_heads=32, batch=batch,
+                                 nnz=int(indptr[-1]))
+    db = DeviceBatch.__new__(DeviceBatch)
+    db.host = None
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    shape = (pool, 16, 8, 128)
+    db.k_cache = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    db.v_cache = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    db.q = torch.randn((batch, 32, 1, 128), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+    db.kv_indptr, db.kv_indices, db.kv_last_page_len = t(indptr), t(indices), t(last)
+    db.query_position_ids = t(lengths.reshape(batch, 1))
+    db.cache_position = db.query_position_ids
+    db.key_position_ids = t(keypos)
+    db.q_norm_weight = torch.from_numpy(rng.uniform(0.5, 1.5, 128).astype(np.float32)).to(device)
+    db.k_norm_weight = torch.from_numpy(rng.uniform(0.5, 1.5, 128).astype(np.float32)).to(device)
+    return meta, db
+
+
 def time_calls(fn, sets, steps, warmup):
     """Run fn(set) over the rotation; return (wall ms per step, mean per-launch event ms)."""
     import torch
@@ -334,6 +370,32 @@ def main():
             "avg_launch_ms": round(unit_launch_ms, 5),
             "frac": round(alg / (unit_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+
+    if not args.decode_only and not args.prefill_only:
+        # Long-context low-batch decode (B=1, L=131,072): the 16-stream tree against the
+        # fixed-chunk policy, which cuts the row into 2,048-token chunks (64 chunks).
+        print("[bench] timing long-context decode", file=sys.stderr, flush=True)
+        lmeta, ldb = long_context_set(1, 131072, device)
+        lout = torch.empty_like(ldb.q)
+        llse = torch.empty(lout.shape[:3], dtype=torch.float32, device=device)
+        lalg = decode_bytes(lmeta)
+        long_result = {"workload": "long_context_decode", "batch": 1, "kv_len": 131072, "num_q_heads": 32,
+                       "num_kv_heads": 8, "algorithmic_bytes_per_call": lalg}
+        for name, policy, chunk in (("split_disabled", pa.PA_SPLIT_DISABLED, 0),
+                                    ("split_fixed_2048", pa.PA_SPLIT_FIXED, 2048)):
+            lplan = pa.Plan(32, 8, max_batch=1, max_q_len=1, max_pages_per_row=8192, rms_eps=1e-6,
+                            split_policy=policy, split_chunk_tokens=chunk)
+            lws = pa.decode_workspace(lplan, 1, device=device)
+
+            def lstep(db, lplan=lplan, lws=lws):
+                pa.decode(lplan, *db.args(), out=lout, lse=llse, workspace=lws)
+
+            l_wall, l_launch = time_calls(lstep, [ldb], 20, 3)
+            long_result[name] = {"ms_per_call": round(l_launch, 5),
+                                 "value": round(lalg / (l_launch * 1e-3) / 1e9, 2), "unit": "GB/s",
+                                 "frac": round(lalg / (l_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        result["long_context_decode"] = long_result
+        del ldb
 
     if not args.decode_only:
         print("[bench] timing prefill", file=sys.stderr, flush=True)

@@ -10,6 +10,7 @@ library; the first call does, and raises if it is not built.
 
 from .binding import (  # noqa: F401
     PA_SPLIT_DISABLED,
+    PA_SPLIT_FIXED,
     PagedAttentionError,
     Plan,
     build_csr,

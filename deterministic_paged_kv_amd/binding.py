@@ -16,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpa.so")
 
 PA_SPLIT_DISABLED = 0
+PA_SPLIT_FIXED = 1
 HEAD_DIM = 128
 PAGE_SIZE = 16
 
@@ -30,7 +31,7 @@ class ValidationReport(ctypes.Structure):
 
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [_i32]),
-    "pa_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _i32, ctypes.POINTER(_p)]),
+    "pa_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _i32, _i32, ctypes.POINTER(_p)]),
     "pa_plan_destroy": (_i32, [_p]),
     "pa_validate_metadata": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                                     ctypes.POINTER(ValidationReport)]),
@@ -124,18 +125,20 @@ class Plan:
     def __init__(self, num_q_heads: int, num_kv_heads: int, *, max_batch: int, max_q_len: int,
                  max_pages_per_row: int, head_dim: int = HEAD_DIM, page_size: int = PAGE_SIZE,
                  rope_theta: float = 1e6, rope_scale: float = 1.0, rms_eps: float = 1e-6,
-                 split_policy: int = PA_SPLIT_DISABLED):
+                 split_policy: int = PA_SPLIT_DISABLED, split_chunk_tokens: int = 0):
         lib = load()
         h = ctypes.c_void_p()
         _check(lib.pa_plan(num_q_heads, num_kv_heads, head_dim, page_size, max_batch, max_q_len,
                            max_pages_per_row, rope_theta, rope_scale, rms_eps, split_policy,
-                           ctypes.byref(h)), "pa_plan")
+                           split_chunk_tokens, ctypes.byref(h)), "pa_plan")
         self.handle = h
         self.num_q_heads = num_q_heads
         self.num_kv_heads = num_kv_heads
         self.max_batch = max_batch
         self.max_q_len = max_q_len
         self.max_pages_per_row = max_pages_per_row
+        self.split_policy = split_policy
+        self.split_chunk_tokens = split_chunk_tokens if split_policy == PA_SPLIT_FIXED else 0
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:
@@ -196,8 +199,9 @@ def decode_workspace_size(plan: Plan, batch: int) -> int:
 
 
 def decode_workspace(plan: Plan, batch: int, device="cuda"):
-    """A workspace for pa_decode's multi-compute-unit schedule (needs no initialisation and
-    can be reused by calls that do not overlap in time)."""
+    """A workspace for pa_decode's multi-compute-unit schedule, sized for the plan's split
+    policy (needs no initialisation and can be reused by calls that do not overlap in time;
+    a PA_SPLIT_FIXED plan requires one)."""
     import torch
 
     return torch.empty(decode_workspace_size(plan, batch), dtype=torch.uint8, device=device)

@@ -94,14 +94,17 @@ const char* pa_status_string(pa_status s) {
 
 pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                   int32_t max_batch, int32_t max_q_len, int32_t max_pages_per_row, float rope_theta,
-                  float rope_scale, float rms_eps, int32_t split_policy, pa_plan_t* plan_out) {
+                  float rope_scale, float rms_eps, int32_t split_policy, int32_t split_chunk_tokens,
+                  pa_plan_t* plan_out) {
   if (!plan_out) return PA_ERR_INVALID_ARGUMENT;
   if (num_q_heads < 1 || num_kv_heads < 1 || max_batch < 1 || max_q_len < 1 || max_pages_per_row < 1)
     return PA_ERR_INVALID_ARGUMENT;
   if (!(rms_eps > 0.0f) || !std::isfinite(rms_eps)) return PA_ERR_INVALID_ARGUMENT;
   if (head_dim != kHeadDim || page_size != kPageSize) return PA_ERR_UNSUPPORTED;
   if (rope_theta != 1.0e6f || rope_scale != 1.0f) return PA_ERR_UNSUPPORTED;
-  if (split_policy != PA_SPLIT_DISABLED) return PA_ERR_UNSUPPORTED;
+  if (split_policy != PA_SPLIT_DISABLED && split_policy != PA_SPLIT_FIXED) return PA_ERR_UNSUPPORTED;
+  if (split_policy == PA_SPLIT_FIXED && (split_chunk_tokens < kPageSize || split_chunk_tokens % kPageSize != 0))
+    return PA_ERR_UNSUPPORTED;
   if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_HEAD_RATIO;
   // positions stay int32 and the table below fits in memory
   if ((long long)max_pages_per_row * kPageSize + 1 > (1LL << 24)) return PA_ERR_CAPACITY;
@@ -119,6 +122,7 @@ pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, i
   p->rope_scale = rope_scale;
   p->rms_eps = rms_eps;
   p->split_policy = split_policy;
+  p->split_chunk_pages = split_policy == PA_SPLIT_FIXED ? split_chunk_tokens / kPageSize : 0;
   p->d_rope = nullptr;
   if (hipGetDevice(&p->device) != hipSuccess) { delete p; return PA_ERR_HIP; }
   if (hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess ||
@@ -240,8 +244,10 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
                               kv_last_page_len, query_position_ids, q, k_cache, v_cache, out, lse);
   if (st != PA_OK || batch == 0) return st;
   if (q_len != 1) return PA_ERR_INVALID_ARGUMENT;
-  if (workspace && workspace_bytes < decode_workspace_bytes(batch, plan->num_kv_heads, plan->group))
-    return PA_ERR_WORKSPACE;
+  const size_t need = decode_workspace_bytes(batch, plan->num_kv_heads, plan->group, plan->split_chunk_pages,
+                                             plan->max_pages_per_row);
+  if (plan->split_chunk_pages > 0 && !workspace) return PA_ERR_WORKSPACE;
+  if (workspace && workspace_bytes < need) return PA_ERR_WORKSPACE;
   DecodeParams p;
   p.batch = batch;
   p.num_q_heads = plan->num_q_heads;
@@ -264,13 +270,15 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
   p.lse = lse;
   p.rope = plan->d_rope;
   p.eps = plan->rms_eps;
+  p.chunk_pages = plan->split_chunk_pages;
   return launch_decode(p, workspace, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_decode_workspace_size(pa_plan_t plan, int32_t batch, size_t* bytes) {
   if (!plan_ok(plan) || !bytes || batch < 0) return PA_ERR_INVALID_ARGUMENT;
   if (batch > plan->max_batch) return PA_ERR_CAPACITY;
-  *bytes = decode_workspace_bytes(batch, plan->num_kv_heads, plan->group);
+  *bytes = decode_workspace_bytes(batch, plan->num_kv_heads, plan->group, plan->split_chunk_pages,
+                                  plan->max_pages_per_row);
   return PA_OK;
 }
 
@@ -290,6 +298,7 @@ pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_p
   pa_status st = check_launch(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices,
                               kv_last_page_len, query_position_ids, q, k_cache, v_cache, out, lse);
   if (st != PA_OK || batch == 0) return st;
+  if (plan->split_policy != PA_SPLIT_DISABLED) return PA_ERR_UNSUPPORTED;  // prefill: one pass per row only
   const size_t need = prefill_workspace_bytes(plan->num_q_heads, plan->num_kv_heads, batch, q_len, num_indices);
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
   PrefillParams p;

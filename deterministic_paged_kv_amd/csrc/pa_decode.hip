@@ -229,7 +229,7 @@ __device__ __forceinline__ void pv_page(const Scored& sc, StreamState& st, int r
 }
 
 // One wavefront's walk over the pages first, first + stride, first + 2 stride, ... of one
-// (row, KV head) unit.  Walk step t feeds state st[t % NS]: with stride = kStreams and NS = 1
+// (row, KV head) unit, at most `count` of them.  Walk step t feeds state st[t % NS]: with stride = kStreams and NS = 1
 // the wavefront is stream `first`; with stride = kStreams / 2 and NS = 2 it runs streams
 // `first` (even steps) and `first` + kStreams / 2 (odd steps).  Either way each stream sees its
 // own pages in ascending order.
@@ -241,7 +241,7 @@ __device__ __forceinline__ void pv_page(const Scored& sc, StreamState& st, int r
 // last page (their data is never used), so every step issues the same loads.
 template <int R, int RC, int NS, class Kw>
 __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& ri, int hk, int first, int stride,
-                                         int lane, VSlot& sv, const Kw& kw, StreamState (&st)[NS]) {
+                                         int count, int lane, VSlot& sv, const Kw& kw, StreamState (&st)[NS]) {
   static_assert(R % RC == 0 && R % NS == 0, "the rings and the state cycle must divide the K/V ring");
   const int r = lane & 15;
   const int g = lane >> 4;
@@ -249,7 +249,7 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
   const int n = ri.n, L = ri.L, qp = ri.qp, p0 = ri.p0;
   const bool qnorm = P.q_norm != nullptr;
   const bool knorm = P.k_norm != nullptr;
-  const int steps = n > first ? (n - first + stride - 1) / stride : 0;
+  const int steps = min(count, n > first ? (n - first + stride - 1) / stride : 0);
 
   // the query's inputs go out first: they depend on nothing loaded here
   uint4 qraw[4];
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
 
   // wavefront w walks pages w, w+8, ...: streams w (even steps) and w+8 (odd steps)
   StreamState st[2];
-  run_walk<kUnitRing, 1, 2>(P, ri, hk, wave, kUnitWaves, lane, sm.u.v[wave], KwLds{sm.kw}, st);
+  run_walk<kUnitRing, 1, 2>(P, ri, hk, wave, kUnitWaves, INT32_MAX, lane, sm.u.v[wave], KwLds{sm.kw}, st);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   kw.load(P.k_norm, g);
 
   StreamState st[1];
-  run_walk<kStreamRing, kStreamCsRing, 1>(P, ri, hk, s, kStreams, lane, sv, kw, st);
+  run_walk<kStreamRing, kStreamCsRing, 1>(P, ri, hk, s, kStreams, INT32_MAX, lane, sv, kw, st);
 
   const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per stream state
   if (r < G) {
@@ -502,17 +502,116 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Fixed-chunk policy: the row's pages are cut into chunks of chunk_pages consecutive pages;
+// chunk c (pages c * chunk_pages ..) is one online softmax over its pages in ascending order,
+// on one wavefront, and the chunk states are folded in ascending chunk order.  The tree
+// depends only on the row's length and the chunk size.  Workspace: an int32 poison flag per
+// (unit, chunk slot), then per unit and chunk slot G records of [m, l, 128 accumulators].
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_chunk_kernel(
+    const DecodeParams P, int max_chunks, int32_t* __restrict__ poisons, float* __restrict__ states) {
+  __shared__ VSlot sv;
+  const int unit = blockIdx.x / max_chunks;
+  const int c = blockIdx.x % max_chunks;
+  const int b = unit / P.num_kv_heads;
+  const int hk = unit % P.num_kv_heads;
+  const int lane = threadIdx.x;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int G = P.group;
+  const RowInfo ri = row_info(P, b, hk);
+  if (ri.bad || ri.L == 0) return;                       // the fold kernel writes these rows
+  if (c * P.chunk_pages >= ri.n) return;                 // past the row's last chunk
+  KwRegs kw;
+  kw.load(P.k_norm, g);
+
+  StreamState st[1];
+  run_walk<kStreamRing, kStreamCsRing, 1>(P, ri, hk, c * P.chunk_pages, 1, P.chunk_pages, lane, sv, kw, st);
+
+  const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per chunk state
+  if (r < G) {
+    float* hrec = states + ((size_t)unit * max_chunks + c) * rec + (size_t)r * (2 + kHeadDim);
+    if (g == 0) { hrec[0] = st[0].m; hrec[1] = st[0].l; }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<f32x4*>(hrec + 2 + 16 * nb + 4 * g) = st[0].acc[nb];
+  }
+  if (lane == 0) poisons[unit * max_chunks + c] = st[0].poison;
+}
+
+// Fold of (m, l, acc) in ascending chunk order: with m' = max(m, m_c),
+//   l <- l 2^(m - m') + l_c 2^(m_c - m'),  acc <- acc 2^(m - m') + acc_c 2^(m_c - m'),  m <- m'
+// (a state with m = -inf weighs 0), then out = acc / l and lse = (m + log2 l) ln 2.
+__global__ __launch_bounds__(kCombineThreads) void decode_fold_kernel(const DecodeParams P, int max_chunks,
+                                                                      const int32_t* __restrict__ poisons,
+                                                                      const float* __restrict__ states) {
+#pragma clang fp contract(off)
+  __shared__ int poison_any;
+  const int unit = blockIdx.x;
+  const int b = unit / P.num_kv_heads;
+  const int hk = unit % P.num_kv_heads;
+  const int G = P.group;
+  const int tid = threadIdx.x;
+  const RowInfo ri = row_info(P, b, hk);
+  if (ri.bad || ri.L == 0) {
+    write_degenerate(P, ri, tid, kCombineThreads);
+    return;
+  }
+  const int nch = (ri.n + P.chunk_pages - 1) / P.chunk_pages;
+  const size_t rec = (size_t)G * (2 + kHeadDim);
+  const float* unit_states = states + (size_t)unit * max_chunks * rec;
+  if (tid == 0) poison_any = 0;
+  __syncthreads();
+  for (int c = tid; c < nch; c += kCombineThreads)
+    if (poisons[unit * max_chunks + c] != 0) atomicOr(&poison_any, 1);
+  __syncthreads();
+  for (int idx = tid; idx < G * kHeadDim; idx += kCombineThreads) {
+    const int h = idx / kHeadDim, d = idx % kHeadDim;
+    float m = -__builtin_inff(), l = 0.0f, a = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+      const float* hrec = unit_states + (size_t)c * rec + (size_t)h * (2 + kHeadDim);
+      const float mc = hrec[0], lc = hrec[1], ac = hrec[2 + d];
+      const float mn = fmaxf(m, mc);
+      const float s0 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+      const float s1 = mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - mn);
+      l = l * s0 + lc * s1;
+      a = a * s0 + ac * s1;
+      m = mn;
+    }
+    float o = a / l;
+    float lse = (m + __builtin_log2f(l)) * kLn2;
+    if (poison_any != 0) { o = __builtin_nanf(""); lse = __builtin_nanf(""); }
+    P.out[(ri.head0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
+    if (d == 0) P.lse[ri.head0 + h] = lse;
+  }
+}
+
+int max_chunks_of(int chunk_pages, int max_pages_per_row) {
+  return (max_pages_per_row + chunk_pages - 1) / chunk_pages;
+}
+
 }  // namespace
 
-size_t decode_workspace_bytes(int batch, int num_kv_heads, int group) {
+size_t decode_workspace_bytes(int batch, int num_kv_heads, int group, int chunk_pages, int max_pages_per_row) {
   const size_t units = (size_t)batch * num_kv_heads;
-  return align256(units * kStreams * sizeof(int32_t)) + units * kStreams * group * (2 + kHeadDim) * sizeof(float);
+  const size_t slots = chunk_pages > 0 ? (size_t)max_chunks_of(chunk_pages, max_pages_per_row) : (size_t)kStreams;
+  return align256(units * slots * sizeof(int32_t)) + units * slots * group * (2 + kHeadDim) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t stream) {
   const unsigned units = (unsigned)p.batch * (unsigned)p.num_kv_heads;
   if (units == 0) return hipSuccess;
-  if (workspace == nullptr) {
+  if (p.chunk_pages > 0) {
+    const int max_chunks = max_chunks_of(p.chunk_pages, p.max_pages_per_row);
+    char* ws = (char*)workspace;
+    int32_t* poisons = (int32_t*)ws;
+    ws += align256((size_t)units * max_chunks * sizeof(int32_t));
+    float* states = (float*)ws;
+    hipLaunchKernelGGL(decode_chunk_kernel, dim3(units * (unsigned)max_chunks), dim3(64), 0, stream, p, max_chunks,
+                       poisons, states);
+    hipLaunchKernelGGL(decode_fold_kernel, dim3(units), dim3(kCombineThreads), 0, stream, p, max_chunks,
+                       (const int32_t*)poisons, (const float*)states);
+  } else if (workspace == nullptr) {
     hipLaunchKernelGGL(decode_unit_kernel, dim3(units), dim3(kDecodeThreads), 0, stream, p);
   } else {
     char* ws = (char*)workspace;

@@ -29,6 +29,7 @@ struct pa_plan_s {
   int32_t table_rows;  // positions covered by the cos/sin table: max_pages_per_row * 16 + 1
   float rope_theta, rope_scale, rms_eps;
   int32_t split_policy;
+  int32_t split_chunk_pages;  // PA_SPLIT_FIXED: pages per chunk (chunk tokens / 16); else 0
   int device;
   int32_t num_cus;  // compute units of that device (work placement only, never arithmetic)
   float* d_rope;  // [table_rows][128]: cos of the 64 frequencies, then sin
@@ -254,12 +255,15 @@ struct DecodeParams {
   float* lse;
   const float* rope;
   float eps;
+  int32_t chunk_pages;  // 0: the fixed 16-stream tree; > 0: fixed chunks of this many pages
 };
 
-// Decode.  workspace == NULL: one workgroup per (row, KV head).  Otherwise (at least
-// decode_workspace_bytes, any contents): one wavefront per (row, KV head, stream) on
-// separate compute units, then a combining kernel.  Same bits either way.
-size_t decode_workspace_bytes(int batch, int num_kv_heads, int group);
+// Decode.  chunk_pages == 0 and workspace == NULL: one workgroup per (row, KV head).
+// chunk_pages == 0 with a workspace (at least decode_workspace_bytes, any contents): one
+// wavefront per (row, KV head, stream) on separate compute units, then a combining kernel;
+// same bits either way.  chunk_pages > 0 (needs a workspace): one wavefront per (row, KV
+// head, chunk), then a kernel folding the chunks in ascending order.
+size_t decode_workspace_bytes(int batch, int num_kv_heads, int group, int chunk_pages, int max_pages_per_row);
 hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t stream);
 
 struct ValidateParams {

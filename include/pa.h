@@ -79,10 +79,18 @@ enum {
   PA_ERR_HIP = -13               /* a HIP runtime call failed                                */
 };
 
-/* Split-KV policy ([PR7] "Split-KV Policy").  Only PA_SPLIT_DISABLED is implemented:
- * one pass over each row's keys in a fixed order.  PA_SPLIT_FIXED is reserved and
- * returns PA_ERR_UNSUPPORTED; PA_SPLIT_AUTO is rejected because it makes a row's
- * reduction depend on the batch. */
+/* Split-KV policy ([PR7] "Split-KV Policy": disabled, fixed:<N> with N in logical KV
+ * tokens divisible by the page size, auto).
+ *   PA_SPLIT_DISABLED  the default: decode's fixed 16-stream tree, prefill's one pass.
+ *   PA_SPLIT_FIXED     decode only: each row's keys are cut into chunks of N tokens at
+ *                      positions 0, N, 2N, ... (a length-only partition: [PR162] "Code
+ *                      audit", the Triton backend whose partition depends only on a row's
+ *                      own length); every chunk is one online softmax over its pages in
+ *                      ascending order, and the chunk states are folded in ascending chunk
+ *                      order in FP32.  The tree depends only on the row's length and N, so
+ *                      results stay batch- and plan-width-invariant; the bits differ from
+ *                      PA_SPLIT_DISABLED's.
+ *   PA_SPLIT_AUTO      rejected: it makes a row's reduction depend on the batch. */
 enum { PA_SPLIT_DISABLED = 0, PA_SPLIT_FIXED = 1, PA_SPLIT_AUTO = 2 };
 
 typedef struct pa_plan_s* pa_plan_t;
@@ -101,7 +109,7 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_string(pa_status status);
 
-/* Create a plan: fixed shapes, capacities and the RoPE cos/sin table.
+/* Create a plan: fixed shapes, capacities, the split policy and the RoPE cos/sin table.
  *   num_q_heads, num_kv_heads  Hq, Hkv of one GPU's head share; Hq % Hkv == 0, Hq/Hkv <= 16
  *                              ([PR279] "Scope": GQA packing fixed from the head layout).
  *   head_dim, page_size        must be 128 and 16 ([PR162] "Summary").
@@ -110,7 +118,10 @@ const char* pa_status_string(pa_status status);
  *                              changes the arithmetic ([PR162] "Design notes").
  *   rope_theta, rope_scale     must be 1e6 and 1.0; rms_eps > 0 ([PR7] "FlashInfer RoPE
  *                              Fusion").
- *   split_policy               PA_SPLIT_DISABLED.
+ *   split_policy               PA_SPLIT_DISABLED or PA_SPLIT_FIXED (else
+ *                              PA_ERR_UNSUPPORTED).
+ *   split_chunk_tokens         PA_SPLIT_FIXED: the chunk size N, a positive multiple of 16
+ *                              (else PA_ERR_UNSUPPORTED); ignored otherwise.
  * Allocates device memory for the cos/sin table (max_pages_per_row * page_size + 1
  * positions, 512 bytes each) and synchronises the current device once.  The plan is
  * immutable afterwards and may serve several streams at once.  *plan_out is written
@@ -118,7 +129,7 @@ const char* pa_status_string(pa_status status);
 pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                   int32_t max_batch, int32_t max_q_len, int32_t max_pages_per_row,
                   float rope_theta, float rope_scale, float rms_eps, int32_t split_policy,
-                  pa_plan_t* plan_out);
+                  int32_t split_chunk_tokens, pa_plan_t* plan_out);
 
 /* Free a plan and its device table.  NULL is accepted.  No call using the plan may be in
  * flight on any stream. */
@@ -169,8 +180,11 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
  * itself.  With workspace == NULL one workgroup runs all 16 streams; with a workspace each
  * stream runs on its own compute unit and writes its state there, and a second kernel
  * combines the states, which spreads a long row over 16 compute units.  Both give
- * bit-identical results.  The workspace needs no initialisation (every call writes what it
- * reads).  Calls that overlap in time need separate workspaces.
+ * bit-identical results.  Under a PA_SPLIT_FIXED plan the chunks of N tokens replace the 16
+ * streams: one wavefront per (row, KV head, chunk) writes the chunk's state to the workspace
+ * and a second kernel folds the states in ascending chunk order; the workspace is then
+ * required (PA_ERR_WORKSPACE without one).  The workspace needs no initialisation (every call
+ * writes what it reads).  Calls that overlap in time need separate workspaces.
  * Asynchronous on `stream`; requires q_len == 1 and batch <= plan capacity. */
 pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
                     int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -179,8 +193,9 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
                     const float* q_norm_weight, const float* k_norm_weight,
                     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of pa_decode's multi-compute-unit schedule for `batch` rows (host
- * arithmetic only). */
+/* Workspace bytes of pa_decode's multi-compute-unit schedule for `batch` rows under this
+ * plan's split policy (host arithmetic only; a PA_SPLIT_FIXED plan needs room for
+ * ceil(max_pages_per_row * 16 / N) chunk states per (row, KV head)). */
 pa_status pa_decode_workspace_size(pa_plan_t plan, int32_t batch, size_t* bytes);
 
 /* Workspace bytes pa_prefill needs for these sizes (host arithmetic only). */
@@ -193,7 +208,8 @@ pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len
  * Fusion").  Same arguments and layouts as pa_decode with Sq = q_len, plus a caller-owned
  * device workspace of at least pa_prefill_workspace_size() bytes that holds the
  * normalised, rotated BF16 k^ of every cached key between the two kernels of the call.  Asynchronous
- * on `stream`.  Concurrent calls need separate workspaces. */
+ * on `stream`.  Concurrent calls need separate workspaces.  Prefill runs one pass per
+ * (query block, head); a plan whose policy is not PA_SPLIT_DISABLED gets PA_ERR_UNSUPPORTED. */
 pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
                      int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
                      const int32_t* kv_last_page_len, const int32_t* query_position_ids,

@@ -43,12 +43,14 @@ class DeviceBatch:
                 self.query_position_ids, self.q_norm_weight, self.k_norm_weight)
 
 
-def make_plan(b, max_pages_per_row=None, max_batch=None, max_q_len=None):
+def make_plan(b, max_pages_per_row=None, max_batch=None, max_q_len=None, chunk_tokens=0):
+    """A plan for batch b; chunk_tokens > 0 selects the fixed-chunk split policy."""
     if max_pages_per_row is None:
         max_pages_per_row = max(1, int(np.max(np.diff(b.kv_indptr))) if b.batch else 1)
+    split = pa.PA_SPLIT_FIXED if chunk_tokens > 0 else pa.PA_SPLIT_DISABLED
     return pa.Plan(b.num_q_heads, b.num_kv_heads, max_batch=max_batch or max(b.batch, 1),
                    max_q_len=max_q_len or b.q_len, max_pages_per_row=max_pages_per_row,
-                   rms_eps=b.eps)
+                   rms_eps=b.eps, split_policy=split, split_chunk_tokens=chunk_tokens)
 
 
 def to_numpy(out, lse):

@@ -47,9 +47,9 @@ def test_status_strings(lib):
     assert lib.pa_status_string(12345).decode() == "PA_ERR_UNKNOWN"
 
 
-def _plan(lib, hq=16, hkv=4, d=128, ps=16, mb=1, mq=1, mp=1, theta=1e6, scale=1.0, eps=1e-6, split=0):
+def _plan(lib, hq=16, hkv=4, d=128, ps=16, mb=1, mq=1, mp=1, theta=1e6, scale=1.0, eps=1e-6, split=0, chunk=0):
     h = ctypes.c_void_p()
-    st = lib.pa_plan(hq, hkv, d, ps, mb, mq, mp, theta, scale, eps, split, ctypes.byref(h))
+    st = lib.pa_plan(hq, hkv, d, ps, mb, mq, mp, theta, scale, eps, split, chunk, ctypes.byref(h))
     assert h.value is None  # written only on success; none of these cases succeed
     return st
 
@@ -59,15 +59,20 @@ def test_plan_fails_closed_on_host_arguments(lib):
     assert _plan(lib, ps=32) == -2
     assert _plan(lib, theta=1e4) == -2
     assert _plan(lib, scale=2.0) == -2
-    assert _plan(lib, split=1) == -2          # fixed split: reserved
+    assert _plan(lib, split=1) == -2          # fixed split without a chunk size
+    assert _plan(lib, split=1, chunk=8) == -2     # chunk below one page
+    assert _plan(lib, split=1, chunk=40) == -2    # chunk not a multiple of the page size
+    assert _plan(lib, split=1, chunk=-16) == -2
     assert _plan(lib, split=2) == -2          # auto split: rejected
+    assert _plan(lib, split=2, chunk=64) == -2
+    assert _plan(lib, split=3) == -2          # unknown policy
     assert _plan(lib, hq=16, hkv=3) == -4     # head ratio
     assert _plan(lib, hq=34, hkv=2) == -4     # group of 17 > 16
     assert _plan(lib, hq=0) == -1
     assert _plan(lib, mb=0) == -1
     assert _plan(lib, eps=0.0) == -1
     assert _plan(lib, mp=1 << 21) == -3       # positions past 2^24
-    assert lib.pa_plan(16, 4, 128, 16, 1, 1, 1, 1e6, 1.0, 1e-6, 0, None) == -1
+    assert lib.pa_plan(16, 4, 128, 16, 1, 1, 1, 1e6, 1.0, 1e-6, 0, 0, None) == -1
 
 
 def test_calls_without_a_plan_fail_closed(lib):
