@@ -26,7 +26,8 @@
 //    and so running streams w and w+8, states combined through LDS (no workspace);
 //  * one single-wavefront workgroup per (row, KV head, stream), states written to a caller
 //    workspace, and a second kernel that combines each unit's states in stream order.  This
-//    spreads a long row over 16 compute units; the bits are identical.
+//    spreads a long row over 16 compute units; the bits are identical.  Rows are launched
+//    longest first.
 //
 // Memory layout.  k_cache/v_cache are NHD [page][slot][Hkv][128] bf16: one KV head of one
 // page is 16 rows of 256 B at a stride of Hkv * 256 B.  A lane (r = lane % 16, g = lane / 16)
@@ -437,11 +438,25 @@ constexpr int kCombineThreads = 512;
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const DecodeParams P, int32_t* __restrict__ poisons, float* __restrict__ states) {
   __shared__ VSlot sv;
-  const int unit = blockIdx.x / kStreams;
-  const int s = blockIdx.x % kStreams;
-  const int b = unit / P.num_kv_heads;
-  const int hk = unit % P.num_kv_heads;
   const int lane = threadIdx.x;
+  const int s = blockIdx.x % kStreams;
+  const int hk = (blockIdx.x / kStreams) % P.num_kv_heads;
+  const int rank = blockIdx.x / (kStreams * P.num_kv_heads);
+  // Launch order: rows with more pages first, ties by row (up to 64 rows; beyond that, row
+  // order).  The long rows' streams finish last; starting them first puts their first pages
+  // at the head of the memory queue.  Only where a stream runs depends on it, not its bits.
+  int b = rank;
+  if (P.batch <= 64) {
+    const int my = lane < P.batch ? P.indptr[lane + 1] - P.indptr[lane] : -1;
+    int rk = 0;
+    for (int j = 0; j < P.batch; ++j) {
+      const int nj = __builtin_amdgcn_readlane(my, j);
+      rk += (nj > my || (nj == my && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < P.batch && rk == rank);
+    b = hit ? (int)__builtin_ctzll(hit) : rank;
+  }
+  const int unit = b * P.num_kv_heads + hk;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = P.group;
