@@ -7,16 +7,17 @@
 // K/V order before arithmetic, Split-KV disabled, FP32 LSE, same post-RoPE boundary).
 //
 // Two kernels per call.
-//  1. key_prologue_kernel: every cached key of every KV head goes once through the shared
-//     Q/K prologue (RMSNorm, RoPE, BF16); k^ is written in logical order to the workspace,
-//     [Hkv][nnz * 16][128], key j of row b at (kv_indptr[b] * 16 + j); slots past a row's
-//     length are written as zeros.
+//  1. key_prologue_kernel: every cached key of every KV head of every valid row goes once
+//     through the shared Q/K prologue (RMSNorm, RoPE, BF16); k^ is written in logical order
+//     to the workspace, [Hkv][nnz * 16][128], key j of row b at (kv_indptr[b] * 16 + j);
+//     slots past a row's length are written as zeros.
 //  2. attend_kernel: one workgroup per (block of 32 queries, row, KV head, group of up to 4
 //     query heads); wavefront w handles one query head of the KV head's GQA group and runs
 //     the prologue of its own queries.  Key tiles of 32 (2 pages) are visited in ascending
 //     order up to the block's last visible key; the workgroup stages each tile's k^ and V in
-//     LDS once for all its heads, with the next tile's loads in flight while the current one
-//     is used.  Per tile: S^T = K^ Q^T (bf16 MFMA, FP32 accumulation), causal mask on logical
+//     LDS once for all its heads, with two tiles' loads in flight, and the step is software-
+//     pipelined (the scores of the next tile on the matrix cores during this tile's softmax).
+//     Long and short items are paired on compute units.  Per tile: S^T = K^ Q^T (bf16 MFMA, FP32 accumulation), causal mask on logical
 //     positions (key j visible to a query at position p iff j <= p) on tiles that cross the
 //     diagonal, FP32 online softmax with a fixed reduction order, O^T += V^T P^T (P rounded
 //     to bf16 for the MFMA, FP32 accumulation).  The softmax reference of a query follows its
@@ -71,12 +72,22 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // ---------------------------------------------------------------------------------------
 // 1. k^ for every cached key
 // ---------------------------------------------------------------------------------------
+// Row b = blockIdx.y; its (page, KV head) tasks are spread over the x blocks, 4 wavefronts each
+// (task t: page t / Hkv of the row, KV head t % Hkv, so neighbouring wavefronts share a page's
+// positions).  Only the keys of valid rows are written; nothing reads the other slots.
 __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int k_tiles = P.num_indices * P.num_kv_heads;
-  const int waves = gridDim.x * (blockDim.x >> 6);
+  const int b = blockIdx.y;
+  const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
+  const int n = p1 - p0;
+  const int lpl = P.last_page_len[b];
+  const bool row_ok = p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && lpl >= 1 &&
+                      lpl <= kPageSize;
+  if (!row_ok) return;  // the attention kernel treats such a row as empty or poisoned
+  const int L = (n - 1) * kPageSize + lpl;
+  const int Hkv = P.num_kv_heads;
   const bool knorm = P.k_norm != nullptr;
   float kw[32];
 #pragma unroll
@@ -85,37 +96,25 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
     for (int e = 0; e < 8; ++e) kw[kb * 8 + e] = knorm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
   const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
-
-  for (int kt = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); kt < k_tiles; kt += waves) {
-    const int hk = kt / P.num_indices;
-    const int gp = kt % P.num_indices;  // page slot in kv_indices
-    // row owning this page slot: last b with indptr[b] <= gp
-    int lo = 0, hi = P.batch;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (P.indptr[mid] <= gp) lo = mid; else hi = mid;
-    }
-    const int b = lo;
-    const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
-    const int n = p1 - p0, pr = gp - p0;
-    const int lpl = P.last_page_len[b];
-    const bool row_ok = p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && pr >= 0 &&
-                        pr < n && lpl >= 1 && lpl <= kPageSize;
-    const int L = row_ok ? (n - 1) * kPageSize + lpl : 0;
+  const int tasks = n * Hkv;
+  const int stride = gridDim.x * (blockDim.x >> 6);
+  for (int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < tasks; t += stride) {
+    const int pr = t / Hkv;
+    const int hk = t % Hkv;
     const int j = pr * kPageSize + r;  // logical key index = key position
-    const bool live = row_ok && j < L;
-    int phys = P.indices[gp];
+    const bool live = j < L;
+    float4 cs[8];
+    load_cos_sin(P.rope, live ? j : 0, g, cs);  // depends on the position only: goes out first
+    int phys = P.indices[p0 + pr];
     const bool page_ok = phys >= 0 && phys < P.num_pages;
     if (!page_ok) phys = 0;
-    const size_t src = (((size_t)phys * kPageSize + r) * P.num_kv_heads + hk) * kHeadDim + 8 * g;
+    const size_t src = (((size_t)phys * kPageSize + r) * Hkv + hk) * kHeadDim + 8 * g;
     uint4 raw[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.k_cache + src + 32 * kb) : zero4;
-    float4 cs[8];
-    load_cos_sin(P.rope, live ? j : 0, g, cs);
     bf16x8 op[4];
     prologue_operand(raw, kw, knorm, P.eps, cs, op);
-    uint16_t* dst = kh + ((size_t)hk * P.num_indices * kPageSize + (size_t)gp * kPageSize + r) * kHeadDim + 8 * g;
+    uint16_t* dst = kh + ((size_t)hk * P.num_indices * kPageSize + (size_t)(p0 + pr) * kPageSize + r) * kHeadDim + 8 * g;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !page_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
   }
@@ -513,10 +512,11 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   uint16_t* kh = (uint16_t*)p.workspace;
-  const long long tasks = (long long)p.num_indices * p.num_kv_heads;
-  if (tasks > 0) {
-    const unsigned pro_blocks = (unsigned)std::min<long long>((tasks + 3) / 4, 8192);
-    hipLaunchKernelGGL(key_prologue_kernel, dim3(pro_blocks), dim3(256), 0, stream, p, kh);
+  if (p.num_indices > 0) {
+    // per row: up to max_pages_per_row * Hkv tasks, 4 per block, at most 512 blocks per row
+    const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * p.num_kv_heads;
+    const unsigned bx = (unsigned)std::min<long long>((row_tasks + 3) / 4, 512);
+    hipLaunchKernelGGL(key_prologue_kernel, dim3(bx, (unsigned)p.batch), dim3(256), 0, stream, p, kh);
   }
   const unsigned nqb = (unsigned)((p.q_len + kQBlock - 1) / kQBlock);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
