@@ -6,8 +6,9 @@ and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
 HIP library: no kernels, headers, helpers, tables or constants.
 
 What it computes, and the passages it follows, are documented function by
-function in :mod:`oracle.definition` (attention) and :mod:`oracle.csr` (the CSR
-block table built from a dense one).  Every function there is pinned by
+function in :mod:`oracle.definition` (attention), :mod:`oracle.csr` (the CSR
+block table built from a dense one) and :mod:`oracle.backward` (the gradients of
+full-prefill attention).  Every function there is pinned by
 ``tests/test_oracle_pins.py`` against closed forms, invariants, library
 routines or brute force on tiny inputs; none is "parity unpinned".
 """
@@ -28,3 +29,4 @@ from .definition import (  # noqa: F401
     paged_attention,
 )
 from .csr import csr_from_block_table  # noqa: F401
+from .backward import prefill_forward_backward  # noqa: F401
