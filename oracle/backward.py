@@ -35,10 +35,11 @@ from .definition import f32_from_bf16_bits, prologue, rope_cos_sin
 
 def _norm_rope_forward(x, w, cos, sin, eps):
     """Exact-arithmetic prologue: y = x r w (r = (mean x^2 + eps)^-1/2), then rotate-half RoPE.
+    Without a weight (w None) there is no RMSNorm, as in the forward reference: y = x.
     x [..., D] float64.  Returns (rotated, r)."""
     d = x.shape[-1]
     r = 1.0 / np.sqrt(np.sum(x * x, axis=-1) / d + eps)
-    y = x * r[..., None] * (1.0 if w is None else w)
+    y = x if w is None else x * r[..., None] * w
     h = d // 2
     y1, y2 = y[..., :h], y[..., h:]
     return np.concatenate([y1 * cos - y2 * sin, y2 * cos + y1 * sin], axis=-1), r
@@ -56,8 +57,9 @@ def _norm_rope_backward(x, w, cos, sin, r, g):
     h = d // 2
     g1, g2 = g[..., :h], g[..., h:]
     dy = np.concatenate([g1 * cos + g2 * sin, -g1 * sin + g2 * cos], axis=-1)
-    wv = 1.0 if w is None else w
-    wdy = wv * dy
+    if w is None:
+        return dy, None
+    wdy = w * dy
     dx = r[..., None] * wdy - x * (r ** 3)[..., None] * (np.sum(x * wdy, axis=-1) / d)[..., None]
     dw = None if w is None else np.sum((x * r[..., None] * dy).reshape(-1, d), axis=0)
     return dx, dw

@@ -19,6 +19,28 @@ def _exact_inputs(rng, B=1, Hq=4, Hkv=2, S=5):
                 wq=rng.uniform(0.5, 1.5, D), wk=rng.uniform(0.5, 1.5, D))
 
 
+def test_gradients_without_norm_match_central_differences():
+    """No norm weights: the prologue is the rotation alone (as the forward reference skips the
+    RMSNorm when the weight is None)."""
+    rng = np.random.default_rng(12)
+    inp = _exact_inputs(rng)
+    inp["wq"] = inp["wk"] = None
+    pos = np.array([[0, 1, 2, 3, 4]])
+    _, _, dq, dk, dv, dwq, dwk = prefill_forward_backward(None, None, None, None, None, pos, None, exact_inputs=inp)
+    assert dwq is None and dwk is None
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        flat = inp[name].reshape(-1)
+        for i in rng.choice(flat.size, size=20, replace=False):
+            keep = flat[i]
+            flat[i] = keep + 1e-6
+            up = _loss(inp, pos)
+            flat[i] = keep - 1e-6
+            dn = _loss(inp, pos)
+            flat[i] = keep
+            fd = (up - dn) / 2e-6
+            assert abs(fd - grad.reshape(-1)[i]) <= 1e-6 * max(1.0, abs(fd)), (name, int(i))
+
+
 def _loss(inp, pos):
     out = prefill_forward_backward(None, None, None, None, None, pos, None, exact_inputs=inp)[0]
     return float(np.sum(out * inp["dout"]))
