@@ -3,8 +3,9 @@
 The computation lives in hand-written HIP kernels behind the C ABI of
 ``include/pa.h`` (``libpa.so``, built in-tree by ``build.py``).  This package is
 the thin Python binding over it: :class:`Plan`, :func:`validate_metadata`,
-:func:`decode`, :func:`prefill`, and the device-side CSR builder :func:`build_csr`
-with its plan-width helper :func:`width_bucket`.  Importing it does not load the
+:func:`decode`, :func:`prefill`, the full-prefill backward :func:`prefill_backward`,
+and the device-side CSR builder :func:`build_csr` with its plan-width helper
+:func:`width_bucket`.  Importing it does not load the
 library; the first call does, and raises if it is not built.
 """
 
@@ -19,6 +20,8 @@ from .binding import (  # noqa: F401
     decode_workspace_size,
     load,
     prefill,
+    prefill_backward,
+    prefill_backward_workspace_size,
     prefill_workspace_size,
     status_string,
     validate_metadata,

@@ -40,6 +40,9 @@ SIGNATURES = {
     "pa_prefill_workspace_size": (_i32, [_p, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "pa_build_csr": (_i32, [_i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "pa_prefill_backward_workspace_size": (_i32, [_p, _i32, _i32, ctypes.POINTER(_sz)]),
+    "pa_prefill_backward": (_i32, [_p, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                   _sz, _p]),
     "pa_width_bucket": (_i32, [_i32, ctypes.POINTER(_i32)]),
 }
 
@@ -305,3 +308,49 @@ def width_bucket(width: int) -> int:
     out = ctypes.c_int32()
     _check(load().pa_width_bucket(int(width), ctypes.byref(out)), "pa_width_bucket")
     return int(out.value)
+
+
+def prefill_backward_workspace_size(plan: Plan, batch: int, seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().pa_prefill_backward_workspace_size(plan.handle, batch, seq_len, ctypes.byref(n)),
+           "pa_prefill_backward_workspace_size")
+    return int(n.value)
+
+
+def prefill_backward(plan: Plan, positions, q, k, v, out, lse, dout, q_norm_weight=None, k_norm_weight=None,
+                     workspace=None, stream=None):
+    """pa_prefill_backward on dense training-layout tensors.
+
+    positions int32 [B, S]; q, out, dout bf16 [B, Hq, S, 128]; k, v bf16 [B, Hkv, S, 128];
+    lse fp32 [B, Hq, S].  Returns (dq, dk, dv, dq_norm_weight, dk_norm_weight) as fp32 tensors
+    (the weight gradients are None where that norm is absent)."""
+    import torch
+
+    _need(q, "q", torch.bfloat16, 4)
+    B, Hq, S, D = q.shape
+    if Hq != plan.num_q_heads or D != HEAD_DIM:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the plan")
+    kv_shape = (B, plan.num_kv_heads, S, D)
+    _need(k, "k", torch.bfloat16, shape=kv_shape)
+    _need(v, "v", torch.bfloat16, shape=kv_shape)
+    _need(out, "out", torch.bfloat16, shape=q.shape)
+    _need(dout, "dout", torch.bfloat16, shape=q.shape)
+    _need(lse, "lse", torch.float32, shape=(B, Hq, S))
+    _need(positions, "positions", torch.int32, shape=(B, S))
+    for name, w in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if w is not None:
+            _need(w, name, torch.float32, shape=(HEAD_DIM,))
+    dev = q.device
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(kv_shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(kv_shape, dtype=torch.float32, device=dev)
+    dwq = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if q_norm_weight is not None else None
+    dwk = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if k_norm_weight is not None else None
+    if workspace is None:
+        workspace = torch.empty(prefill_backward_workspace_size(plan, B, S), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(load().pa_prefill_backward(plan.handle, B, S, _ptr(positions), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(out), _ptr(lse), _ptr(dout),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(workspace),
+                                      int(workspace.numel()), _stream(stream)), "pa_prefill_backward")
+    return dq, dk, dv, dwq, dwk

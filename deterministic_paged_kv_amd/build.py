@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.hip", "pa_validate.hip", "pa_decode.hip", "pa_prefill.hip", "pa_csr.hip"]
+SOURCES = ["pa_api.hip", "pa_validate.hip", "pa_decode.hip", "pa_prefill.hip", "pa_csr.hip", "pa_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -24,6 +24,7 @@ FLAGS = [
 EXTRA = {
     "pa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "pa_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -329,4 +329,53 @@ pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_p
   return launch_prefill(p, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_prefill_backward_workspace_size(pa_plan_t plan, int32_t batch, int32_t seq_len, size_t* bytes) {
+  if (!plan_ok(plan) || !bytes || batch < 0 || seq_len < 1) return PA_ERR_INVALID_ARGUMENT;
+  if (batch > plan->max_batch || seq_len > plan->max_q_len) return PA_ERR_CAPACITY;
+  *bytes = backward_workspace_bytes(batch, seq_len, plan->num_q_heads, plan->num_kv_heads);
+  return PA_OK;
+}
+
+pa_status pa_prefill_backward(pa_plan_t plan, int32_t batch, int32_t seq_len, const int32_t* positions,
+                              const void* q, const void* k, const void* v, const float* q_norm_weight,
+                              const float* k_norm_weight, const void* out, const float* lse, const void* dout,
+                              float* dq, float* dk, float* dv, float* dq_norm_weight, float* dk_norm_weight,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan_ok(plan)) return PA_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || seq_len < 1) return PA_ERR_INVALID_ARGUMENT;
+  if (batch > plan->max_batch || seq_len > plan->max_q_len) return PA_ERR_CAPACITY;
+  if (plan->split_policy != PA_SPLIT_DISABLED) return PA_ERR_UNSUPPORTED;
+  if (batch == 0) return PA_OK;
+  if (!positions || !q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return PA_ERR_INVALID_ARGUMENT;
+  if ((q_norm_weight && !dq_norm_weight) || (k_norm_weight && !dk_norm_weight)) return PA_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < backward_workspace_bytes(batch, seq_len, plan->num_q_heads, plan->num_kv_heads))
+    return PA_ERR_WORKSPACE;
+  pa_status st = check_device(plan);
+  if (st != PA_OK) return st;
+  BackwardArgs a;
+  a.batch = batch;
+  a.seq = seq_len;
+  a.num_q_heads = plan->num_q_heads;
+  a.num_kv_heads = plan->num_kv_heads;
+  a.table_rows = plan->table_rows;
+  a.positions = positions;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.q_norm = q_norm_weight;
+  a.k_norm = k_norm_weight;
+  a.rope = plan->d_rope;
+  a.eps = plan->rms_eps;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_norm = dq_norm_weight;
+  a.dk_norm = dk_norm_weight;
+  a.workspace = workspace;
+  return launch_backward(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -1,0 +1,746 @@
+// Deterministic backward of full-prefill attention (the training layout).
+//
+// Sources: "[WS2][PR7][Attention] Add FlashInfer RoPE-fused paged attention scaffold",
+// section "Scope" (the strict path requires a deterministic backward, dropout 0); "WS2 PR7
+// Fused Attention Backend Alignment", sections "Goal" (a training full-prefill lane) and
+// "Original PR7 Requirements" (the training forward is full prefill; dq/dk/dv belong to the
+// training backward).  The forward it differentiates is the library's: q^ = bf16(RoPE(
+// RMSNorm(q) w_q)), k^ likewise, s = q^.k^ / sqrt(128) over keys at positions <= the query's,
+// softmax, out = P V.  The BF16 roundings at the post-RoPE boundary and of out pass gradients
+// through unchanged.
+//
+// Layout: q, dout, out [B, Hq, S, 128] bf16; k, v [B, Hkv, S, 128] bf16; positions [B, S]
+// (token i of row b has its query and its key at positions[b][i]); lse [B, Hq, S] fp32 (the
+// forward's, natural log).  Outputs dq [B, Hq, S, 128], dk and dv [B, Hkv, S, 128] fp32, and
+// the gradients of the two RMSNorm weights, fp32 [128].
+//
+// Four kernels, every sum in a fixed order (no atomics):
+//  1. bwd_prep_kernel: q^ and k^ (the forward's prologue, bit for bit) into the workspace,
+//     and Dv = sum_d dout * out per query (FP32: a lane's 32 terms in order, then the four
+//     lanes of the query pairwise).
+//  2. bwd_dq_kernel: one workgroup per (32 queries, row, KV head, up to 4 query heads), as in
+//     the forward; per 32-key tile, staged in LDS for the 4 heads: S^T = K^ Q^T, P^T from the
+//     forward's LSE, dP^T = V dO^T, dS^T = P^T (dP^T - Dv), dQ^T += K^T dS^T (key tiles in
+//     ascending order).  The epilogue applies the transposed rotation and the RMSNorm
+//     backward, writes dq, and writes this wavefront's share of the q weight gradient.
+//  3. bwd_dkdv_kernel: one workgroup per (16 keys, row, KV head); wavefront w takes query heads
+//     w, w+4, ... of the group in ascending order, and their 32-query tiles in ascending
+//     order: S = Q^ K^T, P, dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.  The four
+//     wavefronts' sums are added in wavefront order; the epilogue writes dv, and dk through
+//     the prologue backward, and the workgroup's share of the k weight gradient.
+//  4. bwd_dw_kernel: the weight-gradient shares summed in workgroup order.
+// MFMA operands are BF16 (q^, k^, v, dout, and P and dS rounded to BF16), accumulation FP32.
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kQB = 32;                 // queries per wavefront (dq kernel) / per tile (dkdv kernel)
+constexpr int kKTile = 32;              // keys per tile (dq kernel)
+constexpr int kKB = 16;                 // keys per workgroup (dkdv kernel)
+constexpr int kRowB = kHeadDim + 16;    // padded LDS row (conflict-free transposed reads)
+constexpr int kBwdThreads = 256;
+constexpr float kLog2e = 1.4426950408889634074f;
+constexpr float kSoftmaxScale = 0.08838834764831844055f;  // 1 / sqrt(128)
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ i16x8 concat4(const i16x4& a, const i16x4& b) {
+  return i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ i16x4 pack4_bf16(float a, float b, float c, float d) {
+  return i16x4{__builtin_bit_cast(short, (__bf16)a), __builtin_bit_cast(short, (__bf16)b),
+               __builtin_bit_cast(short, (__bf16)c), __builtin_bit_cast(short, (__bf16)d)};
+}
+
+// cos/sin of the frequencies of the accumulator layout: lane group g, block nb = 0..3 holds
+// frequencies 16 nb + 4 g + i (i = 0..3), the rotation partners of dims 16 nb + 4 g + i and
+// 64 + 16 nb + 4 g + i.  Read from the plan's table (blocks of 16 positions, [e][lane][4]; entry
+// q of lane (pos % 16) + 16 g' holds the cos of frequencies f(q, g') .. + 3, entry 4 + q the
+// sin, f(q, g') = 8 g' + 4 q for q < 2 and 32 + 8 g' + 4 (q - 2) otherwise).
+__device__ __forceinline__ void load_cos_sin_acc(const float* rope, int pos, int g, float4 c[4], float4 s[4]) {
+  const float4* blk = reinterpret_cast<const float4*>(rope + (size_t)(pos >> 4) * kRopeBlockFloats);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int f0 = 16 * nb + 4 * g;
+    const int gp = f0 < 32 ? (f0 >> 3) : ((f0 - 32) >> 3);
+    const int q = f0 < 32 ? ((f0 >> 2) & 1) : 2 + (((f0 - 32) >> 2) & 1);
+    const int lane = (pos & 15) + 16 * gp;
+    c[nb] = blk[q * 64 + lane];
+    s[nb] = blk[(4 + q) * 64 + lane];
+  }
+}
+
+struct BwdParams {
+  int32_t batch, seq, num_q_heads, num_kv_heads, group, table_rows;
+  const int32_t* pos;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;
+  const float* q_norm;
+  const float* k_norm;
+  const float* rope;
+  float eps;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dq_norm;
+  float* dk_norm;
+  // workspace
+  uint16_t* qh;   // [B, Hq, S, 128]
+  uint16_t* kh;   // [B, Hkv, S, 128]
+  float* dvec;    // [B, Hq, S]
+  float* dwq_part;  // [dq workgroups][4][128]
+  float* dwk_part;  // [dkdv workgroups][128]
+  int32_t dq_wgs, dkdv_wgs;
+};
+
+__device__ __forceinline__ int safe_pos(const BwdParams& P, int b, int i, bool& bad) {
+  int p = P.pos[(size_t)b * P.seq + i];
+  if (p < 0 || p >= P.table_rows) { bad = true; p = 0; }
+  return p;
+}
+
+// ---------------------------------------------------------------------------------------
+// 1. q^, k^ and Dv.  One wavefront per 16 tokens of one head (queries first, then keys).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const BwdParams P) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int tiles = (P.seq + 15) / 16;
+  const int q_tasks = P.batch * P.num_q_heads * tiles;
+  const int k_tasks = P.batch * P.num_kv_heads * tiles;
+  const int waves = gridDim.x * (blockDim.x >> 6);
+  const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+  for (int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < q_tasks + k_tasks; t += waves) {
+    const bool is_q = t < q_tasks;
+    const int u = is_q ? t : t - q_tasks;
+    const int H = is_q ? P.num_q_heads : P.num_kv_heads;
+    const int tile = u % tiles;
+    const int bh = u / tiles;  // b * H + h
+    const int b = bh / H;
+    const int i = tile * 16 + r;
+    const bool live = i < P.seq;
+    bool bad = false;
+    const int pos = live ? safe_pos(P, b, i, bad) : 0;
+    const size_t row = ((size_t)bh * P.seq + (live ? i : 0)) * kHeadDim + 8 * g;
+    const uint16_t* src = is_q ? P.q : P.k;
+    const float* wsrc = is_q ? P.q_norm : P.k_norm;
+    uint4 raw[4];
+    float w[32];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      raw[kb] = live ? ldg16(src + row + 32 * kb) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = wsrc ? wsrc[32 * kb + 8 * g + e] : 1.0f;
+    }
+    float4 cs[8];
+    load_cos_sin(P.rope, pos, g, cs);
+    bf16x8 op[4];
+    prologue_operand(raw, w, wsrc != nullptr, P.eps, cs, op);
+    uint16_t* dst = (is_q ? P.qh : P.kh) + row;
+    if (live) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        *reinterpret_cast<uint4*>(dst + 32 * kb) = bad ? nan4 : __builtin_bit_cast(uint4, op[kb]);
+    }
+    if (is_q) {
+      // Dv = sum over dims of dout * out
+      float acc = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float a[8], o[8];
+        unpack8(live ? ldg16(P.dout + row + 32 * kb) : make_uint4(0, 0, 0, 0), a);
+        unpack8(live ? ldg16(P.out + row + 32 * kb) : make_uint4(0, 0, 0, 0), o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(a[e], o[e], acc);
+      }
+      acc = pair32_sum(pair16_sum(acc));
+      if (live && g == 0) P.dvec[(size_t)bh * P.seq + i] = acc;
+    }
+  }
+}
+
+// The prologue backward of one token in the accumulator layout (lane (r, g): dims 16 nb + 4 g
+// + i, nb = 0..7), on the four lanes r, r+16, r+32, r+48 together.  grad: d loss / d (rotated
+// vector); x: the pre-norm input; w: the norm weights of the lane's dims (1 without a norm).
+// Writes dx (the gradient of the input) and accumulates x r dy into dw (the weight gradient).
+//   dy1 = g1 c + g2 s, dy2 = -g1 s + g2 c          (the inverse rotation)
+//   dx  = r w dy - x r^3 (1/128) sum_k x_k w_k dy_k,  r = (mean(x^2) + eps)^-1/2
+__device__ __forceinline__ void prologue_backward(const f32x4 grad[8], const float x[8][4], const float4 wv[8],
+                                                  bool norm, float eps, const float4 c[4], const float4 s[4],
+                                                  float dx[8][4], float dw[8][4]) {
+  float dy[8][4];
+  const float* cf = reinterpret_cast<const float*>(c);
+  const float* sf = reinterpret_cast<const float*>(s);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g1 = grad[nb][i], g2 = grad[nb + 4][i];
+      const float cc = cf[4 * nb + i], ss = sf[4 * nb + i];
+      dy[nb][i] = g1 * cc + g2 * ss;
+      dy[nb + 4][i] = g2 * cc - g1 * ss;
+    }
+  if (!norm) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dx[nb][i] = dy[nb][i];
+    return;
+  }
+  // r from the exact sum of squares (as the forward)
+  double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = __builtin_fma((double)x[nb][i], (double)x[nb][i], s4[i]);
+  double ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  ss = pair16_sum(ss);
+  ss = pair32_sum(ss);
+  const float ms = (float)(ss * (1.0 / kHeadDim));
+  const float rr = (float)(1.0 / __builtin_sqrt((double)(ms + eps)));
+  const float* wf = reinterpret_cast<const float*>(wv);
+  float sum = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum = __builtin_fmaf(x[nb][i], wf[4 * nb + i] * dy[nb][i], sum);
+  sum = pair32_sum(pair16_sum(sum));
+  const float k3 = rr * rr * rr * sum * (1.0f / kHeadDim);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dx[nb][i] = rr * wf[4 * nb + i] * dy[nb][i] - x[nb][i] * k3;
+      dw[nb][i] = __builtin_fmaf(x[nb][i] * rr, dy[nb][i], dw[nb][i]);
+    }
+}
+
+// x (bf16 input) and the norm weights of the lane's accumulator-layout dims for one token
+__device__ __forceinline__ void load_acc_layout(const uint16_t* rowp, const float* w, int g, float x[8][4],
+                                                float4 wv[8], bool live) {
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const uint2 u = live ? *reinterpret_cast<const uint2*>(rowp + 16 * nb + 4 * g) : make_uint2(0, 0);
+    x[nb][0] = bf16_lo(u.x); x[nb][1] = bf16_hi(u.x);
+    x[nb][2] = bf16_lo(u.y); x[nb][3] = bf16_hi(u.y);
+    wv[nb] = w ? *reinterpret_cast<const float4*>(w + 16 * nb + 4 * g) : make_float4(1.f, 1.f, 1.f, 1.f);
+  }
+}
+
+// Sum over the 16 lanes of a lane group (a fixed butterfly; both lanes of a pair add the same
+// two values, and IEEE addition is commutative, so they agree) of each of the 32 values.
+__device__ __forceinline__ void sum16(float v[8][4]) {
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[nb][i] = v[nb][i] + __shfl_xor(v[nb][i], sh);
+}
+
+// ---------------------------------------------------------------------------------------
+// 2. dq
+// ---------------------------------------------------------------------------------------
+struct DqSmem {
+  uint16_t k[2][kKTile][kRowB];
+  uint16_t v[2][kKTile][kRowB];
+  int kpos[2][kKTile];
+};
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) {
+  __shared__ DqSmem sm;
+  const int G = P.group;
+  const int Hkv = P.num_kv_heads;
+  const int S = P.seq;
+  const int nqb = (S + kQB - 1) / kQB;
+  const int nhg = (G + 3) / 4;
+  const int per_qb = P.batch * Hkv * nhg;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per_qb);  // longest first
+  int rest = blockIdx.x % per_qb;
+  const int hg = rest % nhg;
+  rest /= nhg;
+  const int b = rest / Hkv;
+  const int hk = rest % Hkv;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int gi = hg * 4 + wave;
+  const bool head_live = gi < G;
+  const int h = hk * G + (head_live ? gi : 0);
+  const size_t qrow0 = ((size_t)b * P.num_q_heads + h) * S;   // token 0 of this head
+  const size_t krow0 = ((size_t)b * Hkv + hk) * S;
+
+  // this lane's queries (t = 0, 1: query 16 t + r of the block)
+  int qpos[2], qi[2];
+  float lse2[2], dv_[2];
+  bf16x8 qop[2][4], dop[2][4];
+  int qmax = -1;
+  bool bad = false;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = qb * kQB + 16 * t + r;
+    qi[t] = i;
+    const bool live = i < S;
+    qpos[t] = live ? safe_pos(P, b, i, bad) : -1;
+    qmax = max(qmax, qpos[t]);
+    lse2[t] = live ? P.lse[qrow0 + i] * kLog2e : 0.0f;
+    dv_[t] = live ? P.dvec[qrow0 + i] : 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const size_t off = (qrow0 + (live ? i : 0)) * kHeadDim + 32 * kb + 8 * g;
+      qop[t][kb] = __builtin_bit_cast(bf16x8, live ? ldg16(P.qh + off) : make_uint4(0, 0, 0, 0));
+      dop[t][kb] = __builtin_bit_cast(bf16x8, live ? ldg16(P.dout + off) : make_uint4(0, 0, 0, 0));
+    }
+  }
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) qmax = max(qmax, __shfl_xor(qmax, sh));
+  qmax = __builtin_amdgcn_readfirstlane(qmax);
+  // every wavefront of the block has the same queries: the key tiles to visit are the ones
+  // holding a key at or before the last query position (keys are visited in token order)
+  const int ntiles = (S + kKTile - 1) / kKTile;
+
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int jr = 4 * g + (r >> 2);
+  const int jc = 4 * (r & 3);
+  const int rt = tid >> 4;     // staging: key rows rt and rt + 16 of a tile
+  const int col = tid & 15;
+
+  // a tile's share of one thread: k^ and V rows rt and rt + 16, and (threads < 32) one key's
+  // position; loaded one tile ahead, written to LDS after the current tile is used
+  uint4 kr[2], vr[2];
+  int kp_next = INT32_MAX;
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = kt * kKTile + 16 * u + rt;
+      const bool live = j < S;
+      const size_t off = (krow0 + (live ? j : 0)) * kHeadDim + col * 8;
+      kr[u] = live ? ldg16(P.kh + off) : make_uint4(0, 0, 0, 0);
+      vr[u] = live ? ldg16(P.v + off) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kKTile) {
+      const int j = kt * kKTile + tid;
+      bool kb_ = false;
+      // keys past the row get a position no query can see
+      kp_next = j < S ? safe_pos(P, b, j, kb_) : INT32_MAX;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<uint4*>(&sm.k[buf][16 * u + rt][col * 8]) = kr[u];
+      *reinterpret_cast<uint4*>(&sm.v[buf][16 * u + rt][col * 8]) = vr[u];
+    }
+    if (tid < kKTile) sm.kpos[buf][tid] = kp_next;
+  };
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) load_tile(kt + 1);
+    // skip the tile when all its keys come after every query of the block
+    int kmin = sm.kpos[buf][lane & 31];
+#pragma unroll
+    for (int sh = 1; sh < 32; sh <<= 1) kmin = min(kmin, __shfl_xor(kmin, sh));
+    kmin = __builtin_amdgcn_readfirstlane(kmin);
+    if (head_live && kmin <= qmax) {
+      f32x4 s[2][2], dp[2][2];  // [ks][t]: keys 16 ks + 4 g + i, query 16 t + r
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 ka[4], va[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
+          va[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.v[buf][16 * ks + r][32 * kb + 8 * g]));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          s[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            s[ks][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], s[ks][t], 0, 0, 0);
+            dp[ks][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kb], dop[t][kb], dp[ks][t], 0, 0, 0);
+          }
+        }
+      }
+      // dS^T = P^T (dP^T - Dv), P^T = 2^(s c log2e - lse log2e) on visible keys, else 0
+      i16x4 dsb[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float d4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kp = sm.kpos[buf][16 * ks + 4 * g + i];
+            const float p = kp <= qpos[t] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks][t][i], kScoreScaleLog2, -lse2[t])) : 0.0f;
+            d4[i] = p * (dp[ks][t][i] - dv_[t]);
+          }
+          dsb[t][ks] = pack4_bf16(d4[0], d4[1], d4[2], d4[3]);
+        }
+      // dQ^T += K^T dS^T over the tile's 32 keys: k-slot 8g+e holds key 4g+e (e < 4) and key
+      // 16+4g+(e-4) (e >= 4) in both operands; K^T from two transposed reads per column block
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][jr][16 * nb + jc]));
+        const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][16 + jr][16 * nb + jc]));
+        const bf16x8 kt8 = __builtin_bit_cast(bf16x8, concat4(k0, k1));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kt8, __builtin_bit_cast(bf16x8, concat4(dsb[t][0], dsb[t][1])), acc[t][nb], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  if (!head_live) {
+    // a trailing slot of a partial group: its share of the weight gradient is zero
+    if (P.q_norm != nullptr && r == 0) {
+      float* part = P.dwq_part + ((size_t)blockIdx.x * 4 + wave) * kHeadDim;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<float4*>(part + 16 * nb + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+
+  // epilogue: dq^ = c acc, then the prologue backward; lane (r, g) of tile t holds query 16t+r,
+  // dims 16 nb + 4 g + i
+  float dwq[8][4];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dwq[nb][i] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = qi[t];
+    const bool live = i < S;
+    f32x4 grad[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) grad[nb] = acc[t][nb] * kSoftmaxScale;
+    float x[8][4];
+    float4 wv[8];
+    load_acc_layout(P.q + (qrow0 + (live ? i : 0)) * kHeadDim, P.q_norm, g, x, wv, live);
+    float4 c[4], sn[4];
+    load_cos_sin_acc(P.rope, live ? qpos[t] : 0, g, c, sn);
+    float dx[8][4];
+    float dwt[8][4];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dwt[nb][e] = 0.0f;
+    prologue_backward(grad, x, wv, P.q_norm != nullptr, P.eps, c, sn, dx, dwt);
+    if (live) {
+      float* dst = P.dq + (qrow0 + i) * kHeadDim;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        float4 o = make_float4(dx[nb][0], dx[nb][1], dx[nb][2], dx[nb][3]);
+        if (bad) o = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+        *reinterpret_cast<float4*>(dst + 16 * nb + 4 * g) = o;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dwq[nb][e] += dwt[nb][e];
+    }
+  }
+  if (P.q_norm != nullptr) {
+    sum16(dwq);
+    if (r == 0) {
+      float* part = P.dwq_part + ((size_t)blockIdx.x * 4 + wave) * kHeadDim;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        *reinterpret_cast<float4*>(part + 16 * nb + 4 * g) = make_float4(dwq[nb][0], dwq[nb][1], dwq[nb][2], dwq[nb][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 3. dk, dv
+// ---------------------------------------------------------------------------------------
+struct DkdvWave {
+  uint16_t q[kQB][kRowB];
+  uint16_t d[kQB][kRowB];
+  float lse2[kQB];
+  float dvec[kQB];
+  int qpos[kQB];
+};
+struct DkdvSmem {
+  union {
+    DkdvWave w[4];
+    float part[4][2][8][64][4];  // per wavefront: dK^T, dV^T in register order
+  } u;
+};
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P) {
+  __shared__ DkdvSmem sm;
+  const int G = P.group;
+  const int Hkv = P.num_kv_heads;
+  const int S = P.seq;
+  const int nkb = (S + kKB - 1) / kKB;
+  const int kblk = blockIdx.x % nkb;
+  const int unit = blockIdx.x / nkb;
+  const int b = unit / Hkv;
+  const int hk = unit % Hkv;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const size_t krow0 = ((size_t)b * Hkv + hk) * S;
+  DkdvWave& ws = sm.u.w[wave];
+
+  // this lane's key (column r of the score tiles) and the key block's operands
+  const int j = kblk * kKB + r;
+  const bool klive = j < S;
+  bool bad = false;
+  const int kpos = klive ? safe_pos(P, b, j, bad) : INT32_MAX;
+  int kmin = kpos;
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) kmin = min(kmin, __shfl_xor(kmin, sh));
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  bf16x8 kop[4], vop[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const size_t off = (krow0 + (klive ? j : 0)) * kHeadDim + 32 * kb + 8 * g;
+    kop[kb] = __builtin_bit_cast(bf16x8, klive ? ldg16(P.kh + off) : make_uint4(0, 0, 0, 0));
+    vop[kb] = __builtin_bit_cast(bf16x8, klive ? ldg16(P.v + off) : make_uint4(0, 0, 0, 0));
+  }
+  f32x4 dk[8], dvv[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) { dk[nb] = f32x4{0.f, 0.f, 0.f, 0.f}; dvv[nb] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  const int jr = 4 * g + (r >> 2);
+  const int jc = 4 * (r & 3);
+  const int nqt = (S + kQB - 1) / kQB;
+
+  for (int gi = wave; gi < G; gi += 4) {
+    const int h = hk * G + gi;
+    const size_t qrow0 = ((size_t)b * P.num_q_heads + h) * S;
+    for (int qt = 0; qt < nqt; ++qt) {
+      // stage this head's 32 queries (q^, dout, lse, Dv, positions) in the wavefront's LDS
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int row = (u * 64 + lane) >> 4;  // 0..31
+        const int cc = lane & 15;
+        const int i = qt * kQB + row;
+        const bool live = i < S;
+        const size_t off = (qrow0 + (live ? i : 0)) * kHeadDim + cc * 8;
+        *reinterpret_cast<uint4*>(&ws.q[row][cc * 8]) = live ? ldg16(P.qh + off) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&ws.d[row][cc * 8]) = live ? ldg16(P.dout + off) : make_uint4(0, 0, 0, 0);
+      }
+      if (lane < kQB) {
+        const int i = qt * kQB + lane;
+        const bool live = i < S;
+        bool qb_ = false;
+        ws.lse2[lane] = live ? P.lse[qrow0 + i] * kLog2e : 0.0f;
+        ws.dvec[lane] = live ? P.dvec[qrow0 + i] : 0.0f;
+        ws.qpos[lane] = live ? safe_pos(P, b, i, qb_) : -1;
+      }
+      wave_lds_sync();
+      int qmax = ws.qpos[lane & 31];
+#pragma unroll
+      for (int sh = 1; sh < 32; sh <<= 1) qmax = max(qmax, __shfl_xor(qmax, sh));
+      qmax = __builtin_amdgcn_readfirstlane(qmax);
+      if (qmax >= kmin) {
+        // S = Q^ K^T: [t] queries 16 t + 4 g + i, key r
+        f32x4 s[2], dp[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&ws.q[16 * t + r][32 * kb + 8 * g]));
+            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&ws.d[16 * t + r][32 * kb + 8 * g]));
+            s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kop[kb], s[t], 0, 0, 0);
+            dp[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vop[kb], dp[t], 0, 0, 0);
+          }
+        }
+        i16x4 pb[2], dsb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float p4[4], d4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int qq = 16 * t + 4 * g + i;
+            const float p = kpos <= ws.qpos[qq] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], kScoreScaleLog2, -ws.lse2[qq])) : 0.0f;
+            p4[i] = p;
+            d4[i] = p * (dp[t][i] - ws.dvec[qq]);
+          }
+          pb[t] = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
+          dsb[t] = pack4_bf16(d4[0], d4[1], d4[2], d4[3]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries: k-slot 8g+e holds query
+        // 4g+e (e < 4) and 16+4g+(e-4) (e >= 4) in both operands
+        const bf16x8 pk = __builtin_bit_cast(bf16x8, concat4(pb[0], pb[1]));
+        const bf16x8 dk8 = __builtin_bit_cast(bf16x8, concat4(dsb[0], dsb[1]));
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.d[jr][16 * nb + jc]));
+          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.d[16 + jr][16 * nb + jc]));
+          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.q[jr][16 * nb + jc]));
+          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.q[16 + jr][16 * nb + jc]));
+          dvv[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, concat4(d0, d1)), pk, dvv[nb], 0, 0, 0);
+          dk[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, concat4(q0, q1)), dk8, dk[nb], 0, 0, 0);
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+  // the four wavefronts' sums, added in wavefront order
+  __syncthreads();
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    *reinterpret_cast<f32x4*>(&sm.u.part[wave][0][nb][lane][0]) = dk[nb];
+    *reinterpret_cast<f32x4*>(&sm.u.part[wave][1][nb][lane][0]) = dvv[nb];
+  }
+  __syncthreads();
+  if (wave >= 2) return;
+  f32x4 tot[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    tot[nb] = *reinterpret_cast<const f32x4*>(&sm.u.part[0][wave][nb][lane][0]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) tot[nb] = tot[nb] + *reinterpret_cast<const f32x4*>(&sm.u.part[w][wave][nb][lane][0]);
+  }
+  if (wave == 1) {  // dv
+    if (klive) {
+      float* dst = P.dv + (krow0 + j) * kHeadDim;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        *reinterpret_cast<float4*>(dst + 16 * nb + 4 * g) = make_float4(tot[nb][0], tot[nb][1], tot[nb][2], tot[nb][3]);
+    }
+    return;
+  }
+  // wave 0: dk through the prologue backward
+  f32x4 grad[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) grad[nb] = tot[nb] * kSoftmaxScale;
+  float x[8][4];
+  float4 wv[8];
+  load_acc_layout(P.k + (krow0 + (klive ? j : 0)) * kHeadDim, P.k_norm, g, x, wv, klive);
+  float4 c[4], sn[4];
+  load_cos_sin_acc(P.rope, klive ? kpos : 0, g, c, sn);
+  float dx[8][4], dwt[8][4];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dwt[nb][e] = 0.0f;
+  prologue_backward(grad, x, wv, P.k_norm != nullptr, P.eps, c, sn, dx, dwt);
+  if (klive) {
+    float* dst = P.dk + (krow0 + j) * kHeadDim;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      float4 o = make_float4(dx[nb][0], dx[nb][1], dx[nb][2], dx[nb][3]);
+      if (bad) o = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+      *reinterpret_cast<float4*>(dst + 16 * nb + 4 * g) = o;
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dwt[nb][e] = 0.0f;
+  }
+  if (P.k_norm != nullptr) {
+    sum16(dwt);
+    if (r == 0) {
+      float* part = P.dwk_part + (size_t)blockIdx.x * kHeadDim;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        *reinterpret_cast<float4*>(part + 16 * nb + 4 * g) = make_float4(dwt[nb][0], dwt[nb][1], dwt[nb][2], dwt[nb][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 4. weight gradients: shares summed in order (thread d sums dimension d)
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kHeadDim) void bwd_dw_kernel(const BwdParams P) {
+  const int d = threadIdx.x;
+  if (blockIdx.x == 0 && P.dq_norm != nullptr) {
+    float s = 0.0f;
+    for (int i = 0; i < P.dq_wgs * 4; ++i) s += P.dwq_part[(size_t)i * kHeadDim + d];
+    P.dq_norm[d] = s;
+  }
+  if (blockIdx.x == 1 && P.dk_norm != nullptr) {
+    float s = 0.0f;
+    for (int i = 0; i < P.dkdv_wgs; ++i) s += P.dwk_part[(size_t)i * kHeadDim + d];
+    P.dk_norm[d] = s;
+  }
+}
+
+int dq_workgroups(int batch, int seq, int hkv, int group) {
+  return ((seq + kQB - 1) / kQB) * batch * hkv * ((group + 3) / 4);
+}
+int dkdv_workgroups(int batch, int seq, int hkv) { return ((seq + kKB - 1) / kKB) * batch * hkv; }
+
+}  // namespace
+
+size_t backward_workspace_bytes(int batch, int seq, int hq, int hkv) {
+  const size_t tok_q = (size_t)batch * hq * seq, tok_k = (size_t)batch * hkv * seq;
+  const int G = hq / hkv;
+  return align256(tok_q * kHeadDim * 2) + align256(tok_k * kHeadDim * 2) + align256(tok_q * 4) +
+         align256((size_t)dq_workgroups(batch, seq, hkv, G) * 4 * kHeadDim * 4) +
+         align256((size_t)dkdv_workgroups(batch, seq, hkv) * kHeadDim * 4);
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.batch = a.batch;
+  p.seq = a.seq;
+  p.num_q_heads = a.num_q_heads;
+  p.num_kv_heads = a.num_kv_heads;
+  p.group = a.num_q_heads / a.num_kv_heads;
+  p.table_rows = a.table_rows;
+  p.pos = a.positions;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.out = (const uint16_t*)a.out;
+  p.dout = (const uint16_t*)a.dout;
+  p.lse = a.lse;
+  p.q_norm = a.q_norm;
+  p.k_norm = a.k_norm;
+  p.rope = a.rope;
+  p.eps = a.eps;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.dq_norm = a.q_norm ? a.dq_norm : nullptr;
+  p.dk_norm = a.k_norm ? a.dk_norm : nullptr;
+  p.dq_wgs = dq_workgroups(a.batch, a.seq, a.num_kv_heads, p.group);
+  p.dkdv_wgs = dkdv_workgroups(a.batch, a.seq, a.num_kv_heads);
+  char* ws = (char*)a.workspace;
+  const size_t tok_q = (size_t)a.batch * a.num_q_heads * a.seq, tok_k = (size_t)a.batch * a.num_kv_heads * a.seq;
+  p.qh = (uint16_t*)ws; ws += align256(tok_q * kHeadDim * 2);
+  p.kh = (uint16_t*)ws; ws += align256(tok_k * kHeadDim * 2);
+  p.dvec = (float*)ws; ws += align256(tok_q * 4);
+  p.dwq_part = (float*)ws; ws += align256((size_t)p.dq_wgs * 4 * kHeadDim * 4);
+  p.dwk_part = (float*)ws;
+  const long long tasks = (long long)(tok_q + tok_k + 15) / 16;
+  const unsigned prep_blocks = (unsigned)std::min<long long>((tasks + 3) / 4 + 1, 8192);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(prep_blocks), dim3(kBwdThreads), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.dq_wgs), dim3(kBwdThreads), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.dkdv_wgs), dim3(kBwdThreads), 0, stream, p);
+  if (p.dq_norm || p.dk_norm) hipLaunchKernelGGL(bwd_dw_kernel, dim3(2), dim3(kHeadDim), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

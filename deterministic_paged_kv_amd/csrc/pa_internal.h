@@ -310,4 +310,19 @@ inline size_t prefill_workspace_bytes(int hq, int hkv, int batch, int q_len, int
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
+// Backward of full-prefill attention (dense training layout).
+struct BackwardArgs {
+  int32_t batch, seq, num_q_heads, num_kv_heads, table_rows;
+  const int32_t* positions;
+  const void *q, *k, *v, *out, *dout;
+  const float* lse;
+  const float *q_norm, *k_norm;
+  const float* rope;
+  float eps;
+  float *dq, *dk, *dv, *dq_norm, *dk_norm;
+  void* workspace;
+};
+size_t backward_workspace_bytes(int batch, int seq, int hq, int hkv);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+
 }  // namespace pa

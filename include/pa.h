@@ -218,6 +218,39 @@ pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_p
                      void* out, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Workspace bytes of pa_prefill_backward for these sizes (host arithmetic only). */
+pa_status pa_prefill_backward_workspace_size(pa_plan_t plan, int32_t batch, int32_t seq_len, size_t* bytes);
+
+/* Deterministic backward of full-prefill attention, the training layout ([PR279] "Scope":
+ * the strict path requires a deterministic backward, dropout 0; [PR7] "Goal", "Original PR7
+ * Requirements": the training forward is full prefill, dq/dk/dv belong to its backward).
+ * The forward it differentiates is pa_prefill's arithmetic on dense inputs: row b's keys are
+ * its own seq_len tokens, token i has its query and its key at positions[b][i], key j is
+ * visible to query i iff positions[b][j] <= positions[b][i].  The BF16 roundings of q^, k^
+ * (the post-RoPE boundary) and of out pass gradients through unchanged.
+ *   positions          int32 [B, S]        in [0, table_rows); a token out of range gets NaN
+ *                                          gradients.
+ *   q                  bf16 [B, Hq, S, 128]   pre-norm, pre-RoPE.
+ *   k, v               bf16 [B, Hkv, S, 128]  k pre-norm, pre-RoPE.
+ *   q_norm_weight, k_norm_weight  fp32 [128] or NULL (no RMSNorm on that side).
+ *   out, lse           the forward's results: bf16 [B, Hq, S, 128], fp32 [B, Hq, S].
+ *   dout               bf16 [B, Hq, S, 128]   gradient of out.
+ *   dq                 fp32 [B, Hq, S, 128]   written.
+ *   dk, dv             fp32 [B, Hkv, S, 128]  written.
+ *   dq_norm_weight, dk_norm_weight  fp32 [128], written when the matching norm weight is
+ *                      given (required then), else ignored.
+ *   workspace          at least pa_prefill_backward_workspace_size() bytes, any contents.
+ * Every sum runs in a fixed order with no atomics: dk and dv of a key sum over the group's
+ * query heads in ascending order and over query tiles in ascending order, dq over key tiles in
+ * ascending order, the weight gradients over fixed shares in a fixed order; results are
+ * bitwise repeatable.  Four kernels on `stream`, no allocation, no synchronisation.  Requires
+ * a PA_SPLIT_DISABLED plan with batch <= max_batch and seq_len <= max_q_len. */
+pa_status pa_prefill_backward(pa_plan_t plan, int32_t batch, int32_t seq_len, const int32_t* positions,
+                              const void* q, const void* k, const void* v, const float* q_norm_weight,
+                              const float* k_norm_weight, const void* out, const float* lse, const void* dout,
+                              float* dq, float* dk, float* dv, float* dq_norm_weight, float* dk_norm_weight,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Build the CSR block table on the device from a dense one ([PR162] "Design notes": CSR
  * metadata built once per traversal, fixed-shape and device-only; "Code audit", "Data
  * flows checked": indptr = running sum of ceil(len / 16), compact indices by a fixed-shape

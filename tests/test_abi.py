@@ -129,3 +129,12 @@ def test_width_bucket_is_the_next_power_of_two(lib):
     assert lib.pa_width_bucket(0, ctypes.byref(out)) == -1
     assert lib.pa_width_bucket((1 << 30) + 1, ctypes.byref(out)) == -1
     assert lib.pa_width_bucket(8, None) == -1
+
+
+def test_backward_without_a_plan_fails_closed(lib):
+    """pa_prefill_backward and its workspace query check the plan before anything else."""
+    p = ctypes.c_void_p(16)  # never dereferenced: both calls fail the plan check
+    assert lib.pa_prefill_backward(None, 1, 1, p, p, p, p, None, None, p, p, p, p, p, p, None, None,
+                                   p, 1 << 20, None) == -1
+    n = ctypes.c_size_t()
+    assert lib.pa_prefill_backward_workspace_size(None, 1, 1, ctypes.byref(n)) == -1
