@@ -16,7 +16,10 @@ served from cache and are not counted).  The roofline entry divides the same byt
 decode kernel's average duration, measured with HIP events recorded on the launch stream.
 The chunked-prefill workload (B=4 x 512-query chunks after prefixes 0/1024/2048/3584,
 Hq=32, Hkv=8) is reported alongside with its algorithmic FLOPs (QK^T and PV over the
-causally visible pairs) per call.  The CPU oracle is timed on a bounded sample on the host.
+causally visible pairs) per call.  The full-prefill backward
+(B=4 rows of 2,048 tokens, Hq=32, Hkv=8, Q/K RMSNorm + RoPE) is reported with its algorithmic
+FLOPs (five products over the causal pairs).  The CPU oracle is timed on a bounded sample on
+the host.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
        python bench.py --profile-copy     # plain copy of a known size, for counter scaling
@@ -175,6 +178,58 @@ def time_calls(fn, sets, steps, warmup):
     return wall_ms, launch_ms
 
 
+def backward_flops(batch, seq, num_q_heads) -> int:
+    """Five products over the causally visible pairs of every query head (S = QK^T recomputed,
+    dP = dO V^T, dV += P^T dO, dQ = dS K, dK += dS^T Q): 10 * D * Hq * pairs."""
+    return 10 * 128 * num_q_heads * batch * (seq * (seq + 1) // 2)
+
+
+def bench_backward(device, steps, warmup, batch=4, seq=2048, hq=32, hkv=8):
+    """Full-prefill backward (training layout): B rows of S tokens at positions 0..S-1, Q/K
+    RMSNorm + RoPE, GQA 32/8, bf16 N(0,1) inputs drawn on the device.  The forward's out and lse
+    come from one pa_prefill call over the same tokens laid out in pages."""
+    import torch
+
+    import deterministic_paged_kv_amd as pa
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(9100)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    q, k, v, dout = rnd(batch, hq, seq, 128), rnd(batch, hkv, seq, 128), rnd(batch, hkv, seq, 128), rnd(batch, hq, seq, 128)
+    wq = torch.rand(128, generator=gen, device=device) + 0.5
+    wk = torch.rand(128, generator=gen, device=device) + 0.5
+    npg = seq // 16
+    pages = lambda x: x.permute(0, 2, 1, 3).reshape(batch * npg, 16, hkv, 128).contiguous()
+    i32 = lambda x: x.to(device=device, dtype=torch.int32)
+    indptr = i32(torch.arange(batch + 1) * npg)
+    indices = i32(torch.arange(batch * npg))
+    last = i32(torch.full((batch,), 16))
+    pos = i32(torch.arange(seq).repeat(batch, 1)).contiguous()
+    plan = pa.Plan(hq, hkv, max_batch=batch, max_q_len=seq, max_pages_per_row=npg, rms_eps=1e-6)
+    out, lse = pa.prefill(plan, q, pages(k), pages(v), indptr, indices, last, pos, wq, wk)
+    ws = torch.empty(pa.prefill_backward_workspace_size(plan, batch, seq), dtype=torch.uint8, device=device)
+    grads = (torch.empty(q.shape, dtype=torch.float32, device=device),
+             torch.empty(k.shape, dtype=torch.float32, device=device),
+             torch.empty(k.shape, dtype=torch.float32, device=device),
+             torch.empty(128, dtype=torch.float32, device=device), torch.empty(128, dtype=torch.float32, device=device))
+
+    def bstep(_):
+        pa.prefill_backward(plan, pos, q, k, v, out, lse, dout, q_norm_weight=wq, k_norm_weight=wk, workspace=ws,
+                            grads=grads)
+
+    b_wall, b_launch = time_calls(bstep, [None], steps, warmup)
+    flops = backward_flops(batch, seq, hq)
+    return {"workload": "full_prefill_backward", "batch": batch, "seq_len": seq, "num_q_heads": hq,
+            "num_kv_heads": hkv, "steps": steps, "ms_per_call": round(b_wall, 5),
+            "value": round(flops / (b_wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(flops / (b_launch * 1e-3) / 1e12, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (b_launch * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel + bwd_sum_rows_kernel (whole call)",
+                         "algorithmic_flops_per_call": flops, "avg_call_ms": round(b_launch, 5)}}
+
+
 def host_cores() -> int:
     """Cores this process may run on (the CPU share of the machine), capped at 16."""
     try:
@@ -290,6 +345,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="skip prefill and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the chunked prefill")
+    ap.add_argument("--backward-only", action="store_true", help="time only the full-prefill backward")
     ap.add_argument("--ingest-counters", nargs=4, metavar="CSV")
     args = ap.parse_args()
     if args.ingest_counters:
@@ -313,6 +369,9 @@ def main():
 
     device = "cuda:0"
     torch.cuda.set_device(0)
+    if args.backward_only:
+        print(json.dumps({"prefill_backward": bench_backward(device, max(10, args.steps // 10), 3)}), flush=True)
+        return
     print("[bench] building inputs", file=sys.stderr, flush=True)
     base = workloads.qwen3_8b_decode(canary=False)
     sets = [device_rotation(base, i, device) for i in range(ROTATIONS)]
@@ -422,6 +481,8 @@ def main():
                          "traffic": None, "kernel": "prologue_kernel + attend_kernel (whole call)",
                          "algorithmic_flops_per_call": flops, "avg_call_ms": round(p_launch, 5)},
         }
+        print("[bench] timing the full-prefill backward", file=sys.stderr, flush=True)
+        result["prefill_backward"] = bench_backward(device, max(10, args.steps // 10), 3)
         if not args.no_cpu_baseline:
             print("[bench] timing the CPU oracle (decode, then prefill)", file=sys.stderr, flush=True)
             result["cpu_baseline"] = cpu_baseline_decode(base, alg)

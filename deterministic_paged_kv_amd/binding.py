@@ -318,12 +318,13 @@ def prefill_backward_workspace_size(plan: Plan, batch: int, seq_len: int) -> int
 
 
 def prefill_backward(plan: Plan, positions, q, k, v, out, lse, dout, q_norm_weight=None, k_norm_weight=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, grads=None):
     """pa_prefill_backward on dense training-layout tensors.
 
     positions int32 [B, S]; q, out, dout bf16 [B, Hq, S, 128]; k, v bf16 [B, Hkv, S, 128];
     lse fp32 [B, Hq, S].  Returns (dq, dk, dv, dq_norm_weight, dk_norm_weight) as fp32 tensors
-    (the weight gradients are None where that norm is absent)."""
+    (the weight gradients are None where that norm is absent).  ``grads``: optional tuple of
+    those five tensors to write into instead of allocating them."""
     import torch
 
     _need(q, "q", torch.bfloat16, 4)
@@ -341,11 +342,20 @@ def prefill_backward(plan: Plan, positions, q, k, v, out, lse, dout, q_norm_weig
         if w is not None:
             _need(w, name, torch.float32, shape=(HEAD_DIM,))
     dev = q.device
-    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    dk = torch.empty(kv_shape, dtype=torch.float32, device=dev)
-    dv = torch.empty(kv_shape, dtype=torch.float32, device=dev)
-    dwq = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if q_norm_weight is not None else None
-    dwk = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if k_norm_weight is not None else None
+    if grads is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(kv_shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(kv_shape, dtype=torch.float32, device=dev)
+        dwq = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if q_norm_weight is not None else None
+        dwk = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if k_norm_weight is not None else None
+    else:
+        dq, dk, dv, dwq, dwk = grads
+        _need(dq, "dq", torch.float32, shape=q.shape)
+        _need(dk, "dk", torch.float32, shape=kv_shape)
+        _need(dv, "dv", torch.float32, shape=kv_shape)
+        for name, g, w in (("dq_norm_weight", dwq, q_norm_weight), ("dk_norm_weight", dwk, k_norm_weight)):
+            if w is not None:
+                _need(g, name, torch.float32, shape=(HEAD_DIM,))
     if workspace is None:
         workspace = torch.empty(prefill_backward_workspace_size(plan, B, S), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1)

@@ -16,19 +16,22 @@
 //
 // Four kernels, every sum in a fixed order (no atomics):
 //  1. bwd_prep_kernel: q^ and k^ (the forward's prologue, bit for bit) into the workspace,
-//     and Dv = sum_d dout * out per query (FP32: a lane's 32 terms in order, then the four
-//     lanes of the query pairwise).
+//     Dv = sum_d dout * out per query (FP32: a lane's 32 terms in order, then the four lanes of
+//     the query pairwise), and the least and greatest position of every 16 tokens.
 //  2. bwd_dq_kernel: one workgroup per (32 queries, row, KV head, up to 4 query heads), as in
 //     the forward; per 32-key tile, staged in LDS for the 4 heads: S^T = K^ Q^T, P^T from the
 //     forward's LSE, dP^T = V dO^T, dS^T = P^T (dP^T - Dv), dQ^T += K^T dS^T (key tiles in
-//     ascending order).  The epilogue applies the transposed rotation and the RMSNorm
-//     backward, writes dq, and writes this wavefront's share of the q weight gradient.
-//  3. bwd_dkdv_kernel: one workgroup per (16 keys, row, KV head); wavefront w takes query heads
-//     w, w+4, ... of the group in ascending order, and their 32-query tiles in ascending
-//     order: S = Q^ K^T, P, dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.  The four
-//     wavefronts' sums are added in wavefront order; the epilogue writes dv, and dk through
-//     the prologue backward, and the workgroup's share of the k weight gradient.
-//  4. bwd_dw_kernel: the weight-gradient shares summed in workgroup order.
+//     ascending order; tiles whose keys all follow every query are not visited).  The
+//     epilogue applies the transposed rotation and the RMSNorm backward, writes dq, and writes
+//     this wavefront's share of the q weight gradient.
+//  3. bwd_dkdv_kernel: one workgroup per (64 keys, row, KV head), 16 keys per wavefront; the
+//     group's query heads in ascending order, each head's 32-query tiles in ascending order
+//     (staged in LDS once for the four wavefronts; tiles whose queries all precede every key
+//     are not visited): S = Q^ K^T, P, dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.  The
+//     epilogue writes dv, and dk through the prologue backward, and the wavefront's share of
+//     the k weight gradient.
+//  4. bwd_sum_rows_kernel: the weight-gradient shares summed by a fixed tree (64 rows per
+//     workgroup, levels until one row is left).
 // MFMA operands are BF16 (q^, k^, v, dout, and P and dS rounded to BF16), accumulation FP32.
 #include "pa_internal.h"
 
@@ -38,7 +41,6 @@ namespace {
 
 constexpr int kQB = 32;                 // queries per wavefront (dq kernel) / per tile (dkdv kernel)
 constexpr int kKTile = 32;              // keys per tile (dq kernel)
-constexpr int kKB = 16;                 // keys per workgroup (dkdv kernel)
 constexpr int kRowB = kHeadDim + 16;    // padded LDS row (conflict-free transposed reads)
 constexpr int kBwdThreads = 256;
 constexpr float kLog2e = 1.4426950408889634074f;
@@ -96,8 +98,10 @@ struct BwdParams {
   uint16_t* qh;   // [B, Hq, S, 128]
   uint16_t* kh;   // [B, Hkv, S, 128]
   float* dvec;    // [B, Hq, S]
+  int* tmin;       // [B, ceil(S / 16)]: least position of each 16 tokens (INT32_MAX past the row)
+  int* tmax;       // [B, ceil(S / 16)]: greatest position of each 16 tokens (-1 past the row)
   float* dwq_part;  // [dq workgroups][4][128]
-  float* dwk_part;  // [dkdv workgroups][128]
+  float* dwk_part;  // [dkdv workgroups][4][128]
   int32_t dq_wgs, dkdv_wgs;
 };
 
@@ -140,6 +144,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const BwdParams P
       raw[kb] = live ? ldg16(src + row + 32 * kb) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[kb * 8 + e] = wsrc ? wsrc[32 * kb + 8 * g + e] : 1.0f;
+    }
+    if (is_q && bh % H == 0) {
+      // the position bounds of these 16 tokens (the same for every head), for tile skipping
+      int lo = live ? pos : INT32_MAX, hi = live ? pos : -1;
+#pragma unroll
+      for (int sh = 1; sh < 16; sh <<= 1) {
+        lo = min(lo, __shfl_xor(lo, sh));
+        hi = max(hi, __shfl_xor(hi, sh));
+      }
+      if (lane == 0) {
+        P.tmin[(size_t)b * tiles + tile] = lo;
+        P.tmax[(size_t)b * tiles + tile] = hi;
+      }
     }
     float4 cs[8];
     load_cos_sin(P.rope, pos, g, cs);
@@ -348,68 +365,87 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
     }
     if (tid < kKTile) sm.kpos[buf][tid] = kp_next;
   };
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
-    // skip the tile when all its keys come after every query of the block
-    int kmin = sm.kpos[buf][lane & 31];
-#pragma unroll
-    for (int sh = 1; sh < 32; sh <<= 1) kmin = min(kmin, __shfl_xor(kmin, sh));
-    kmin = __builtin_amdgcn_readfirstlane(kmin);
-    if (head_live && kmin <= qmax) {
-      f32x4 s[2][2], dp[2][2];  // [ks][t]: keys 16 ks + 4 g + i, query 16 t + r
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 ka[4], va[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
-          va[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.v[buf][16 * ks + r][32 * kb + 8 * g]));
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          s[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            s[ks][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], s[ks][t], 0, 0, 0);
-            dp[ks][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kb], dop[t][kb], dp[ks][t], 0, 0, 0);
-          }
-        }
+  // the first key tile at or after kt holding a key at or before the block's last query
+  // position (tiles whose keys all come after every query contribute nothing)
+  const int n16 = (S + 15) / 16;
+  auto next_tile = [&](int kt) -> int {
+    for (; kt < ntiles; kt += 64) {
+      const int c = kt + lane;
+      int m = INT32_MAX;
+      if (c < ntiles) {
+        m = P.tmin[(size_t)b * n16 + 2 * c];
+        if (2 * c + 1 < n16) m = min(m, P.tmin[(size_t)b * n16 + 2 * c + 1]);
       }
-      // dS^T = P^T (dP^T - Dv), P^T = 2^(s c log2e - lse log2e) on visible keys, else 0
-      i16x4 dsb[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(m <= qmax);
+      if (hit != 0) return kt + (int)__builtin_ctzll(hit);
+    }
+    return ntiles;
+  };
+  const int first = __builtin_amdgcn_readfirstlane(next_tile(0));
+  if (first < ntiles) {
+    load_tile(first);
+    store_tile(0);
+    __syncthreads();
+    int buf = 0;
+    for (int kt = first;;) {
+      const int nk = __builtin_amdgcn_readfirstlane(next_tile(kt + 1));
+      const bool more = nk < ntiles;
+      if (more) load_tile(nk);
+      if (head_live) {
+        f32x4 s[2][2], dp[2][2];  // [ks][t]: keys 16 ks + 4 g + i, query 16 t + r
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          float d4[4];
+          bf16x8 ka[4], va[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kp = sm.kpos[buf][16 * ks + 4 * g + i];
-            const float p = kp <= qpos[t] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks][t][i], kScoreScaleLog2, -lse2[t])) : 0.0f;
-            d4[i] = p * (dp[ks][t][i] - dv_[t]);
+          for (int kb = 0; kb < 4; ++kb) {
+            ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
+            va[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.v[buf][16 * ks + r][32 * kb + 8 * g]));
           }
-          dsb[t][ks] = pack4_bf16(d4[0], d4[1], d4[2], d4[3]);
-        }
-      // dQ^T += K^T dS^T over the tile's 32 keys: k-slot 8g+e holds key 4g+e (e < 4) and key
-      // 16+4g+(e-4) (e >= 4) in both operands; K^T from two transposed reads per column block
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][jr][16 * nb + jc]));
-        const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][16 + jr][16 * nb + jc]));
-        const bf16x8 kt8 = __builtin_bit_cast(bf16x8, concat4(k0, k1));
+          for (int t = 0; t < 2; ++t) {
+            s[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              s[ks][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], s[ks][t], 0, 0, 0);
+              dp[ks][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kb], dop[t][kb], dp[ks][t], 0, 0, 0);
+            }
+          }
+        }
+        // dS^T = P^T (dP^T - Dv), P^T = 2^(s c log2e - lse log2e) on visible keys, else 0
+        i16x4 dsb[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              kt8, __builtin_bit_cast(bf16x8, concat4(dsb[t][0], dsb[t][1])), acc[t][nb], 0, 0, 0);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            float d4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kp = sm.kpos[buf][16 * ks + 4 * g + i];
+              const float p = kp <= qpos[t] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks][t][i], kScoreScaleLog2, -lse2[t])) : 0.0f;
+              d4[i] = p * (dp[ks][t][i] - dv_[t]);
+            }
+            dsb[t][ks] = pack4_bf16(d4[0], d4[1], d4[2], d4[3]);
+          }
+        // dQ^T += K^T dS^T over the tile's 32 keys: k-slot 8g+e holds key 4g+e (e < 4) and key
+        // 16+4g+(e-4) (e >= 4) in both operands; K^T from two transposed reads per column block
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][jr][16 * nb + jc]));
+          const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][16 + jr][16 * nb + jc]));
+          const bf16x8 kt8 = __builtin_bit_cast(bf16x8, concat4(k0, k1));
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                kt8, __builtin_bit_cast(bf16x8, concat4(dsb[t][0], dsb[t][1])), acc[t][nb], 0, 0, 0);
+        }
       }
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+      if (!more) break;
+      kt = nk;
+      buf ^= 1;
     }
-    if (kt + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
   }
   if (!head_live) {
     // a trailing slot of a partial group: its share of the weight gradient is zero
@@ -475,28 +511,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
 // ---------------------------------------------------------------------------------------
 // 3. dk, dv
 // ---------------------------------------------------------------------------------------
-struct DkdvWave {
+constexpr int kKBlock = 64;   // keys per workgroup, 16 per wavefront
+
+// one 32-query tile of one query head, shared by the workgroup's four wavefronts
+struct DkdvTile {
   uint16_t q[kQB][kRowB];
   uint16_t d[kQB][kRowB];
   float lse2[kQB];
   float dvec[kQB];
   int qpos[kQB];
 };
-struct DkdvSmem {
-  union {
-    DkdvWave w[4];
-    float part[4][2][8][64][4];  // per wavefront: dK^T, dV^T in register order
-  } u;
-};
 
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P) {
-  __shared__ DkdvSmem sm;
+  __shared__ DkdvTile sm[2];
   const int G = P.group;
   const int Hkv = P.num_kv_heads;
   const int S = P.seq;
-  const int nkb = (S + kKB - 1) / kKB;
-  const int kblk = blockIdx.x % nkb;
-  const int unit = blockIdx.x / nkb;
+  const int units = P.batch * Hkv;
+  const int kblk = (int)blockIdx.x / units;  // the first key blocks see the most queries: launched first
+  const int unit = (int)blockIdx.x % units;
   const int b = unit / Hkv;
   const int hk = unit % Hkv;
   const int tid = threadIdx.x;
@@ -505,10 +538,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
   const int r = lane & 15;
   const int g = lane >> 4;
   const size_t krow0 = ((size_t)b * Hkv + hk) * S;
-  DkdvWave& ws = sm.u.w[wave];
+  const int n16 = (S + 15) / 16;
+  const int nqt = (S + kQB - 1) / kQB;
 
-  // this lane's key (column r of the score tiles) and the key block's operands
-  const int j = kblk * kKB + r;
+  // this lane's key (column r of the wavefront's score tiles) and the wavefront's operands
+  const int j = kblk * kKBlock + 16 * wave + r;
   const bool klive = j < S;
   bool bad = false;
   const int kpos = klive ? safe_pos(P, b, j, bad) : INT32_MAX;
@@ -516,6 +550,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
 #pragma unroll
   for (int sh = 1; sh < 16; sh <<= 1) kmin = min(kmin, __shfl_xor(kmin, sh));
   kmin = __builtin_amdgcn_readfirstlane(kmin);
+  // the block's least key position, from the bounds of its four 16-token groups
+  int bmin = INT32_MAX;
+  {
+    const int t16 = kblk * 4 + (lane & 3);
+    if (t16 < n16) bmin = P.tmin[(size_t)b * n16 + t16];
+    bmin = min(bmin, __shfl_xor(bmin, 1));
+    bmin = min(bmin, __shfl_xor(bmin, 2));
+    bmin = __builtin_amdgcn_readfirstlane(bmin);
+  }
   bf16x8 kop[4], vop[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -528,48 +571,95 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
   for (int nb = 0; nb < 8; ++nb) { dk[nb] = f32x4{0.f, 0.f, 0.f, 0.f}; dvv[nb] = f32x4{0.f, 0.f, 0.f, 0.f}; }
   const int jr = 4 * g + (r >> 2);
   const int jc = 4 * (r & 3);
-  const int nqt = (S + kQB - 1) / kQB;
 
-  for (int gi = wave; gi < G; gi += 4) {
-    const int h = hk * G + gi;
-    const size_t qrow0 = ((size_t)b * P.num_q_heads + h) * S;
-    for (int qt = 0; qt < nqt; ++qt) {
-      // stage this head's 32 queries (q^, dout, lse, Dv, positions) in the wavefront's LDS
+  // the first query tile at or after qt holding a query that some key of the block can see
+  // (tiles where every query precedes every key contribute nothing and are not visited)
+  auto next_tile = [&](int qt) -> int {
+    for (; qt < nqt; qt += 64) {
+      const int c = qt + lane;
+      int m = -1;
+      if (c < nqt) {
+        m = P.tmax[(size_t)b * n16 + 2 * c];
+        if (2 * c + 1 < n16) m = max(m, P.tmax[(size_t)b * n16 + 2 * c + 1]);
+      }
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(m >= bmin);
+      if (hit != 0) return qt + (int)__builtin_ctzll(hit);
+    }
+    return nqt;
+  };
+
+  // a tile's share of one thread: q^ and dout rows rt and rt + 16, and (threads < 32) one
+  // query's lse, Dv and position; loaded one tile ahead, written after the current tile is used
+  const int rt = tid >> 4;
+  const int col = tid & 15;
+  uint4 qr[2], dr[2];
+  float lse_n = 0.0f, dv_n = 0.0f;
+  int qp_n = -1;
+  auto load_tile = [&](int gi, int qt) {
+    const size_t qrow0 = ((size_t)b * P.num_q_heads + hk * G + gi) * S;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int row = (u * 64 + lane) >> 4;  // 0..31
-        const int cc = lane & 15;
-        const int i = qt * kQB + row;
-        const bool live = i < S;
-        const size_t off = (qrow0 + (live ? i : 0)) * kHeadDim + cc * 8;
-        *reinterpret_cast<uint4*>(&ws.q[row][cc * 8]) = live ? ldg16(P.qh + off) : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&ws.d[row][cc * 8]) = live ? ldg16(P.dout + off) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      const int i = qt * kQB + 16 * u + rt;
+      const bool live = i < S;
+      const size_t off = (qrow0 + (live ? i : 0)) * kHeadDim + col * 8;
+      qr[u] = live ? ldg16(P.qh + off) : make_uint4(0, 0, 0, 0);
+      dr[u] = live ? ldg16(P.dout + off) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kQB) {
+      const int i = qt * kQB + tid;
+      const bool live = i < S;
+      bool qb_ = false;
+      lse_n = live ? P.lse[qrow0 + i] * kLog2e : 0.0f;
+      dv_n = live ? P.dvec[qrow0 + i] : 0.0f;
+      qp_n = live ? safe_pos(P, b, i, qb_) : -1;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<uint4*>(&sm[buf].q[16 * u + rt][col * 8]) = qr[u];
+      *reinterpret_cast<uint4*>(&sm[buf].d[16 * u + rt][col * 8]) = dr[u];
+    }
+    if (tid < kQB) {
+      sm[buf].lse2[tid] = lse_n;
+      sm[buf].dvec[tid] = dv_n;
+      sm[buf].qpos[tid] = qp_n;
+    }
+  };
+
+  // query heads of the group in ascending order, each head's visited tiles in ascending order
+  const int first = __builtin_amdgcn_readfirstlane(next_tile(0));
+  if (first < nqt) {
+    int gi = 0, qt = first, buf = 0;
+    load_tile(gi, qt);
+    store_tile(0);
+    __syncthreads();
+    while (true) {
+      int ngi = gi;
+      int nq = __builtin_amdgcn_readfirstlane(next_tile(qt + 1));
+      if (nq >= nqt) {
+        ngi = gi + 1;
+        nq = first;
       }
-      if (lane < kQB) {
-        const int i = qt * kQB + lane;
-        const bool live = i < S;
-        bool qb_ = false;
-        ws.lse2[lane] = live ? P.lse[qrow0 + i] * kLog2e : 0.0f;
-        ws.dvec[lane] = live ? P.dvec[qrow0 + i] : 0.0f;
-        ws.qpos[lane] = live ? safe_pos(P, b, i, qb_) : -1;
-      }
-      wave_lds_sync();
-      int qmax = ws.qpos[lane & 31];
+      const bool more = ngi < G;
+      if (more) load_tile(ngi, nq);
+      const DkdvTile& T = sm[buf];
+      int qmax = T.qpos[lane & 31];
 #pragma unroll
       for (int sh = 1; sh < 32; sh <<= 1) qmax = max(qmax, __shfl_xor(qmax, sh));
       qmax = __builtin_amdgcn_readfirstlane(qmax);
       if (qmax >= kmin) {
-        // S = Q^ K^T: [t] queries 16 t + 4 g + i, key r
-        f32x4 s[2], dp[2];
+        // S = Q^ K^T and dP = dO V^T: [t] queries 16 t + 4 g + i, key r
+        f32x4 sc[2], dp[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&ws.q[16 * t + r][32 * kb + 8 * g]));
-            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&ws.d[16 * t + r][32 * kb + 8 * g]));
-            s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kop[kb], s[t], 0, 0, 0);
+            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.q[16 * t + r][32 * kb + 8 * g]));
+            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.d[16 * t + r][32 * kb + 8 * g]));
+            sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kop[kb], sc[t], 0, 0, 0);
             dp[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vop[kb], dp[t], 0, 0, 0);
           }
         }
@@ -580,9 +670,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int qq = 16 * t + 4 * g + i;
-            const float p = kpos <= ws.qpos[qq] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], kScoreScaleLog2, -ws.lse2[qq])) : 0.0f;
+            const float p = kpos <= T.qpos[qq] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][i], kScoreScaleLog2, -T.lse2[qq])) : 0.0f;
             p4[i] = p;
-            d4[i] = p * (dp[t][i] - ws.dvec[qq]);
+            d4[i] = p * (dp[t][i] - T.dvec[qq]);
           }
           pb[t] = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
           dsb[t] = pack4_bf16(d4[0], d4[1], d4[2], d4[3]);
@@ -593,46 +683,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
         const bf16x8 dk8 = __builtin_bit_cast(bf16x8, concat4(dsb[0], dsb[1]));
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.d[jr][16 * nb + jc]));
-          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.d[16 + jr][16 * nb + jc]));
-          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.q[jr][16 * nb + jc]));
-          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ws.q[16 + jr][16 * nb + jc]));
+          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[jr][16 * nb + jc]));
+          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[16 + jr][16 * nb + jc]));
+          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[jr][16 * nb + jc]));
+          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[16 + jr][16 * nb + jc]));
           dvv[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, concat4(d0, d1)), pk, dvv[nb], 0, 0, 0);
           dk[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, concat4(q0, q1)), dk8, dk[nb], 0, 0, 0);
         }
       }
-      wave_lds_sync();
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+      if (!more) break;
+      gi = ngi;
+      qt = nq;
+      buf ^= 1;
     }
   }
-  // the four wavefronts' sums, added in wavefront order
-  __syncthreads();
+
+  // epilogue: lane (r, g) holds key r of the wavefront, dims 16 nb + 4 g + i
+  if (klive) {
+    float* dst = P.dv + (krow0 + j) * kHeadDim;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    *reinterpret_cast<f32x4*>(&sm.u.part[wave][0][nb][lane][0]) = dk[nb];
-    *reinterpret_cast<f32x4*>(&sm.u.part[wave][1][nb][lane][0]) = dvv[nb];
+    for (int nb = 0; nb < 8; ++nb)
+      *reinterpret_cast<float4*>(dst + 16 * nb + 4 * g) = make_float4(dvv[nb][0], dvv[nb][1], dvv[nb][2], dvv[nb][3]);
   }
-  __syncthreads();
-  if (wave >= 2) return;
-  f32x4 tot[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    tot[nb] = *reinterpret_cast<const f32x4*>(&sm.u.part[0][wave][nb][lane][0]);
-#pragma unroll
-    for (int w = 1; w < 4; ++w) tot[nb] = tot[nb] + *reinterpret_cast<const f32x4*>(&sm.u.part[w][wave][nb][lane][0]);
-  }
-  if (wave == 1) {  // dv
-    if (klive) {
-      float* dst = P.dv + (krow0 + j) * kHeadDim;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        *reinterpret_cast<float4*>(dst + 16 * nb + 4 * g) = make_float4(tot[nb][0], tot[nb][1], tot[nb][2], tot[nb][3]);
-    }
-    return;
-  }
-  // wave 0: dk through the prologue backward
+  // dk through the prologue backward
   f32x4 grad[8];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) grad[nb] = tot[nb] * kSoftmaxScale;
+  for (int nb = 0; nb < 8; ++nb) grad[nb] = dk[nb] * kSoftmaxScale;
   float x[8][4];
   float4 wv[8];
   load_acc_layout(P.k + (krow0 + (klive ? j : 0)) * kHeadDim, P.k_norm, g, x, wv, klive);
@@ -661,7 +739,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
   if (P.k_norm != nullptr) {
     sum16(dwt);
     if (r == 0) {
-      float* part = P.dwk_part + (size_t)blockIdx.x * kHeadDim;
+      float* part = P.dwk_part + ((size_t)blockIdx.x * 4 + wave) * kHeadDim;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
         *reinterpret_cast<float4*>(part + 16 * nb + 4 * g) = make_float4(dwt[nb][0], dwt[nb][1], dwt[nb][2], dwt[nb][3]);
@@ -670,35 +748,85 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
 }
 
 // ---------------------------------------------------------------------------------------
-// 4. weight gradients: shares summed in order (thread d sums dimension d)
+// 4. weight gradients: a fixed tree over the shares.  Each workgroup sums 64 consecutive rows
+// of in[rows][128]: four groups of 128 threads take 16 rows each in ascending order, and the
+// group sums are added in group order; levels repeat until one row is left.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadDim) void bwd_dw_kernel(const BwdParams P) {
-  const int d = threadIdx.x;
-  if (blockIdx.x == 0 && P.dq_norm != nullptr) {
-    float s = 0.0f;
-    for (int i = 0; i < P.dq_wgs * 4; ++i) s += P.dwq_part[(size_t)i * kHeadDim + d];
-    P.dq_norm[d] = s;
+constexpr int kSumRows = 64;
+__global__ __launch_bounds__(512) void bwd_sum_rows_kernel(const float* in, int rows, float* out) {
+  __shared__ float part[4][kHeadDim];
+  const int d = threadIdx.x & (kHeadDim - 1);
+  const int grp = threadIdx.x >> 7;
+  const int r0 = blockIdx.x * kSumRows + grp * 16;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = r0 + i < rows ? in[(size_t)(r0 + i) * kHeadDim + d] : 0.0f;
+  float s = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) s += v[i];
+  part[grp][d] = s;
+  __syncthreads();
+  if (grp == 0) out[(size_t)blockIdx.x * kHeadDim + d] = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+}
+
+// floats of the intermediate levels of the tree over `rows` rows
+size_t sum_scratch_floats(long long rows) {
+  size_t n = 0;
+  while (rows > 1) {
+    rows = (rows + kSumRows - 1) / kSumRows;
+    if (rows > 1) n += (size_t)rows * kHeadDim;
   }
-  if (blockIdx.x == 1 && P.dk_norm != nullptr) {
-    float s = 0.0f;
-    for (int i = 0; i < P.dkdv_wgs; ++i) s += P.dwk_part[(size_t)i * kHeadDim + d];
-    P.dk_norm[d] = s;
+  return n;
+}
+
+void launch_sum_rows(const float* in, long long rows, float* scratch, float* out, hipStream_t stream) {
+  while (true) {
+    const long long chunks = (rows + kSumRows - 1) / kSumRows;
+    float* dst = chunks == 1 ? out : scratch;
+    hipLaunchKernelGGL(bwd_sum_rows_kernel, dim3((unsigned)chunks), dim3(512), 0, stream, in, (int)rows, dst);
+    if (chunks == 1) return;
+    in = dst;
+    scratch += (size_t)chunks * kHeadDim;
+    rows = chunks;
   }
 }
 
 int dq_workgroups(int batch, int seq, int hkv, int group) {
   return ((seq + kQB - 1) / kQB) * batch * hkv * ((group + 3) / 4);
 }
-int dkdv_workgroups(int batch, int seq, int hkv) { return ((seq + kKB - 1) / kKB) * batch * hkv; }
+int dkdv_workgroups(int batch, int seq, int hkv) { return ((seq + kKBlock - 1) / kKBlock) * batch * hkv; }
+
+// The workspace, in order: q^, k^ (bf16), Dv, the 16-token position bounds, the weight-gradient
+// shares of the dq and dkdv workgroups (4 rows of 128 each), and the levels of their sums.
+struct BwdLayout {
+  size_t qh, kh, dvec, tmin, tmax, dwq_part, dwk_part, dwq_sum, dwk_sum, total;
+  long long dwq_rows, dwk_rows;
+};
+
+BwdLayout backward_layout(int batch, int seq, int hq, int hkv) {
+  BwdLayout L;
+  const size_t tok_q = (size_t)batch * hq * seq, tok_k = (size_t)batch * hkv * seq;
+  const size_t n16 = (size_t)batch * ((seq + 15) / 16);
+  L.dwq_rows = (long long)dq_workgroups(batch, seq, hkv, hq / hkv) * 4;
+  L.dwk_rows = (long long)dkdv_workgroups(batch, seq, hkv) * 4;
+  size_t o = 0;
+  L.qh = o;       o += align256(tok_q * kHeadDim * 2);
+  L.kh = o;       o += align256(tok_k * kHeadDim * 2);
+  L.dvec = o;     o += align256(tok_q * 4);
+  L.tmin = o;     o += align256(n16 * 4);
+  L.tmax = o;     o += align256(n16 * 4);
+  L.dwq_part = o; o += align256((size_t)L.dwq_rows * kHeadDim * 4);
+  L.dwk_part = o; o += align256((size_t)L.dwk_rows * kHeadDim * 4);
+  L.dwq_sum = o;  o += align256(sum_scratch_floats(L.dwq_rows) * 4);
+  L.dwk_sum = o;  o += align256(sum_scratch_floats(L.dwk_rows) * 4);
+  L.total = o;
+  return L;
+}
 
 }  // namespace
 
 size_t backward_workspace_bytes(int batch, int seq, int hq, int hkv) {
-  const size_t tok_q = (size_t)batch * hq * seq, tok_k = (size_t)batch * hkv * seq;
-  const int G = hq / hkv;
-  return align256(tok_q * kHeadDim * 2) + align256(tok_k * kHeadDim * 2) + align256(tok_q * 4) +
-         align256((size_t)dq_workgroups(batch, seq, hkv, G) * 4 * kHeadDim * 4) +
-         align256((size_t)dkdv_workgroups(batch, seq, hkv) * kHeadDim * 4);
+  return backward_layout(batch, seq, hq, hkv).total;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
@@ -727,19 +855,22 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   p.dk_norm = a.k_norm ? a.dk_norm : nullptr;
   p.dq_wgs = dq_workgroups(a.batch, a.seq, a.num_kv_heads, p.group);
   p.dkdv_wgs = dkdv_workgroups(a.batch, a.seq, a.num_kv_heads);
+  const BwdLayout L = backward_layout(a.batch, a.seq, a.num_q_heads, a.num_kv_heads);
   char* ws = (char*)a.workspace;
-  const size_t tok_q = (size_t)a.batch * a.num_q_heads * a.seq, tok_k = (size_t)a.batch * a.num_kv_heads * a.seq;
-  p.qh = (uint16_t*)ws; ws += align256(tok_q * kHeadDim * 2);
-  p.kh = (uint16_t*)ws; ws += align256(tok_k * kHeadDim * 2);
-  p.dvec = (float*)ws; ws += align256(tok_q * 4);
-  p.dwq_part = (float*)ws; ws += align256((size_t)p.dq_wgs * 4 * kHeadDim * 4);
-  p.dwk_part = (float*)ws;
-  const long long tasks = (long long)(tok_q + tok_k + 15) / 16;
-  const unsigned prep_blocks = (unsigned)std::min<long long>((tasks + 3) / 4 + 1, 8192);
+  p.qh = (uint16_t*)(ws + L.qh);
+  p.kh = (uint16_t*)(ws + L.kh);
+  p.dvec = (float*)(ws + L.dvec);
+  p.tmin = (int*)(ws + L.tmin);
+  p.tmax = (int*)(ws + L.tmax);
+  p.dwq_part = (float*)(ws + L.dwq_part);
+  p.dwk_part = (float*)(ws + L.dwk_part);
+  const long long tasks = (long long)a.batch * (a.num_q_heads + a.num_kv_heads) * ((a.seq + 15) / 16);
+  const unsigned prep_blocks = (unsigned)std::min<long long>((tasks + 3) / 4, 8192);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(prep_blocks), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.dq_wgs), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.dkdv_wgs), dim3(kBwdThreads), 0, stream, p);
-  if (p.dq_norm || p.dk_norm) hipLaunchKernelGGL(bwd_dw_kernel, dim3(2), dim3(kHeadDim), 0, stream, p);
+  if (p.dq_norm) launch_sum_rows(p.dwq_part, L.dwq_rows, (float*)(ws + L.dwq_sum), p.dq_norm, stream);
+  if (p.dk_norm) launch_sum_rows(p.dwk_part, L.dwk_rows, (float*)(ws + L.dwk_sum), p.dk_norm, stream);
   return hipGetLastError();
 }
 

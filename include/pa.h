@@ -243,7 +243,8 @@ pa_status pa_prefill_backward_workspace_size(pa_plan_t plan, int32_t batch, int3
  * Every sum runs in a fixed order with no atomics: dk and dv of a key sum over the group's
  * query heads in ascending order and over query tiles in ascending order, dq over key tiles in
  * ascending order, the weight gradients over fixed shares in a fixed order; results are
- * bitwise repeatable.  Four kernels on `stream`, no allocation, no synchronisation.  Requires
+ * bitwise repeatable.  Kernels on `stream` only (three, then a few small ones that sum the
+ * weight gradients), no allocation, no synchronisation, no memset.  Requires
  * a PA_SPLIT_DISABLED plan with batch <= max_batch and seq_len <= max_q_len. */
 pa_status pa_prefill_backward(pa_plan_t plan, int32_t batch, int32_t seq_len, const int32_t* positions,
                               const void* q, const void* k, const void* v, const float* q_norm_weight,

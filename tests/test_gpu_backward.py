@@ -120,3 +120,24 @@ def test_backward_row_alone_equals_row_in_batch(gpu):
         outs.append([t.cpu().numpy() for t in g[:3]])
     for full, alone in zip(outs[0], outs[1]):
         assert np.array_equal(full[1:2].view(np.uint32), alone.view(np.uint32))
+
+
+def test_backward_positions_not_in_token_order(gpu):
+    """Visibility follows positions, not token order: row 0 holds a permutation of 0..S-1, row 1
+    starts at 37.  Tiles are skipped only where every pair is masked, so the gradients still
+    match the oracle.  out and lse come from the oracle's forward (the paged forward places
+    keys at their token index)."""
+    rng = np.random.default_rng(77)
+    B, Hq, Hkv, S = 2, 8, 2, 150
+    q, k, v, do, wq, wk, _ = _case(78, B, Hq, Hkv, S)
+    pos = np.stack([rng.permutation(S), 37 + np.arange(S)]).astype(np.int32)
+    ref = oracle.prefill_forward_backward(q, k, v, wq, wk, pos, do)
+    out = bf16_tensor(oracle.bf16_bits_from_f32(ref[0].astype(np.float32)))
+    lse = torch.from_numpy(ref[1].astype(np.float32)).cuda()
+    plan = pa.Plan(Hq, Hkv, max_batch=B, max_q_len=S, max_pages_per_row=16)
+    f = lambda a: torch.from_numpy(a).cuda()
+    g = pa.prefill_backward(plan, i32(pos), bf16_tensor(q), bf16_tensor(k), bf16_tensor(v), out, lse,
+                            bf16_tensor(do), q_norm_weight=f(wq), k_norm_weight=f(wk))
+    torch.cuda.synchronize()
+    for name, got, r in zip(("dq", "dk", "dv", "dw_q", "dw_k"), g, ref[2:]):
+        _check(name, got.cpu().numpy(), r)
