@@ -92,3 +92,24 @@ def test_forward_matches_the_forward_reference():
     # (half an ulp of an 8-bit significand: 2^-8 relative), lse by its float32 rounding
     assert np.all(np.abs(ref - out) <= 2.0 ** -8 * np.abs(out) + 1e-30)
     assert np.all(np.abs(ref_lse - lse) <= 2.0 ** -23 * np.abs(lse) + 1e-30)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 1)])
+def test_gradients_other_groups_and_two_rows(Hq, Hkv):
+    """GQA groups 1 and 4 with two rows at different positions: the head-to-KV-head map and the
+    per-row sums, against central differences of q, k and v."""
+    rng = np.random.default_rng(20 + Hq)
+    inp = _exact_inputs(rng, B=2, Hq=Hq, Hkv=Hkv, S=4)
+    pos = np.array([[0, 1, 2, 3], [3, 0, 5, 1]])
+    _, _, dq, dk, dv, _, _ = prefill_forward_backward(None, None, None, None, None, pos, None, exact_inputs=inp)
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        flat = inp[name].reshape(-1)
+        for i in rng.choice(flat.size, size=15, replace=False):
+            keep = flat[i]
+            flat[i] = keep + 1e-6
+            up = _loss(inp, pos)
+            flat[i] = keep - 1e-6
+            dn = _loss(inp, pos)
+            flat[i] = keep
+            fd = (up - dn) / 2e-6
+            assert abs(fd - grad.reshape(-1)[i]) <= 1e-6 * max(1.0, abs(fd)), (name, int(i))
