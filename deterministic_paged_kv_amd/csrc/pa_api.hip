@@ -108,6 +108,8 @@ pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, i
   if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_HEAD_RATIO;
   // positions stay int32 and the table below fits in memory
   if ((long long)max_pages_per_row * kPageSize + 1 > (1LL << 24)) return PA_ERR_CAPACITY;
+  // (row, KV head) units and their streams index int32 arrays and grids
+  if ((long long)max_batch * num_kv_heads > (1LL << 24)) return PA_ERR_CAPACITY;
 
   pa_plan_s* p = new (std::nothrow) pa_plan_s();
   if (!p) return PA_ERR_HIP;
