@@ -273,6 +273,7 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
   p.rope = plan->d_rope;
   p.eps = plan->rms_eps;
   p.chunk_pages = plan->split_chunk_pages;
+  p.num_cus = plan->num_cus;
   return launch_decode(p, workspace, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -24,10 +24,12 @@
 // pinned off in it, so both compile to the same arithmetic):
 //  * one workgroup of 8 wavefronts per (row, KV head), wavefront w walking pages w, w+8, ...
 //    and so running streams w and w+8, states combined through LDS (no workspace);
-//  * one single-wavefront workgroup per (row, KV head, stream), states written to a caller
-//    workspace, and a second kernel that combines each unit's states in stream order.  This
-//    spreads a long row over 16 compute units; the bits are identical.  Rows are launched
-//    longest first.
+//  * one wavefront per (row, KV head, stream), states written to a caller workspace, and a
+//    second kernel that combines each unit's states in stream order.  This spreads a long row
+//    over 16 compute units; the bits are identical.  Rows are launched longest first.  When
+//    the batch fills the device, the wavefronts of up to four KV heads of one (row, stream)
+//    form a workgroup: they walk the same pages, so each page's cos/sin rows are read once
+//    and shared through LDS instead of once per KV head.
 //
 // Memory layout.  k_cache/v_cache are NHD [page][slot][Hkv][128] bf16: one KV head of one
 // page is 16 rows of 256 B at a stride of Hkv * 256 B.  A lane (r = lane % 16, g = lane / 16)
@@ -35,12 +37,16 @@
 // load instruction covers 64 contiguous bytes of each of the 16 rows.  K goes straight from
 // registers through the prologue into the MFMA A operand; V is staged in LDS and read back
 // with keys along the MFMA reduction dimension.
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
 
 namespace {
 
+// s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding)
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kStreams = 16;                 // streams of the reduction tree
 constexpr int kUnitWaves = 8;                // wavefronts of the one-workgroup schedule
 constexpr int kDecodeThreads = kUnitWaves * 64;
@@ -48,7 +54,6 @@ constexpr int kDecodeThreads = kUnitWaves * 64;
 // multi-CU schedule one or two with the register file to itself
 constexpr int kUnitRing = 2;
 constexpr int kStreamRing = 2;
-constexpr int kStreamCsRing = 1;
 // V staging rows are padded by 16 bytes to spread the transposed reads over the LDS banks.
 constexpr int kVRow = kHeadDim + 8;
 typedef uint16_t VSlot[kPageSize][kVRow];
@@ -62,18 +67,21 @@ struct RowInfo {
   size_t head0;  // index of the group's first query head in [B * Hq]
 };
 
-__device__ __forceinline__ RowInfo row_info(const DecodeParams& P, int b, int hk) {
+// From the row's four metadata values (indptr[b], indptr[b + 1], last_page_len[b], qpos[b]).
+__device__ __forceinline__ RowInfo row_info_of(const DecodeParams& P, int b, int hk, int p0, int p1, int lpl, int qp) {
   RowInfo ri;
-  ri.p0 = P.indptr[b];
-  const int p1 = P.indptr[b + 1];
+  ri.p0 = p0;
   ri.n = p1 - ri.p0;
-  const int lpl = P.last_page_len[b];
-  ri.qp = P.qpos[b];
+  ri.qp = qp;
   ri.bad = ri.p0 < 0 || ri.n < 0 || p1 > P.num_indices || ri.n > P.max_pages_per_row || ri.qp < 0 ||
            ri.qp >= P.table_rows || (ri.n > 0 && (lpl < 1 || lpl > kPageSize));
   ri.L = (ri.n > 0 && !ri.bad) ? (ri.n - 1) * kPageSize + lpl : 0;
   ri.head0 = (size_t)b * P.num_q_heads + (size_t)hk * P.group;
   return ri;
+}
+
+__device__ __forceinline__ RowInfo row_info(const DecodeParams& P, int b, int hk) {
+  return row_info_of(P, b, hk, P.indptr[b], P.indptr[b + 1], P.last_page_len[b], P.qpos[b]);
 }
 
 // Output of a row with no keys (0, -inf) or with out-of-range metadata (NaN, NaN).
@@ -229,6 +237,79 @@ __device__ __forceinline__ void pv_page(const Scored& sc, StreamState& st, int r
   }
 }
 
+// Where a walk step's cos/sin rows come from (one row of 64 cos and 64 sin per key position,
+// 512 bytes).  CsOwn: the wavefront loads its own, one step ahead.  CsShared<HW>: the HW
+// wavefronts of a workgroup walk the same pages for HW KV heads, so they need the same rows;
+// each loads 8/HW of the eight 16-byte pieces per lane two steps ahead, they are staged in
+// an LDS ring of two slots, and a workgroup barrier per step publishes them.  The values are
+// the same either way, only the traffic differs (the rows of a page are read from the cache
+// hierarchy once per workgroup instead of once per KV head).
+struct CsOwn {
+  float4 cs[8];
+  int g;
+  __device__ __forceinline__ CsOwn(int g_) : g(g_) {}
+  template <class KP>
+  __device__ __forceinline__ void start(const DecodeParams& P, KP key_pos) { load_cos_sin(P.rope, key_pos(0), g, cs); }
+  template <int K>
+  __device__ __forceinline__ const float4* get() const { return cs; }
+  template <int K, class KP>
+  __device__ __forceinline__ void after_score(const DecodeParams& P, KP key_pos, int t) {
+    load_cos_sin(P.rope, key_pos(t + 1), g, cs);
+  }
+  template <int K>
+  __device__ __forceinline__ void end_step() {}
+};
+
+typedef f32x4 CsSlots[2][8][64];  // LDS ring: slot, piece, lane (native vectors: kept in registers)
+
+template <int HW>
+struct CsShared {
+  static constexpr int kPieces = 8 / HW;  // pieces this wavefront loads
+  f32x4 share0[kPieces], share1[kPieces];  // in flight for even / odd steps
+  float4 cs[8];
+  template <int K>
+  __device__ __forceinline__ f32x4 (&share())[kPieces] {
+    if constexpr ((K & 1) == 0) return share0;
+    else return share1;
+  }
+  CsSlots& slots;
+  int g, lane, w;
+  __device__ __forceinline__ CsShared(CsSlots& s, int g_, int lane_, int w_) : slots(s), g(g_), lane(lane_), w(w_) {}
+  __device__ __forceinline__ void load_share(const DecodeParams& P, int pos, f32x4 (&dst)[kPieces]) {
+    const f32x4* blk = reinterpret_cast<const f32x4*>(P.rope + (size_t)(pos >> 4) * kRopeBlockFloats);
+    const int l = (pos & 15) + 16 * g;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) dst[i] = blk[(w * kPieces + i) * 64 + l];
+  }
+  __device__ __forceinline__ void publish(int slot, const f32x4 (&src)[kPieces]) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) slots[slot][w * kPieces + i][lane] = src[i];
+    workgroup_lds_sync();
+  }
+  template <class KP>
+  __device__ __forceinline__ void start(const DecodeParams& P, KP key_pos) {
+    load_share(P, key_pos(0), share0);
+    load_share(P, key_pos(1), share1);
+    publish(0, share0);
+  }
+  // K: the walk step's parity (steps go in pairs, so the slots are compile-time constants)
+  template <int K>
+  __device__ __forceinline__ const float4* get() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x4 v = slots[K & 1][e][lane];
+      cs[e] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    return cs;
+  }
+  template <int K, class KP>
+  __device__ __forceinline__ void after_score(const DecodeParams& P, KP key_pos, int t) {
+    load_share(P, key_pos(t + 2), share<K>());
+  }
+  template <int K>
+  __device__ __forceinline__ void end_step() { publish((K + 1) & 1, share<K + 1>()); }
+};
+
 // One wavefront's walk over the pages first, first + stride, first + 2 stride, ... of one
 // (row, KV head) unit, at most `count` of them.  Walk step t feeds state st[t % NS]: with stride = kStreams and NS = 1
 // the wavefront is stream `first`; with stride = kStreams / 2 and NS = 2 it runs streams
@@ -240,10 +321,11 @@ __device__ __forceinline__ void pv_page(const Scored& sc, StreamState& st, int r
 // 64 at a time in one vector load (lane l: walk step 64 blk + l) and are taken out with
 // readlane, so they never wait behind other loads.  Steps past the row's end load the row's
 // last page (their data is never used), so every step issues the same loads.
-template <int R, int RC, int NS, class Kw>
+template <int R, int NS, class Kw, class Cs>
 __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& ri, int hk, int first, int stride,
-                                         int count, int lane, VSlot& sv, const Kw& kw, StreamState (&st)[NS]) {
-  static_assert(R % RC == 0 && R % NS == 0, "the rings and the state cycle must divide the K/V ring");
+                                         int count, int lane, VSlot& sv, const Kw& kw, Cs& csrc,
+                                         StreamState (&st)[NS]) {
+  static_assert(R % NS == 0 && R % 2 == 0, "the state cycle must divide the K/V ring, which holds whole pairs of steps");
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = P.group;
@@ -293,11 +375,9 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
   __builtin_amdgcn_sched_barrier(0);
 
   PageIn in[R];
-  float4 cs[RC][8];
 #pragma unroll
   for (int k = 0; k < R; ++k) issue_page(in[k], P, phys_at(k), hk, r, g);
-#pragma unroll
-  for (int c = 0; c < RC; ++c) load_cos_sin(P.rope, key_pos(c), g, cs[c]);
+  csrc.start(P, key_pos);
 
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -307,29 +387,41 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
     for (int nb = 0; nb < 8; ++nb) st[i].acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int t0 = 0; t0 < steps; t0 += R) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int t = t0 + k;
-      if (t >= steps) continue;  // (not break: an early exit from the unrolled body costs registers)
-      const int c = k % RC;
-      StreamState& sk = st[k % NS];
-      const Scored sc = score_page(in[k], cs[c], first + t * stride, sk, qop, kw, knorm, P.eps, L, qp, r, g, sv);
-      load_cos_sin(P.rope, key_pos(t + RC), g, cs[c]);
-      // refill the slot with step t + R; a new block of page numbers is due when t + R
-      // enters the next one
-      const int u = t + R;
-      if ((u & 63) == 0 && (u >> 6) != cur_blk) {
-        vcur = vnext;
-        cur_blk = u >> 6;
-        vnext = index_block(cur_blk + 1);
-      }
-      issue_page(in[k], P, phys_at(u), hk, r, g);
-      wave_lds_sync();
-      pv_page(sc, sk, r, g, sv);
-      wave_lds_sync();
+  // one walk step; K = t % R is a compile-time constant (ring slots stay in registers)
+  auto step = [&](auto kc, int t0) {
+    constexpr int k = decltype(kc)::value;
+    const int t = t0 + k;
+    StreamState& sk = st[k % NS];
+    const Scored sc =
+        score_page(in[k], csrc.template get<k>(), first + t * stride, sk, qop, kw, knorm, P.eps, L, qp, r, g, sv);
+    csrc.template after_score<k>(P, key_pos, t);
+    // refill the slot with step t + R; a new block of page numbers is due when t + R
+    // enters the next one
+    const int u = t + R;
+    if ((u & 63) == 0 && (u >> 6) != cur_blk) {
+      vcur = vnext;
+      cur_blk = u >> 6;
+      vnext = index_block(cur_blk + 1);
+      // wait for the new block here, on this rare path, so that the common path after the
+      // branch does not have to wait for every load in flight
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
+    issue_page(in[k], P, phys_at(u), hk, r, g);
+    wave_lds_sync();
+    pv_page(sc, sk, r, g, sv);
+    wave_lds_sync();
+    csrc.template end_step<k>();
+  };
+  // Whole pairs of steps, then the odd last one.  No path through the loop body skips a step,
+  // so the wait counts at the loop head know both slots' loads are in flight and wait only
+  // for the older one.
+  static_assert(R == 2, "the walk below is written out for a ring of two");
+  int t0 = 0;
+  for (; t0 + 2 <= steps; t0 += 2) {
+    step(std::integral_constant<int, 0>{}, t0);
+    step(std::integral_constant<int, 1>{}, t0);
   }
+  if (t0 < steps) step(std::integral_constant<int, 0>{}, t0);
 }
 
 // Combine the kStreams states of head h at dim d in stream order and write out (and lse at
@@ -392,7 +484,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
 
   // wavefront w walks pages w, w+8, ...: streams w (even steps) and w+8 (odd steps)
   StreamState st[2];
-  run_walk<kUnitRing, 1, 2>(P, ri, hk, wave, kUnitWaves, INT32_MAX, lane, sm.u.v[wave], KwLds{sm.kw}, st);
+  CsOwn cso(g);
+  run_walk<kUnitRing, 2>(P, ri, hk, wave, kUnitWaves, INT32_MAX, lane, sm.u.v[wave], KwLds{sm.kw}, cso, st);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -435,38 +528,60 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
 // ---------------------------------------------------------------------------------------
 constexpr int kCombineThreads = 512;
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
+template <int HW>
+__global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const DecodeParams P, int32_t* __restrict__ poisons, float* __restrict__ states) {
-  __shared__ VSlot sv;
-  const int lane = threadIdx.x;
+  __shared__ VSlot svs[HW];
+  __shared__ CsSlots cs_slots;  // used only when HW > 1
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  VSlot& sv = svs[w];
   const int s = blockIdx.x % kStreams;
-  const int hk = (blockIdx.x / kStreams) % P.num_kv_heads;
-  const int rank = blockIdx.x / (kStreams * P.num_kv_heads);
+  const int hgroups = P.num_kv_heads / HW;
+  const int hk = ((blockIdx.x / kStreams) % hgroups) * HW + w;
+  const int rank = blockIdx.x / (kStreams * hgroups);
   // Launch order: rows with more pages first, ties by row (up to 64 rows; beyond that, row
   // order).  The long rows' streams finish last; starting them first puts their first pages
   // at the head of the memory queue.  Only where a stream runs depends on it, not its bits.
+  // Lane j holds row j's metadata (one round of loads for the whole batch); the row picked is
+  // then read out of the lanes instead of being loaded again.
   int b = rank;
+  RowInfo ri;
   if (P.batch <= 64) {
-    const int my = lane < P.batch ? P.indptr[lane + 1] - P.indptr[lane] : -1;
+    const bool lv = lane < P.batch;
+    const int ip0 = lv ? P.indptr[lane] : 0;
+    const int ip1 = lv ? P.indptr[lane + 1] : 0;
+    const int lpl = lv ? P.last_page_len[lane] : 0;
+    const int qpl = lv ? P.qpos[lane] : 0;
+    const int my = lv ? ip1 - ip0 : -1;
     int rk = 0;
     for (int j = 0; j < P.batch; ++j) {
       const int nj = __builtin_amdgcn_readlane(my, j);
       rk += (nj > my || (nj == my && j < lane)) ? 1 : 0;
     }
-    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < P.batch && rk == rank);
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lv && rk == rank);
     b = hit ? (int)__builtin_ctzll(hit) : rank;
+    ri = row_info_of(P, b, hk, __builtin_amdgcn_readlane(ip0, b), __builtin_amdgcn_readlane(ip1, b),
+                     __builtin_amdgcn_readlane(lpl, b), __builtin_amdgcn_readlane(qpl, b));
+  } else {
+    ri = row_info(P, b, hk);
   }
   const int unit = b * P.num_kv_heads + hk;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = P.group;
-  const RowInfo ri = row_info(P, b, hk);
   if (ri.bad || ri.L == 0) return;  // the combine kernel writes these rows
   KwRegs kw;
   kw.load(P.k_norm, g);
 
   StreamState st[1];
-  run_walk<kStreamRing, kStreamCsRing, 1>(P, ri, hk, s, kStreams, INT32_MAX, lane, sv, kw, st);
+  if constexpr (HW == 1) {
+    CsOwn cso(g);
+    run_walk<kStreamRing, 1>(P, ri, hk, s, kStreams, INT32_MAX, lane, sv, kw, cso, st);
+  } else {
+    CsShared<HW> css(cs_slots, g, lane, w);
+    run_walk<kStreamRing, 1>(P, ri, hk, s, kStreams, INT32_MAX, lane, sv, kw, css, st);
+  }
 
   const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per stream state
   if (r < G) {
@@ -478,43 +593,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   if (lane == 0) poisons[unit * kStreams + s] = st[0].poison;
 }
 
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeParams P,
-                                                                         const int32_t* __restrict__ poisons,
-                                                                         const float* __restrict__ states) {
-  __shared__ float ml[kStreams][kMaxGroup][2];  // m and l of every stream and head
-  __shared__ int poison_any;
-  const int unit = blockIdx.x;
+// One workgroup per (unit, query head h), one thread per output dimension d.  The stream
+// maxima, sums and poison flags are the same for every thread of the workgroup (wave-uniform
+// loads); each thread reads its own dimension of the 16 accumulators.
+__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const DecodeParams P,
+                                                                  const int32_t* __restrict__ poisons,
+                                                                  const float* __restrict__ states) {
+  const int G = P.group;
+  const int unit = blockIdx.x / G;
+  const int h = blockIdx.x % G;
   const int b = unit / P.num_kv_heads;
   const int hk = unit % P.num_kv_heads;
-  const int G = P.group;
-  const int tid = threadIdx.x;
+  const int d = threadIdx.x;
   const RowInfo ri = row_info(P, b, hk);
   if (ri.bad || ri.L == 0) {
-    write_degenerate(P, ri, tid, kCombineThreads);
+    P.out[(ri.head0 + h) * kHeadDim + d] = ri.bad ? (uint16_t)0x7FC0 : (uint16_t)0;
+    if (d == 0) P.lse[ri.head0 + h] = ri.bad ? __builtin_nanf("") : -__builtin_inff();
     return;
   }
   const size_t rec = (size_t)G * (2 + kHeadDim);
-  const float* unit_states = states + (size_t)unit * kStreams * rec;
-  if (tid == 0) poison_any = 0;
-  __syncthreads();
-  // every stream's m, l and poison flag once into LDS, while the accumulators are loaded below
-  if (tid < kStreams * G * 2) {
-    const int w = tid / (2 * G), h = (tid / 2) % G, c = tid & 1;
-    ml[w][h][c] = unit_states[(size_t)w * rec + (size_t)h * (2 + kHeadDim) + c];
-  }
-  if (tid < kStreams && poisons[unit * kStreams + tid] != 0) atomicOr(&poison_any, 1);
-  for (int idx0 = 0; idx0 < G * kHeadDim; idx0 += kCombineThreads) {
-    const int idx = idx0 + tid;
-    const bool live = idx < G * kHeadDim;
-    const int h = live ? idx / kHeadDim : 0, d = idx % kHeadDim;
-    float a[kStreams];
+  const float* hs = states + (size_t)unit * kStreams * rec + (size_t)h * (2 + kHeadDim);
+  float mw[kStreams], lw[kStreams], a[kStreams];
+  int poison = 0;
 #pragma unroll
-    for (int w = 0; w < kStreams; ++w) a[w] = live ? unit_states[(size_t)w * rec + (size_t)h * (2 + kHeadDim) + 2 + d] : 0.0f;
-    __syncthreads();
-    if (live)
-      combine_one(P, ri, h, d, poison_any != 0, [&](int w) { return ml[w][h][0]; }, [&](int w) { return ml[w][h][1]; },
-                  [&](int w) { return a[w]; });
+  for (int w = 0; w < kStreams; ++w) {
+    mw[w] = load_uniform_f32(hs + (size_t)w * rec, 0);
+    lw[w] = load_uniform_f32(hs + (size_t)w * rec, 1);
+    poison |= load_uniform(poisons, unit * kStreams + w);
+    a[w] = hs[(size_t)w * rec + 2 + d];
   }
+  combine_one(P, ri, h, d, poison != 0, [&](int w) { return mw[w]; }, [&](int w) { return lw[w]; },
+              [&](int w) { return a[w]; });
 }
 
 // ---------------------------------------------------------------------------------------
@@ -542,7 +651,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   kw.load(P.k_norm, g);
 
   StreamState st[1];
-  run_walk<kStreamRing, kStreamCsRing, 1>(P, ri, hk, c * P.chunk_pages, 1, P.chunk_pages, lane, sv, kw, st);
+  CsOwn cso(g);
+  run_walk<kStreamRing, 1>(P, ri, hk, c * P.chunk_pages, 1, P.chunk_pages, lane, sv, kw, cso, st);
 
   const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per chunk state
   if (r < G) {
@@ -633,8 +743,18 @@ hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t str
     int32_t* poisons = (int32_t*)ws;
     ws += align256((size_t)units * kStreams * sizeof(int32_t));
     float* states = (float*)ws;
-    hipLaunchKernelGGL(decode_stream_kernel, dim3(units * kStreams), dim3(64), 0, stream, p, poisons, states);
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(units), dim3(kCombineThreads), 0, stream, p,
+    // The KV heads of a (row, stream) share a workgroup when they can (they walk the same
+    // pages and need the same cos/sin rows), as long as that still gives every compute unit a
+    // workgroup; a batch too small for that keeps one wavefront per workgroup and spreads its
+    // streams over more compute units.  Where a stream runs never changes its bits.
+    const long long waves = (long long)units * kStreams;
+    if (p.num_kv_heads % 4 == 0 && waves / 4 >= p.num_cus)
+      hipLaunchKernelGGL(decode_stream_kernel<4>, dim3(units / 4 * kStreams), dim3(256), 0, stream, p, poisons, states);
+    else if (p.num_kv_heads % 2 == 0 && waves / 2 >= p.num_cus)
+      hipLaunchKernelGGL(decode_stream_kernel<2>, dim3(units / 2 * kStreams), dim3(128), 0, stream, p, poisons, states);
+    else
+      hipLaunchKernelGGL(decode_stream_kernel<1>, dim3(units * kStreams), dim3(64), 0, stream, p, poisons, states);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(units * (unsigned)p.group), dim3(kHeadDim), 0, stream, p,
                        (const int32_t*)poisons, (const float*)states);
   }
   return hipGetLastError();

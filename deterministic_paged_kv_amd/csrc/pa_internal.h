@@ -230,6 +230,10 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 __device__ __forceinline__ int32_t load_uniform(const int32_t* p, int i) {
   return ((const_i32_ptr)p)[i];
 }
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+__device__ __forceinline__ float load_uniform_f32(const float* p, int i) {
+  return ((const_f32_ptr)p)[i];
+}
 
 // Intra-wavefront LDS hand-off: make this lane's LDS writes visible to the other lanes of
 // the same wavefront, and keep the compiler from moving LDS accesses across this point.
@@ -237,6 +241,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// LDS writes of every wavefront of the workgroup visible to all of them: waits for this
+// wavefront's LDS operations, then the workgroup barrier.  Vector memory loads in flight are
+// not waited for.
+__device__ __forceinline__ void workgroup_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 struct DecodeParams {
@@ -256,6 +269,7 @@ struct DecodeParams {
   const float* rope;
   float eps;
   int32_t chunk_pages;  // 0: the fixed 16-stream tree; > 0: fixed chunks of this many pages
+  int32_t num_cus;      // compute units of the device (work placement only, never arithmetic)
 };
 
 // Decode.  chunk_pages == 0 and workspace == NULL: one workgroup per (row, KV head).

@@ -72,9 +72,12 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // ---------------------------------------------------------------------------------------
 // 1. k^ for every cached key
 // ---------------------------------------------------------------------------------------
-// Row b = blockIdx.y; its (page, KV head) tasks are spread over the x blocks, 4 wavefronts each
-// (task t: page t / Hkv of the row, KV head t % Hkv, so neighbouring wavefronts share a page's
-// positions).  Only the keys of valid rows are written; nothing reads the other slots.
+// Row b = blockIdx.y; its tasks are spread over the x blocks, 4 wavefronts each.  A task is
+// one page of the row and HG consecutive KV heads: the wavefront reads the page's RoPE rows once
+// and issues the K loads of all HG heads before the first prologue, so the 16 positions' cos/sin
+// (512 B each) are fetched once per HG heads.  Only the keys of valid rows are written; nothing
+// reads the other slots.
+template <int HG>
 __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
@@ -88,6 +91,7 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
   if (!row_ok) return;  // the attention kernel treats such a row as empty or poisoned
   const int L = (n - 1) * kPageSize + lpl;
   const int Hkv = P.num_kv_heads;
+  const int groups = Hkv / HG;
   const bool knorm = P.k_norm != nullptr;
   float kw[32];
 #pragma unroll
@@ -96,11 +100,11 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
     for (int e = 0; e < 8; ++e) kw[kb * 8 + e] = knorm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
   const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  const int tasks = n * Hkv;
+  const int tasks = n * groups;
   const int stride = gridDim.x * (blockDim.x >> 6);
   for (int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < tasks; t += stride) {
-    const int pr = t / Hkv;
-    const int hk = t % Hkv;
+    const int pr = t / groups;
+    const int hk0 = (t % groups) * HG;
     const int j = pr * kPageSize + r;  // logical key index = key position
     const bool live = j < L;
     float4 cs[8];
@@ -108,16 +112,31 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
     int phys = P.indices[p0 + pr];
     const bool page_ok = phys >= 0 && phys < P.num_pages;
     if (!page_ok) phys = 0;
-    const size_t src = (((size_t)phys * kPageSize + r) * Hkv + hk) * kHeadDim + 8 * g;
-    uint4 raw[4];
+    // the HG heads of slot r are contiguous: HG * 256 bytes
+    const size_t src = (((size_t)phys * kPageSize + r) * Hkv + hk0) * kHeadDim + 8 * g;
+    uint4 raw[HG][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.k_cache + src + 32 * kb) : zero4;
-    bf16x8 op[4];
-    prologue_operand(raw, kw, knorm, P.eps, cs, op);
-    uint16_t* dst = kh + ((size_t)hk * P.num_indices * kPageSize + (size_t)(p0 + pr) * kPageSize + r) * kHeadDim + 8 * g;
+    for (int h = 0; h < HG; ++h)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !page_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
+      for (int kb = 0; kb < 4; ++kb) raw[h][kb] = live ? ldg16(P.k_cache + src + h * kHeadDim + 32 * kb) : zero4;
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      bf16x8 op[4];
+      prologue_operand(raw[h], kw, knorm, P.eps, cs, op);
+      uint16_t* dst =
+          kh + ((size_t)(hk0 + h) * P.num_indices * kPageSize + (size_t)(p0 + pr) * kPageSize + r) * kHeadDim + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !page_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
+    }
   }
+}
+
+template <int HG>
+void launch_key_prologue(const PrefillParams& p, uint16_t* kh, hipStream_t stream) {
+  // per row: up to max_pages_per_row * Hkv / HG tasks, 4 per block, at most 512 blocks per row
+  const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * (p.num_kv_heads / HG);
+  const unsigned bx = (unsigned)std::min<long long>((row_tasks + 3) / 4, 512);
+  hipLaunchKernelGGL(key_prologue_kernel<HG>, dim3(bx, (unsigned)p.batch), dim3(256), 0, stream, p, kh);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -513,10 +532,12 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   uint16_t* kh = (uint16_t*)p.workspace;
   if (p.num_indices > 0) {
-    // per row: up to max_pages_per_row * Hkv tasks, 4 per block, at most 512 blocks per row
-    const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * p.num_kv_heads;
-    const unsigned bx = (unsigned)std::min<long long>((row_tasks + 3) / 4, 512);
-    hipLaunchKernelGGL(key_prologue_kernel, dim3(bx, (unsigned)p.batch), dim3(256), 0, stream, p, kh);
+#ifndef PA_KEY_HEADS
+#define PA_KEY_HEADS 4
+#endif
+    if (PA_KEY_HEADS >= 4 && p.num_kv_heads % 4 == 0) launch_key_prologue<4>(p, kh, stream);
+    else if (PA_KEY_HEADS >= 2 && p.num_kv_heads % 2 == 0) launch_key_prologue<2>(p, kh, stream);
+    else launch_key_prologue<1>(p, kh, stream);
   }
   const unsigned nqb = (unsigned)((p.q_len + kQBlock - 1) / kQBlock);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
