@@ -42,6 +42,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 METRIC = "paged decode KV GB/s (% HBM peak); paged prefill TFLOP/s (% MFMA peak)"
 ROTATIONS = 4
+# untimed calls before each secondary workload (long-context decode, prefill, backward)
+SETTLE_MS = 60.0
 
 
 def decode_bytes(b) -> int:
@@ -157,12 +159,24 @@ def long_context_set(batch, length, device, seed=1004):
     return meta, db
 
 
-def time_calls(fn, sets, steps, warmup):
-    """Run fn(set) over the rotation; return (wall ms per step, mean per-launch event ms)."""
+def time_calls(fn, sets, steps, warmup, settle_ms=0.0):
+    """Run fn(set) over the rotation; return (wall ms per step, mean per-launch event ms).
+
+    After the `warmup` calls, further untimed calls run until `settle_ms` of wall time has
+    passed, so that a workload timed right after another one is measured at its steady clock
+    (the first tens of milliseconds of a new load run at a lower shader clock)."""
     import torch
 
     for i in range(warmup):
         fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        fn(sets[i % len(sets)])
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -217,7 +231,7 @@ def bench_backward(device, steps, warmup, batch=4, seq=2048, hq=32, hkv=8):
         pa.prefill_backward(plan, pos, q, k, v, out, lse, dout, q_norm_weight=wq, k_norm_weight=wk, workspace=ws,
                             grads=grads)
 
-    b_wall, b_launch = time_calls(bstep, [None], steps, warmup)
+    b_wall, b_launch = time_calls(bstep, [None], steps, warmup, settle_ms=SETTLE_MS)
     flops = backward_flops(batch, seq, hq)
     return {"workload": "full_prefill_backward", "batch": batch, "seq_len": seq, "num_q_heads": hq,
             "num_kv_heads": hkv, "steps": steps, "ms_per_call": round(b_wall, 5),
@@ -432,7 +446,7 @@ def main():
 
     if not args.decode_only and not args.prefill_only:
         # Long-context low-batch decode (B=1, L=131,072): the 16-stream tree against the
-        # fixed-chunk policy, which cuts the row into 2,048-token chunks (64 chunks).
+        # fixed-chunk policy, which cuts the row into 1,024-token chunks (128 chunks).
         print("[bench] timing long-context decode", file=sys.stderr, flush=True)
         lmeta, ldb = long_context_set(1, 131072, device)
         lout = torch.empty_like(ldb.q)
@@ -441,7 +455,7 @@ def main():
         long_result = {"workload": "long_context_decode", "batch": 1, "kv_len": 131072, "num_q_heads": 32,
                        "num_kv_heads": 8, "algorithmic_bytes_per_call": lalg}
         for name, policy, chunk in (("split_disabled", pa.PA_SPLIT_DISABLED, 0),
-                                    ("split_fixed_2048", pa.PA_SPLIT_FIXED, 2048)):
+                                    ("split_fixed_1024", pa.PA_SPLIT_FIXED, 1024)):
             lplan = pa.Plan(32, 8, max_batch=1, max_q_len=1, max_pages_per_row=8192, rms_eps=1e-6,
                             split_policy=policy, split_chunk_tokens=chunk)
             lws = pa.decode_workspace(lplan, 1, device=device)
@@ -449,7 +463,7 @@ def main():
             def lstep(db, lplan=lplan, lws=lws):
                 pa.decode(lplan, *db.args(), out=lout, lse=llse, workspace=lws)
 
-            l_wall, l_launch = time_calls(lstep, [ldb], 20, 3)
+            l_wall, l_launch = time_calls(lstep, [ldb], 20, 3, settle_ms=SETTLE_MS)
             long_result[name] = {"ms_per_call": round(l_launch, 5),
                                  "value": round(lalg / (l_launch * 1e-3) / 1e9, 2), "unit": "GB/s",
                                  "frac": round(lalg / (l_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -469,7 +483,7 @@ def main():
             pa.prefill(pplan, *db.args(), out=pout, lse=plse, workspace=ws)
 
         psteps = max(20, args.steps // 4)
-        p_wall, p_launch = time_calls(pstep, [pdb], psteps, args.warmup)
+        p_wall, p_launch = time_calls(pstep, [pdb], psteps, args.warmup, settle_ms=SETTLE_MS)
         flops = prefill_flops(pb)
         result["prefill"] = {
             "workload": "chunked_prefill", "batch": 4, "q_len": 512, "prefixes": [0, 1024, 2048, 3584],

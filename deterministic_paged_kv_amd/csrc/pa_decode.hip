@@ -526,7 +526,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_unit_kernel(const Decod
 // Workspace: an int32 poison flag per (unit, stream), then per unit and stream G records of
 // [m, l, 128 accumulators].
 // ---------------------------------------------------------------------------------------
-constexpr int kCombineThreads = 512;
 
 template <int HW>
 __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
@@ -633,14 +632,22 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const DecodePa
 // depends only on the row's length and the chunk size.  Workspace: an int32 poison flag per
 // (unit, chunk slot), then per unit and chunk slot G records of [m, l, 128 accumulators].
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_chunk_kernel(
+// One wavefront per (row, KV head, chunk); as in the stream schedule, the wavefronts of up to
+// HW KV heads of one (row, chunk) form a workgroup and share the chunk's cos/sin rows.
+template <int HW>
+__global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_chunk_kernel(
     const DecodeParams P, int max_chunks, int32_t* __restrict__ poisons, float* __restrict__ states) {
-  __shared__ VSlot sv;
-  const int unit = blockIdx.x / max_chunks;
+  __shared__ VSlot svs[HW];
+  __shared__ CsSlots cs_slots;  // used only when HW > 1
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  VSlot& sv = svs[w];
+  const int hgroups = P.num_kv_heads / HW;
+  const int grp = blockIdx.x / max_chunks;
   const int c = blockIdx.x % max_chunks;
-  const int b = unit / P.num_kv_heads;
-  const int hk = unit % P.num_kv_heads;
-  const int lane = threadIdx.x;
+  const int b = grp / hgroups;
+  const int hk = (grp % hgroups) * HW + w;
+  const int unit = b * P.num_kv_heads + hk;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = P.group;
@@ -651,8 +658,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   kw.load(P.k_norm, g);
 
   StreamState st[1];
-  CsOwn cso(g);
-  run_walk<kStreamRing, 1>(P, ri, hk, c * P.chunk_pages, 1, P.chunk_pages, lane, sv, kw, cso, st);
+  if constexpr (HW == 1) {
+    CsOwn cso(g);
+    run_walk<kStreamRing, 1>(P, ri, hk, c * P.chunk_pages, 1, P.chunk_pages, lane, sv, kw, cso, st);
+  } else {
+    CsShared<HW> css(cs_slots, g, lane, w);
+    run_walk<kStreamRing, 1>(P, ri, hk, c * P.chunk_pages, 1, P.chunk_pages, lane, sv, kw, css, st);
+  }
 
   const size_t rec = (size_t)G * (2 + kHeadDim);  // floats per chunk state
   if (r < G) {
@@ -667,48 +679,70 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // Fold of (m, l, acc) in ascending chunk order: with m' = max(m, m_c),
 //   l <- l 2^(m - m') + l_c 2^(m_c - m'),  acc <- acc 2^(m - m') + acc_c 2^(m_c - m'),  m <- m'
 // (a state with m = -inf weighs 0), then out = acc / l and lse = (m + log2 l) ln 2.
-__global__ __launch_bounds__(kCombineThreads) void decode_fold_kernel(const DecodeParams P, int max_chunks,
-                                                                      const int32_t* __restrict__ poisons,
-                                                                      const float* __restrict__ states) {
+// One workgroup per (unit, query head h), one thread per output dimension d: the chunk states
+// are folded left to right, c = 0, 1, ..., in FP32.  The loads of a batch of chunks go out
+// together (the chunk maxima and sums are wave-uniform); only the arithmetic is sequential.
+constexpr int kFoldBatch = 8;
+__global__ __launch_bounds__(kHeadDim) void decode_fold_kernel(const DecodeParams P, int max_chunks,
+                                                               const int32_t* __restrict__ poisons,
+                                                               const float* __restrict__ states) {
 #pragma clang fp contract(off)
-  __shared__ int poison_any;
-  const int unit = blockIdx.x;
+  const int G = P.group;
+  const int unit = blockIdx.x / G;
+  const int h = blockIdx.x % G;
   const int b = unit / P.num_kv_heads;
   const int hk = unit % P.num_kv_heads;
-  const int G = P.group;
-  const int tid = threadIdx.x;
+  const int d = threadIdx.x;
   const RowInfo ri = row_info(P, b, hk);
   if (ri.bad || ri.L == 0) {
-    write_degenerate(P, ri, tid, kCombineThreads);
+    P.out[(ri.head0 + h) * kHeadDim + d] = ri.bad ? (uint16_t)0x7FC0 : (uint16_t)0;
+    if (d == 0) P.lse[ri.head0 + h] = ri.bad ? __builtin_nanf("") : -__builtin_inff();
     return;
   }
   const int nch = (ri.n + P.chunk_pages - 1) / P.chunk_pages;
   const size_t rec = (size_t)G * (2 + kHeadDim);
-  const float* unit_states = states + (size_t)unit * max_chunks * rec;
-  if (tid == 0) poison_any = 0;
-  __syncthreads();
-  for (int c = tid; c < nch; c += kCombineThreads)
-    if (poisons[unit * max_chunks + c] != 0) atomicOr(&poison_any, 1);
-  __syncthreads();
-  for (int idx = tid; idx < G * kHeadDim; idx += kCombineThreads) {
-    const int h = idx / kHeadDim, d = idx % kHeadDim;
-    float m = -__builtin_inff(), l = 0.0f, a = 0.0f;
-    for (int c = 0; c < nch; ++c) {
-      const float* hrec = unit_states + (size_t)c * rec + (size_t)h * (2 + kHeadDim);
-      const float mc = hrec[0], lc = hrec[1], ac = hrec[2 + d];
-      const float mn = fmaxf(m, mc);
+  const float* hs = states + (size_t)unit * max_chunks * rec + (size_t)h * (2 + kHeadDim);
+  int poison = 0;
+  for (int c = d; c < nch; c += kHeadDim) poison |= poisons[unit * max_chunks + c];
+  const bool poisoned = __syncthreads_or(poison) != 0;
+  float m = -__builtin_inff(), l = 0.0f, a = 0.0f;
+  for (int c0 = 0; c0 < nch; c0 += kFoldBatch) {
+    float mc[kFoldBatch], lc[kFoldBatch], ac[kFoldBatch];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const int c = min(c0 + i, nch - 1);
+      mc[i] = load_uniform_f32(hs + (size_t)c * rec, 0);
+      lc[i] = load_uniform_f32(hs + (size_t)c * rec, 1);
+      ac[i] = hs[(size_t)c * rec + 2 + d];
+    }
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      if (c0 + i >= nch) break;
+      const float mn = fmaxf(m, mc[i]);
       const float s0 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-      const float s1 = mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - mn);
-      l = l * s0 + lc * s1;
-      a = a * s0 + ac * s1;
+      const float s1 = mc[i] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc[i] - mn);
+      l = l * s0 + lc[i] * s1;
+      a = a * s0 + ac[i] * s1;
       m = mn;
     }
-    float o = a / l;
-    float lse = (m + __builtin_log2f(l)) * kLn2;
-    if (poison_any != 0) { o = __builtin_nanf(""); lse = __builtin_nanf(""); }
-    P.out[(ri.head0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
-    if (d == 0) P.lse[ri.head0 + h] = lse;
   }
+  float o = a / l;
+  float lse = (m + __builtin_log2f(l)) * kLn2;
+  if (poisoned) { o = __builtin_nanf(""); lse = __builtin_nanf(""); }
+  P.out[(ri.head0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
+  if (d == 0) P.lse[ri.head0 + h] = lse;
+}
+
+// KV heads per workgroup of the multi-CU and chunk schedules.  The KV heads of one (row, stream
+// or chunk) share a workgroup when the grid is large enough (at least four wavefronts per compute
+// unit): they walk the same pages and need the same cos/sin rows.  A smaller grid keeps one
+// wavefront per workgroup and spreads over more compute units.  Where a wavefront runs never
+// changes its bits.
+int heads_per_workgroup(const DecodeParams& p, long long waves) {
+  if (waves < 4LL * p.num_cus) return 1;
+  if (p.num_kv_heads % 4 == 0) return 4;
+  if (p.num_kv_heads % 2 == 0) return 2;
+  return 1;
 }
 
 int max_chunks_of(int chunk_pages, int max_pages_per_row) {
@@ -732,9 +766,17 @@ hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t str
     int32_t* poisons = (int32_t*)ws;
     ws += align256((size_t)units * max_chunks * sizeof(int32_t));
     float* states = (float*)ws;
-    hipLaunchKernelGGL(decode_chunk_kernel, dim3(units * (unsigned)max_chunks), dim3(64), 0, stream, p, max_chunks,
-                       poisons, states);
-    hipLaunchKernelGGL(decode_fold_kernel, dim3(units), dim3(kCombineThreads), 0, stream, p, max_chunks,
+    const int hw = heads_per_workgroup(p, (long long)units * max_chunks);
+    if (hw == 4)
+      hipLaunchKernelGGL(decode_chunk_kernel<4>, dim3(units / 4 * (unsigned)max_chunks), dim3(256), 0, stream, p,
+                         max_chunks, poisons, states);
+    else if (hw == 2)
+      hipLaunchKernelGGL(decode_chunk_kernel<2>, dim3(units / 2 * (unsigned)max_chunks), dim3(128), 0, stream, p,
+                         max_chunks, poisons, states);
+    else
+      hipLaunchKernelGGL(decode_chunk_kernel<1>, dim3(units * (unsigned)max_chunks), dim3(64), 0, stream, p,
+                         max_chunks, poisons, states);
+    hipLaunchKernelGGL(decode_fold_kernel, dim3(units * (unsigned)p.group), dim3(kHeadDim), 0, stream, p, max_chunks,
                        (const int32_t*)poisons, (const float*)states);
   } else if (workspace == nullptr) {
     hipLaunchKernelGGL(decode_unit_kernel, dim3(units), dim3(kDecodeThreads), 0, stream, p);
@@ -743,14 +785,10 @@ hipError_t launch_decode(const DecodeParams& p, void* workspace, hipStream_t str
     int32_t* poisons = (int32_t*)ws;
     ws += align256((size_t)units * kStreams * sizeof(int32_t));
     float* states = (float*)ws;
-    // The KV heads of a (row, stream) share a workgroup when they can (they walk the same
-    // pages and need the same cos/sin rows), as long as that still gives every compute unit a
-    // workgroup; a batch too small for that keeps one wavefront per workgroup and spreads its
-    // streams over more compute units.  Where a stream runs never changes its bits.
-    const long long waves = (long long)units * kStreams;
-    if (p.num_kv_heads % 4 == 0 && waves / 4 >= p.num_cus)
+    const int hw = heads_per_workgroup(p, (long long)units * kStreams);
+    if (hw == 4)
       hipLaunchKernelGGL(decode_stream_kernel<4>, dim3(units / 4 * kStreams), dim3(256), 0, stream, p, poisons, states);
-    else if (p.num_kv_heads % 2 == 0 && waves / 2 >= p.num_cus)
+    else if (hw == 2)
       hipLaunchKernelGGL(decode_stream_kernel<2>, dim3(units / 2 * kStreams), dim3(128), 0, stream, p, poisons, states);
     else
       hipLaunchKernelGGL(decode_stream_kernel<1>, dim3(units * kStreams), dim3(64), 0, stream, p, poisons, states);

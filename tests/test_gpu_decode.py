@@ -148,10 +148,10 @@ def test_multi_cu_schedule_is_bit_identical(gpu, name):
         b = workloads.invariance_batch(alone=False)
     elif name == "groups16":
         b = workloads.make_batch(42, [900, 77], q_len=1, num_q_heads=32, num_kv_heads=2, num_pages=128)
-    else:  # KV head counts that take one (kv1, kv3) and two (kv6: 8 rows, 768 streams) KV heads per
-        # workgroup of the multi-CU schedule
+    else:  # KV head counts that take one (kv1, kv3) and two (kv6: 12 rows, 1,152 streams) KV heads
+        # per workgroup of the multi-CU schedule
         hkv = int(name[2:])
-        lengths = [530, 17, 0, 64] * (2 if hkv == 6 else 1)
+        lengths = [530, 17, 0, 64] * (3 if hkv == 6 else 1)
         b = workloads.make_batch(43, lengths, q_len=1, num_q_heads=2 * hkv, num_kv_heads=hkv, num_pages=256)
     plan = make_plan(b, max_pages_per_row=max(256, int(np.max(np.diff(b.kv_indptr)))))
     db = DeviceBatch(b)
