@@ -31,11 +31,20 @@ namespace pa {
 
 namespace {
 
-constexpr int kQBlock = 32;          // queries per wavefront (two 16-row MFMA tiles)
-constexpr int kQT = kQBlock / 16;
+constexpr int kQBlock = 32;          // queries per work item (two 16-row MFMA tiles)
 constexpr int kKT = 32;              // keys per tile (2 pages)
 constexpr int kRow = kHeadDim + 16;  // LDS row, padded by 32 bytes (conflict-free transposed reads)
-constexpr int kAttendThreads = 256;
+// Workgroup shape: H wavefronts per query head, each taking 32 / H of the item's 32 queries
+// (H = 1: one wavefront per head with both 16-query tiles; H = 2: two wavefronts per head with
+// one tile each).  Every query's arithmetic is the same either way (the bits are identical);
+// H = 2 doubles the wavefronts that walk one item's keys, which shortens the longest items.
+template <int H>
+struct Shape {
+  static constexpr int kQT = kQBlock / 16 / H;         // 16-query MFMA tiles per wavefront
+  static constexpr int kThreads = 256 * H;             // 4 query heads x H wavefronts
+  static constexpr int kTileRows = kThreads / 16;      // tile rows one pass of the threads covers
+  static constexpr int kRowsPerThread = 32 / kTileRows;  // key rows of a 32-key tile per thread
+};
 // A query's softmax reference is moved only when a tile's scaled score exceeds it by more
 // than this (log2 domain), so probabilities stay below 2^8 and rescaling is rare.
 constexpr float kLazyMax = 8.0f;
@@ -154,21 +163,25 @@ struct RankSmem {
   int sel;
 };
 
-// The tile's share of one thread: k^ and V rows rt and rt + 16 of the tile (rt = tid / 16), 16
-// bytes each at column chunk tid % 16.  Keys past the row's end read the row's last key, so
+// The tile's share of one thread: k^ and V rows rt + kTileRows u of the tile (rt = tid / 16),
+// 16 bytes each at column chunk tid % 16.  Keys past the row's end read the row's last key, so
 // every load is in bounds and finite (their scores are masked and their probabilities are 0).
+template <int H>
 struct TileRegs {
-  uint4 k[2];
-  uint4 v[2];
+  uint4 k[Shape<H>::kRowsPerThread];
+  uint4 v[Shape<H>::kRowsPerThread];
 };
 
-__device__ __forceinline__ void store_tile(const TileRegs& tr, AttendSmem& sm, int buf, int tid) {
+template <int H>
+__device__ __forceinline__ void store_tile(const TileRegs<H>& tr, AttendSmem& sm, int buf, int tid) {
+  constexpr int kTileRows = Shape<H>::kTileRows;
+  constexpr int kRowsPerThread = Shape<H>::kRowsPerThread;
   const int rt = tid >> 4;
   const int col = tid & 15;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    *reinterpret_cast<uint4*>(&sm.k[buf][16 * u + rt][col * 8]) = tr.k[u];
-    *reinterpret_cast<uint4*>(&sm.v[buf][16 * u + rt][col * 8]) = tr.v[u];
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    *reinterpret_cast<uint4*>(&sm.k[buf][kTileRows * u + rt][col * 8]) = tr.k[u];
+    *reinterpret_cast<uint4*>(&sm.v[buf][kTileRows * u + rt][col * 8]) = tr.v[u];
   }
 }
 
@@ -193,10 +206,11 @@ __device__ int unit_tiles(const PrefillParams& P, int nqb, int u) {
 
 // The unit of rank `target` in the order: more tiles first, then lower unit number.
 // All threads of the workgroup call it; U <= kMaxRankUnits.
-__device__ int unit_of_rank(const PrefillParams& P, int nqb, int U, int target, int tid, RankSmem& rs) {
-  for (int u = tid; u < U; u += kAttendThreads) rs.tiles[u] = unit_tiles(P, nqb, u);
+__device__ int unit_of_rank(const PrefillParams& P, int nqb, int U, int target, int tid, int nthreads,
+                            RankSmem& rs) {
+  for (int u = tid; u < U; u += nthreads) rs.tiles[u] = unit_tiles(P, nqb, u);
   __syncthreads();
-  for (int u = tid; u < U; u += kAttendThreads) {
+  for (int u = tid; u < U; u += nthreads) {
     const int c = rs.tiles[u];
     int rank = 0;
     for (int v = 0; v < U; ++v) {
@@ -209,8 +223,13 @@ __device__ int unit_of_rank(const PrefillParams& P, int nqb, int U, int target, 
   return rs.sel;
 }
 
-__global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillParams P,
-                                                                const uint16_t* __restrict__ kh) {
+template <int H>
+__global__ __launch_bounds__(256 * H) __attribute__((amdgpu_waves_per_eu(2 * H, 2 * H))) void attend_kernel(
+    const PrefillParams P, const uint16_t* __restrict__ kh) {
+  constexpr int kQT = Shape<H>::kQT;
+  constexpr int kAttendThreads = Shape<H>::kThreads;
+  constexpr int kTileRows = Shape<H>::kTileRows;
+  constexpr int kRowsPerThread = Shape<H>::kRowsPerThread;
   __shared__ AttendSmem sm;
   __shared__ RankSmem sched;
   const int G = P.group;
@@ -232,7 +251,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
     // number of key tiles each unit visits), so every compute unit holds one long and one
     // short item.
     const int rank = (int)blockIdx.x < P.num_cus ? (int)blockIdx.x : N - 1 - ((int)blockIdx.x - P.num_cus);
-    unit = unit_of_rank(P, nqb, U, rank / HH, tid, sched);
+    unit = unit_of_rank(P, nqb, U, rank / HH, tid, kAttendThreads, sched);
     head = rank % HH;
   } else {
     // Otherwise longest first in launch order: the last query blocks of every row see the
@@ -245,10 +264,11 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
   const int hg = head % nhg;
   const int hk = head / nhg;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2;         // which 32 / H queries of the block (0 when H = 1)
   const int lane = tid & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int gi = hg * 4 + wave;       // head within the GQA group
+  const int gi = hg * 4 + (wave & 3);  // head within the GQA group
   const bool head_live = gi < G;      // trailing waves of a partial group only help stage tiles
   const int h = hk * G + (head_live ? gi : 0);
 
@@ -260,23 +280,29 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
                    (n > 0 && (lpl < 1 || lpl > kPageSize));
   const int L = (n > 0 && !bad) ? (n - 1) * kPageSize + lpl : 0;
 
-  // positions of this lane's queries (-1: past the chunk, sees nothing)
-  int qp[kQT];
-  int i_of[kQT];
+  // positions of the block's queries (-1: past the chunk, sees nothing): every wavefront takes
+  // the first and last key positions over all 32 (the tile walk is the block's, the same in
+  // every wavefront), then keeps those of its own 16
+  int qp_blk[kQBlock / 16];
   int poison = bad;
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) {
+  for (int t = 0; t < kQBlock / 16; ++t) {
     const int i = qb * kQBlock + 16 * t + r;
-    i_of[t] = i;
-    qp[t] = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
-    if (qp[t] >= P.table_rows) { poison = 1; qp[t] = -1; }
+    qp_blk[t] = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
+    if (qp_blk[t] >= P.table_rows) { poison = 1; qp_blk[t] = -1; }
   }
-  // first and last key positions any query of the block can see
-  int qmax = qp[0], qmin = qp[0] < 0 ? INT32_MAX : qp[0];
+  int qp[kQT];
+  int i_of[kQT];
 #pragma unroll
-  for (int t = 1; t < kQT; ++t) {
-    qmax = max(qmax, qp[t]);
-    if (qp[t] >= 0) qmin = min(qmin, qp[t]);
+  for (int t = 0; t < kQT; ++t) {
+    i_of[t] = qb * kQBlock + 16 * (half * kQT + t) + r;
+    qp[t] = half == 0 ? qp_blk[t] : qp_blk[kQT + t];
+  }
+  int qmax = qp_blk[0], qmin = qp_blk[0] < 0 ? INT32_MAX : qp_blk[0];
+#pragma unroll
+  for (int t = 1; t < kQBlock / 16; ++t) {
+    qmax = max(qmax, qp_blk[t]);
+    if (qp_blk[t] >= 0) qmin = min(qmin, qp_blk[t]);
   }
 #pragma unroll
   for (int sh = 1; sh < 16; sh <<= 1) {
@@ -344,20 +370,22 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
   // holding the page of the tile's half u), so no scalar load shares a counter with the LDS
   // reads.
   constexpr int kRing = 3;
-  TileRegs ring[kRing];
+  TileRegs<H> ring[kRing];
   const int32_t* row_idx = P.indices + p0;
   const size_t page_elems = (size_t)kPageSize * Hkv * kHeadDim;
   const int rt = tid >> 4;
   const int col = tid & 15;
   const uint32_t v_lane_off = (uint32_t)hk * kHeadDim + col * 8;
+  static_assert(kTileRows % 16 == 0 || kRowsPerThread * kTileRows == 32, "tile rows must split into pages");
   // page numbers of tile t (lane u: page min(2t + u, n - 1)); only called with n >= 1
   auto page_vec = [&](int t) -> int { return row_idx[min(2 * t + (lane & 1), n - 1)]; };
-  auto load = [&](TileRegs& tr, int t, int pv) {
+  auto load = [&](TileRegs<H>& tr, int t, int pv) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int phys = __builtin_amdgcn_readlane(pv, u);
+    for (int u = 0; u < kRowsPerThread; ++u) {
+      const int ro = kTileRows * u + rt;  // row of the tile; its page is the tile's half ro / 16
+      int phys = __builtin_amdgcn_readlane(pv, __builtin_amdgcn_readfirstlane(ro >> 4));
       if (phys < 0 || phys >= P.num_pages) { poison = 1; phys = 0; }
-      const int j = min(t * kKT + 16 * u + rt, L - 1);  // logical key (clamped)
+      const int j = min(t * kKT + ro, L - 1);  // logical key (clamped)
       tr.k[u] = ldg16(kh_row0 + (uint32_t)j * kHeadDim + col * 8);
       tr.v[u] = ldg16(P.v_cache + (size_t)phys * page_elems + ((uint32_t)(j & (kPageSize - 1)) * Hkv * kHeadDim + v_lane_off));
     }
@@ -391,8 +419,8 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
     load(ring[1], 1, pv1);
     load(ring[2], 2, pv2);
     pv_next = page_vec(3);
-    store_tile(ring[0], sm, 0, tid);
-    store_tile(ring[1], sm, 1, tid);
+    store_tile<H>(ring[0], sm, 0, tid);
+    store_tile<H>(ring[1], sm, 1, tid);
   }
   __syncthreads();
   f32x4 sc[kQT][2];
@@ -411,7 +439,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) pbt[ks] = pack_bf16(p[ks][0], p[ks][1], p[ks][2], p[ks][3]);
   };
-  auto step = [&](const int kt, TileRegs& to_load, TileRegs& to_store) {
+  auto step = [&](const int kt, TileRegs<H>& to_load, TileRegs<H>& to_store) {
     // ---- A: causal mask (tiles that reach past the block's first query), then S(kt+1) and
     // the softmax of S(kt)
     if ((kt + 1) * kKT > free_end) {
@@ -484,7 +512,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
     for (int t = 0; t < kQT; ++t)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) sc[t][ks] = sn[t][ks];
-    store_tile(to_store, sm, (kt + 2) % 3, tid);
+    store_tile<H>(to_store, sm, (kt + 2) % 3, tid);
     __syncthreads();
   };
   // whole rounds of the ring, then the last one or two tiles (no exit from inside a round)
@@ -532,17 +560,23 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(const PrefillPar
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   uint16_t* kh = (uint16_t*)p.workspace;
   if (p.num_indices > 0) {
-#ifndef PA_KEY_HEADS
-#define PA_KEY_HEADS 4
-#endif
-    if (PA_KEY_HEADS >= 4 && p.num_kv_heads % 4 == 0) launch_key_prologue<4>(p, kh, stream);
-    else if (PA_KEY_HEADS >= 2 && p.num_kv_heads % 2 == 0) launch_key_prologue<2>(p, kh, stream);
+    // two KV heads per wavefront: half the cos/sin reads, still about two wavefronts per SIMD
+    // (four heads per wavefront leave too few wavefronts to hide the load latency)
+    if (p.num_kv_heads % 2 == 0) launch_key_prologue<2>(p, kh, stream);
     else launch_key_prologue<1>(p, kh, stream);
   }
   const unsigned nqb = (unsigned)((p.q_len + kQBlock - 1) / kQBlock);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
   const unsigned grid = nqb * (unsigned)p.batch * (unsigned)p.num_kv_heads * nhg;
-  if (grid > 0) hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh);
+  if (grid > 0) {
+    // Two wavefronts per query head when the items fit one dispatch round (the longest-first
+    // pairing on compute units is in use and the longest items decide the time); one otherwise.
+    const unsigned U = nqb * (unsigned)p.batch;
+    if (grid > (unsigned)p.num_cus && grid <= 2u * (unsigned)p.num_cus && U <= (unsigned)kMaxRankUnits)
+      hipLaunchKernelGGL(attend_kernel<2>, dim3(grid), dim3(Shape<2>::kThreads), 0, stream, p, kh);
+    else
+      hipLaunchKernelGGL(attend_kernel<1>, dim3(grid), dim3(Shape<1>::kThreads), 0, stream, p, kh);
+  }
   return hipGetLastError();
 }
 
