@@ -105,6 +105,11 @@ pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, i
   if (split_policy != PA_SPLIT_DISABLED && split_policy != PA_SPLIT_FIXED) return PA_ERR_UNSUPPORTED;
   if (split_policy == PA_SPLIT_FIXED && (split_chunk_tokens < kPageSize || split_chunk_tokens % kPageSize != 0))
     return PA_ERR_UNSUPPORTED;
+  // the chunk states of a row are folded through an LDS table of kMaxFixedChunks entries
+  if (split_policy == PA_SPLIT_FIXED &&
+      ((long long)max_pages_per_row + split_chunk_tokens / kPageSize - 1) / (split_chunk_tokens / kPageSize) >
+          kMaxFixedChunks)
+    return PA_ERR_CAPACITY;
   if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_HEAD_RATIO;
   // positions stay int32 and the table below fits in memory
   if ((long long)max_pages_per_row * kPageSize + 1 > (1LL << 24)) return PA_ERR_CAPACITY;

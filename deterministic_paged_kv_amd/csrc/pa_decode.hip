@@ -680,13 +680,15 @@ __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 //   l <- l 2^(m - m') + l_c 2^(m_c - m'),  acc <- acc 2^(m - m') + acc_c 2^(m_c - m'),  m <- m'
 // (a state with m = -inf weighs 0), then out = acc / l and lse = (m + log2 l) ln 2.
 // One workgroup per (unit, query head h), one thread per output dimension d: the chunk states
-// are folded left to right, c = 0, 1, ..., in FP32.  The loads of a batch of chunks go out
-// together (the chunk maxima and sums are wave-uniform); only the arithmetic is sequential.
-constexpr int kFoldBatch = 8;
+// are folded left to right, c = 0, 1, ..., in FP32.  The chunk maxima and sums go to LDS first
+// (one load per thread); the accumulators then come in batches of kFoldBatch chunks whose
+// loads all go out before the batch is folded.  Only the arithmetic is sequential.
+constexpr int kFoldBatch = 32;
 __global__ __launch_bounds__(kHeadDim) void decode_fold_kernel(const DecodeParams P, int max_chunks,
                                                                const int32_t* __restrict__ poisons,
                                                                const float* __restrict__ states) {
 #pragma clang fp contract(off)
+  __shared__ float ml[kMaxFixedChunks][2];
   const int G = P.group;
   const int unit = blockIdx.x / G;
   const int h = blockIdx.x % G;
@@ -699,29 +701,29 @@ __global__ __launch_bounds__(kHeadDim) void decode_fold_kernel(const DecodeParam
     if (d == 0) P.lse[ri.head0 + h] = ri.bad ? __builtin_nanf("") : -__builtin_inff();
     return;
   }
-  const int nch = (ri.n + P.chunk_pages - 1) / P.chunk_pages;
+  const int nch = (ri.n + P.chunk_pages - 1) / P.chunk_pages;  // <= kMaxFixedChunks (checked at plan time)
   const size_t rec = (size_t)G * (2 + kHeadDim);
   const float* hs = states + (size_t)unit * max_chunks * rec + (size_t)h * (2 + kHeadDim);
   int poison = 0;
-  for (int c = d; c < nch; c += kHeadDim) poison |= poisons[unit * max_chunks + c];
+  for (int c = d; c < nch; c += kHeadDim) {
+    poison |= poisons[unit * max_chunks + c];
+    ml[c][0] = hs[(size_t)c * rec];
+    ml[c][1] = hs[(size_t)c * rec + 1];
+  }
   const bool poisoned = __syncthreads_or(poison) != 0;
   float m = -__builtin_inff(), l = 0.0f, a = 0.0f;
   for (int c0 = 0; c0 < nch; c0 += kFoldBatch) {
-    float mc[kFoldBatch], lc[kFoldBatch], ac[kFoldBatch];
+    float ac[kFoldBatch];
 #pragma unroll
-    for (int i = 0; i < kFoldBatch; ++i) {
-      const int c = min(c0 + i, nch - 1);
-      mc[i] = load_uniform_f32(hs + (size_t)c * rec, 0);
-      lc[i] = load_uniform_f32(hs + (size_t)c * rec, 1);
-      ac[i] = hs[(size_t)c * rec + 2 + d];
-    }
+    for (int i = 0; i < kFoldBatch; ++i) ac[i] = hs[(size_t)min(c0 + i, nch - 1) * rec + 2 + d];
 #pragma unroll
     for (int i = 0; i < kFoldBatch; ++i) {
       if (c0 + i >= nch) break;
-      const float mn = fmaxf(m, mc[i]);
+      const float mc = ml[c0 + i][0], lc = ml[c0 + i][1];
+      const float mn = fmaxf(m, mc);
       const float s0 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-      const float s1 = mc[i] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc[i] - mn);
-      l = l * s0 + lc[i] * s1;
+      const float s1 = mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - mn);
+      l = l * s0 + lc * s1;
       a = a * s0 + ac[i] * s1;
       m = mn;
     }

@@ -252,6 +252,10 @@ __device__ __forceinline__ void workgroup_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Most chunks one row may have under the fixed-chunk policy (the fold keeps their maxima and
+// sums in LDS).
+constexpr int kMaxFixedChunks = 4096;
+
 struct DecodeParams {
   int32_t batch, num_q_heads, num_kv_heads, group;
   int32_t num_pages, num_indices, max_pages_per_row, table_rows;

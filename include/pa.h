@@ -121,7 +121,9 @@ const char* pa_status_string(pa_status status);
  *   split_policy               PA_SPLIT_DISABLED or PA_SPLIT_FIXED (else
  *                              PA_ERR_UNSUPPORTED).
  *   split_chunk_tokens         PA_SPLIT_FIXED: the chunk size N, a positive multiple of 16
- *                              (else PA_ERR_UNSUPPORTED); ignored otherwise.
+ *                              (else PA_ERR_UNSUPPORTED); ignored otherwise.  A row may hold
+ *                              at most 4096 chunks: max_pages_per_row * 16 / N above 4096
+ *                              returns PA_ERR_CAPACITY.
  * Allocates device memory for the cos/sin table (max_pages_per_row * page_size + 1
  * positions, 512 bytes each) and synchronises the current device once.  The plan is
  * immutable afterwards and may serve several streams at once.  *plan_out is written

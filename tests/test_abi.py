@@ -73,6 +73,8 @@ def test_plan_fails_closed_on_host_arguments(lib):
     assert _plan(lib, eps=0.0) == -1
     assert _plan(lib, mp=1 << 21) == -3       # positions past 2^24
     assert _plan(lib, mb=1 << 23) == -3       # (row, KV head) units past 2^24
+    assert _plan(lib, split=1, chunk=16, mp=4097) == -3   # 4,097 chunks of one page per row
+    assert _plan(lib, split=1, chunk=32, mp=8193) == -3   # 4,097 chunks of two pages
     assert lib.pa_plan(16, 4, 128, 16, 1, 1, 1, 1e6, 1.0, 1e-6, 0, 0, None) == -1
 
 
