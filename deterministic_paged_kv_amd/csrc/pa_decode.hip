@@ -535,10 +535,16 @@ __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   VSlot& sv = svs[w];
-  const int s = blockIdx.x % kStreams;
+  // Placement.  When the grid is one dispatch round of two workgroups per compute unit,
+  // workgroups i and i + #CU share a compute unit: the second round takes the order backwards,
+  // so the longest rows' streams share compute units with the shortest rows'.
+  const int nwg = (int)gridDim.x;
+  int slot = (int)blockIdx.x;
+  if (nwg > P.num_cus && nwg <= 2 * P.num_cus && slot >= P.num_cus) slot = nwg - 1 - (slot - P.num_cus);
+  const int s = slot % kStreams;
   const int hgroups = P.num_kv_heads / HW;
-  const int hk = ((blockIdx.x / kStreams) % hgroups) * HW + w;
-  const int rank = blockIdx.x / (kStreams * hgroups);
+  const int hk = ((slot / kStreams) % hgroups) * HW + w;
+  const int rank = slot / (kStreams * hgroups);
   // Launch order: rows with more pages first, ties by row (up to 64 rows; beyond that, row
   // order).  The long rows' streams finish last; starting them first puts their first pages
   // at the head of the memory queue.  Only where a stream runs depends on it, not its bits.
