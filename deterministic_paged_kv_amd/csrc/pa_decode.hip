@@ -718,20 +718,34 @@ __global__ __launch_bounds__(kHeadDim) void decode_fold_kernel(const DecodeParam
   }
   const bool poisoned = __syncthreads_or(poison) != 0;
   float m = -__builtin_inff(), l = 0.0f, a = 0.0f;
-  for (int c0 = 0; c0 < nch; c0 += kFoldBatch) {
+  auto fold_one = [&](int c, float ac) {
+    const float mc = ml[c][0], lc = ml[c][1];
+    const float mn = fmaxf(m, mc);
+    const float s0 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float s1 = mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - mn);
+    l = l * s0 + lc * s1;
+    a = a * s0 + ac * s1;
+    m = mn;
+  };
+  // whole batches with no exit inside (their loads all go out first), then the last one
+  int c0 = 0;
+  for (; c0 + kFoldBatch <= nch; c0 += kFoldBatch) {
+    float ac[kFoldBatch];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) ac[i] = hs[(size_t)(c0 + i) * rec + 2 + d];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) fold_one(c0 + i, ac[i]);
+  }
+  if (c0 < nch) {
     float ac[kFoldBatch];
 #pragma unroll
     for (int i = 0; i < kFoldBatch; ++i) ac[i] = hs[(size_t)min(c0 + i, nch - 1) * rec + 2 + d];
+    // the loads are used here, before any exit, so none of them waits for the previous step
+    asm volatile("" ::"v"(ac[0]), "v"(ac[kFoldBatch / 2]), "v"(ac[kFoldBatch - 1]));
 #pragma unroll
     for (int i = 0; i < kFoldBatch; ++i) {
       if (c0 + i >= nch) break;
-      const float mc = ml[c0 + i][0], lc = ml[c0 + i][1];
-      const float mn = fmaxf(m, mc);
-      const float s0 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-      const float s1 = mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - mn);
-      l = l * s0 + lc * s1;
-      a = a * s0 + ac[i] * s1;
-      m = mn;
+      fold_one(c0 + i, ac[i]);
     }
   }
   float o = a / l;
