@@ -610,12 +610,8 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const DecodePa
   const int b = unit / P.num_kv_heads;
   const int hk = unit % P.num_kv_heads;
   const int d = threadIdx.x;
-  const RowInfo ri = row_info(P, b, hk);
-  if (ri.bad || ri.L == 0) {
-    P.out[(ri.head0 + h) * kHeadDim + d] = ri.bad ? (uint16_t)0x7FC0 : (uint16_t)0;
-    if (d == 0) P.lse[ri.head0 + h] = ri.bad ? __builtin_nanf("") : -__builtin_inff();
-    return;
-  }
+  // The states are read before the row's metadata is looked at (both go out together); the
+  // workspace holds a record for every unit, so the reads are in bounds for any row.
   const size_t rec = (size_t)G * (2 + kHeadDim);
   const float* hs = states + (size_t)unit * kStreams * rec + (size_t)h * (2 + kHeadDim);
   float mw[kStreams], lw[kStreams], a[kStreams];
@@ -626,6 +622,16 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const DecodePa
     lw[w] = load_uniform_f32(hs + (size_t)w * rec, 1);
     poison |= load_uniform(poisons, unit * kStreams + w);
     a[w] = hs[(size_t)w * rec + 2 + d];
+  }
+  const RowInfo ri = row_info(P, b, hk);
+  // keep the state reads ahead of the branch (the compiler would otherwise issue them after it)
+  asm volatile("" ::"v"(a[0]), "v"(a[kStreams - 1]));
+#pragma unroll
+  for (int w = 0; w < kStreams; ++w) asm volatile("" ::"s"(mw[w]), "s"(lw[w]));
+  if (ri.bad || ri.L == 0) {
+    P.out[(ri.head0 + h) * kHeadDim + d] = ri.bad ? (uint16_t)0x7FC0 : (uint16_t)0;
+    if (d == 0) P.lse[ri.head0 + h] = ri.bad ? __builtin_nanf("") : -__builtin_inff();
+    return;
   }
   combine_one(P, ri, h, d, poison != 0, [&](int w) { return mw[w]; }, [&](int w) { return lw[w]; },
               [&](int w) { return a[w]; });
