@@ -123,9 +123,25 @@ def device_rotation(base, i, device):
     return db
 
 
-def long_context_set(batch, length, device, seed=1004):
+LONG_POOL_PAGES = 40960
+
+
+def long_context_pool(device, seed=1004):
+    """The 40,960-page K/V pool of the long-context decode shape (Hkv=8), drawn on the device."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    shape = (LONG_POOL_PAGES, 16, 8, 128)
+    k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return k, v
+
+
+def long_context_set(batch, length, device, seed=1004, pool=None):
     """The long-context low-batch decode shape (Hq=32, Hkv=8, pages scattered over a 40,960-page
-    pool) with K/V/q drawn on the device (seeded); returns (host metadata, device batch)."""
+    pool) with K/V/q drawn on the device (seeded); returns (host metadata, device batch).
+    `pool` = (k_cache, v_cache) from long_context_pool reuses that pool's K/V."""
     import types
 
     import numpy as np
@@ -136,18 +152,15 @@ def long_context_set(batch, length, device, seed=1004):
 
     rng = np.random.Generator(np.random.PCG64(seed))
     lengths = np.full(batch, length, dtype=np.int64)
-    pool = 40960
-    order = rng.permutation(pool).astype(np.int32)
+    order = rng.permutation(LONG_POOL_PAGES).astype(np.int32)
     indptr, indices, last, keypos = workloads.csr_from_lengths(lengths, order)
     meta = types.SimpleNamespace(lengths=lengths, num_kv_heads=8, num_q_heads=32, batch=batch,
                                  nnz=int(indptr[-1]))
     db = DeviceBatch.__new__(DeviceBatch)
     db.host = None
     gen = torch.Generator(device=device)
-    gen.manual_seed(seed)
-    shape = (pool, 16, 8, 128)
-    db.k_cache = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
-    db.v_cache = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    gen.manual_seed(seed + 1)
+    db.k_cache, db.v_cache = pool if pool is not None else long_context_pool(device, seed)
     db.q = torch.randn((batch, 32, 1, 128), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
     db.kv_indptr, db.kv_indices, db.kv_last_page_len = t(indptr), t(indices), t(last)
@@ -469,6 +482,35 @@ def main():
                                  "frac": round(lalg / (l_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         result["long_context_decode"] = long_result
         del ldb
+        # The whole long-context grid: B in {1, 2, 4} x L in {32,768, 65,536, 131,072}, one pool.
+        print("[bench] timing the long-context grid", file=sys.stderr, flush=True)
+        pool = long_context_pool(device)
+        sweep = []
+        for lb in (1, 2, 4):
+            for ll in (32768, 65536, 131072):
+                smeta, sdb = long_context_set(lb, ll, device, pool=pool)
+                sout = torch.empty_like(sdb.q)
+                slse = torch.empty(sout.shape[:3], dtype=torch.float32, device=device)
+                salg = decode_bytes(smeta)
+                entry = {"batch": lb, "kv_len": ll, "algorithmic_bytes_per_call": salg}
+                for name, policy, chunk in (("split_disabled", pa.PA_SPLIT_DISABLED, 0),
+                                            ("split_fixed_1024", pa.PA_SPLIT_FIXED, 1024)):
+                    splan = pa.Plan(32, 8, max_batch=lb, max_q_len=1, max_pages_per_row=ll // 16, rms_eps=1e-6,
+                                    split_policy=policy, split_chunk_tokens=chunk)
+                    sws = pa.decode_workspace(splan, lb, device=device)
+
+                    def sstep(db, splan=splan, sws=sws):
+                        pa.decode(splan, *db.args(), out=sout, lse=slse, workspace=sws)
+
+                    _, s_launch = time_calls(sstep, [sdb], 20, 3, settle_ms=SETTLE_MS)
+                    entry[name] = {"ms_per_call": round(s_launch, 5),
+                                   "value": round(salg / (s_launch * 1e-3) / 1e9, 2), "unit": "GB/s",
+                                   "frac": round(salg / (s_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    splan.close()
+                sweep.append(entry)
+                del sdb
+        result["long_context_grid"] = sweep
+        del pool
 
     if not args.decode_only:
         print("[bench] timing prefill", file=sys.stderr, flush=True)
