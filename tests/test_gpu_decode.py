@@ -132,7 +132,8 @@ def test_long_context_decode_sampled(gpu, batch, length):
                   f"long decode B={batch} L={length}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "qwen3_8b", "batch8", "groups16", "kv1", "kv3", "kv6"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "qwen3_8b", "batch8", "groups16", "kv1", "kv3", "kv6",
+                                  "kv3x8", "rows80"])
 def test_multi_cu_schedule_is_bit_identical(gpu, name):
     """One wavefront per stream on separate compute units, then a combining kernel, gives the
     same bits as one workgroup per (row, KV head); the workspace needs no initialisation (it is
@@ -148,6 +149,12 @@ def test_multi_cu_schedule_is_bit_identical(gpu, name):
         b = workloads.invariance_batch(alone=False)
     elif name == "groups16":
         b = workloads.make_batch(42, [900, 77], q_len=1, num_q_heads=32, num_kv_heads=2, num_pages=128)
+    elif name == "kv3x8":  # 384 single-wavefront workgroups: one dispatch round, second one mirrored
+        b = workloads.make_batch(44, [530, 17, 0, 64, 300, 1, 900, 33], q_len=1, num_q_heads=6, num_kv_heads=3,
+                                 num_pages=256)
+    elif name == "rows80":  # more than 64 rows: launched in row order, no ranking
+        lengths = list(np.random.default_rng(45).integers(0, 300, 80))
+        b = workloads.make_batch(45, lengths, q_len=1, num_q_heads=8, num_kv_heads=2, num_pages=2048)
     else:  # KV head counts that take one (kv1, kv3) and two (kv6: 12 rows, 1,152 streams) KV heads
         # per workgroup of the multi-CU schedule
         hkv = int(name[2:])
@@ -161,3 +168,16 @@ def test_multi_cu_schedule_is_bit_identical(gpu, name):
         ws.fill_(0xFF)
         multi = run("decode", plan, db, workspace=ws)
         assert same_bits(unit, multi), name
+
+
+def test_decode_more_than_64_rows(gpu):
+    """80 rows (beyond the on-device ranking's 64) through the multi-CU schedule: oracle parity
+    on sampled rows."""
+    lengths = list(np.random.default_rng(46).integers(0, 600, 80))
+    b = workloads.make_batch(46, lengths, q_len=1, num_q_heads=8, num_kv_heads=2, num_pages=4096)
+    plan = make_plan(b)
+    ws = pa.decode_workspace(plan, b.batch)
+    out, lse = run("decode", plan, DeviceBatch(b), workspace=ws)
+    rows = [0, 17, 40, 63, 64, 79]
+    ref_out, ref_lse = oracle_ref(b, rows=rows)
+    assert_parity(out[rows], lse[rows], ref_out, ref_lse, f"80-row decode rows {rows}")

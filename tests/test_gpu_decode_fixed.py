@@ -109,3 +109,13 @@ def test_policy_errors(gpu):
     with pytest.raises(pa.PagedAttentionError) as e:
         pa.prefill(pplan, *DeviceBatch(pb).args())
     assert e.value.name == "PA_ERR_UNSUPPORTED"
+
+
+def test_most_chunks_per_row(gpu):
+    """4,096 one-page chunks in one row (the fold's limit): oracle parity on a few heads."""
+    b = workloads.make_batch(64, [4096 * 16], q_len=1, num_q_heads=8, num_kv_heads=2, num_pages=4096)
+    plan = make_plan(b, max_pages_per_row=4096, chunk_tokens=16)
+    out, lse = run_fixed(plan, DeviceBatch(b), b.batch)
+    heads = [0, 5]
+    ref_out, ref_lse = oracle_ref(b, q_heads=heads)
+    assert_parity(out[:, heads], lse[:, heads], ref_out, ref_lse, "fixed:16 with 4,096 chunks")

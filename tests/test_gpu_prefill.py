@@ -80,3 +80,30 @@ def test_prefill_row_alone_equals_row_in_batch(gpu):
     o_p, l_p = run("prefill", wide, DeviceBatch(workloads.permute_pages(alone, 3)))
     assert np.array_equal(o_p[0], o_full[r])
     assert np.array_equal(l_p[0].view(np.uint32), l_full[r].view(np.uint32))
+
+
+def test_two_wavefronts_per_head_shape(gpu):
+    """A batch whose work items fit one dispatch round (320 items) runs the two-wavefronts-per-
+    head shape: ragged query blocks (Sq = 300), a partial group of query heads (Hq = 24, Hkv = 4,
+    groups of 4 + 2), parity with the oracle and a row alone (one wavefront per head) bitwise
+    equal to the same row in the batch."""
+    full = workloads.make_batch(35, [300, 420, 555, 700], q_len=300, num_q_heads=24, num_kv_heads=4,
+                                num_pages=256, query_mode="prefill")
+    plan = make_plan(full)
+    o_full, l_full = run("prefill", plan, DeviceBatch(full))
+    ref_out, ref_lse = oracle_ref(full)
+    assert_parity(o_full, l_full, ref_out, ref_lse, "prefill, two wavefronts per head", kind="prefill")
+    r = 1
+    lo, hi = int(full.kv_indptr[r]), int(full.kv_indptr[r + 1])
+    alone = workloads.PagedBatch(**{**full.__dict__,
+                                    "q": full.q[r:r + 1].copy(),
+                                    "kv_indptr": np.array([0, hi - lo], np.int32),
+                                    "kv_indices": full.kv_indices[lo:hi].copy(),
+                                    "kv_last_page_len": full.kv_last_page_len[r:r + 1].copy(),
+                                    "cache_position": full.cache_position[r:r + 1].copy(),
+                                    "query_position_ids": full.query_position_ids[r:r + 1].copy(),
+                                    "key_position_ids": full.key_position_ids[lo * 16:hi * 16].copy(),
+                                    "lengths": full.lengths[r:r + 1].copy()})
+    o_a, l_a = run("prefill", make_plan(alone, max_pages_per_row=64), DeviceBatch(alone))
+    assert np.array_equal(o_a[0], o_full[r])
+    assert np.array_equal(l_a[0].view(np.uint32), l_full[r].view(np.uint32))
