@@ -174,7 +174,9 @@ def long_context_set(batch, length, device, seed=1004, pool=None):
 
 
 def time_calls(fn, sets, steps, warmup, settle_ms=0.0):
-    """Run fn(set) over the rotation; return (wall ms per step, mean per-launch event ms).
+    """Run fn(set) over the rotation; return (wall ms per step, ms per call from HIP events on
+    the launch stream around the timed calls; back-to-back calls, so this includes the short
+    gaps between them and is never below the kernels' own durations).
 
     After the `warmup` calls, further untimed calls run until `settle_ms` of wall time has
     passed, so that a workload timed right after another one is measured at its steady clock
@@ -192,17 +194,20 @@ def time_calls(fn, sets, steps, warmup, settle_ms=0.0):
         if i % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # One event pair around the whole timed region, on the stream the calls are launched on:
+    # an event pair around every call would add several microseconds per decode step (each
+    # timing event is a packet of its own that waits for the work before it).
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         fn(sets[i % len(sets)])
-        ev[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    launch_ms = start.elapsed_time(end) / steps
     return wall_ms, launch_ms
 
 
@@ -367,8 +372,8 @@ def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--profile-copy", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="skip prefill and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
