@@ -30,15 +30,19 @@ def test_tiny_decode_parity(gpu):
     check_full(workloads.tiny_decode(), "tiny decode")
 
 
-def test_qwen3_8b_decode_parity_sampled(gpu):
-    """Full Qwen3-8B per-GPU shape (B=32, Hq=16, Hkv=4, L ~ U[512, 4096]); oracle on sampled rows."""
+@pytest.mark.parametrize("schedule", ["unit", "multi_cu"])
+def test_qwen3_8b_decode_parity_sampled(gpu, schedule):
+    """Full Qwen3-8B per-GPU shape (B=32, Hq=16, Hkv=4, L ~ U[512, 4096]); oracle on sampled rows.
+    Both schedules: one workgroup per (row, KV head), and the multi-CU one (stream kernel +
+    combine, the launch configuration the benchmark times)."""
     b = workloads.qwen3_8b_decode()
     db = DeviceBatch(b)
     plan = make_plan(b, max_pages_per_row=256)
-    out, lse = run("decode", plan, db)
+    ws = pa.decode_workspace(plan, b.batch) if schedule == "multi_cu" else None
+    out, lse = run("decode", plan, db, workspace=ws)
     rows = [0, 5, 17, 31, int(np.argmax(b.lengths)), int(np.argmin(b.lengths))]
     ref_out, ref_lse = oracle_ref(b, rows=rows)
-    assert_parity(out[rows], lse[rows], ref_out, ref_lse, "qwen3-8b decode rows %s" % rows)
+    assert_parity(out[rows], lse[rows], ref_out, ref_lse, f"qwen3-8b decode ({schedule}) rows {rows}")
     # every row finite
     assert np.all(np.isfinite(lse))
 
@@ -88,8 +92,9 @@ def test_decode_bitwise_repeat_and_page_permutation(gpu):
 
 def test_batch_and_plan_width_invariance(gpu):
     """The 1,500-token row (Hq=32, Hkv=8): alone under 128- and 256-page plans, as row 3 of a batch of
-    8 under 512- and 1024-page plans, and alone with its pages permuted: bitwise equal out and LSE,
-    each run repeated 10 times; and within tolerance of the oracle."""
+    8 under 512- and 1024-page plans, and alone with its pages permuted, through both schedules
+    (one workgroup per unit; stream kernel + combine): bitwise equal out and LSE, each run
+    repeated; and within tolerance of the oracle."""
     alone = workloads.invariance_batch(alone=True)
     full = workloads.invariance_batch(alone=False)
     r = workloads.INVARIANCE_ROW_INDEX
@@ -110,6 +115,19 @@ def test_batch_and_plan_width_invariance(gpu):
         for _ in range(10):
             o, l = run("decode", plan, db_full)
             results.append((f"batch8 w={width}", o[r], l[r]))
+    # the same row through the multi-CU schedule (stream kernel + combine)
+    for width in (128, 256):
+        plan = make_plan(alone, max_pages_per_row=width)
+        ws = pa.decode_workspace(plan, 1)
+        for _ in range(3):
+            o, l = run("decode", plan, db_alone, workspace=ws)
+            results.append((f"alone multi-CU w={width}", o[0], l[0]))
+    for width in (512, 1024):
+        plan = make_plan(full, max_pages_per_row=width, max_batch=8)
+        ws = pa.decode_workspace(plan, 8)
+        for _ in range(3):
+            o, l = run("decode", plan, db_full, workspace=ws)
+            results.append((f"batch8 multi-CU w={width}", o[r], l[r]))
     ref_label, ref_o, ref_l = results[0]
     for label, o, l in results[1:]:
         assert np.array_equal(o, ref_o), f"out differs: {label} vs {ref_label}"
@@ -118,18 +136,20 @@ def test_batch_and_plan_width_invariance(gpu):
     assert_parity(ref_o[None], ref_l[None], ref_out, ref_lse, "1500-token row")
 
 
-@pytest.mark.parametrize("batch,length", [(1, 131072), (2, 32768)])
-def test_long_context_decode_sampled(gpu, batch, length):
+@pytest.mark.parametrize("batch,length,schedule", [(1, 131072, "unit"), (1, 131072, "multi_cu"),
+                                                    (2, 32768, "unit"), (4, 32768, "multi_cu")])
+def test_long_context_decode_sampled(gpu, batch, length, schedule):
     """Long-context low-batch decode (Hq=32, Hkv=8): oracle on one row and two heads per KV group edge."""
     pages = batch * length // 16
     b = workloads.long_decode(batch, length, num_pages=pages + 512)
     db = DeviceBatch(b)
     plan = make_plan(b, max_pages_per_row=length // 16)
-    out, lse = run("decode", plan, db)
+    ws = pa.decode_workspace(plan, batch) if schedule == "multi_cu" else None
+    out, lse = run("decode", plan, db, workspace=ws)
     heads = [0, 3, 31]
     ref_out, ref_lse = oracle_ref(b, rows=[batch - 1], q_heads=heads)
     assert_parity(out[[batch - 1]][:, heads], lse[[batch - 1]][:, heads], ref_out, ref_lse,
-                  f"long decode B={batch} L={length}")
+                  f"long decode B={batch} L={length} ({schedule})")
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "qwen3_8b", "batch8", "groups16", "kv1", "kv3", "kv6",
