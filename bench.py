@@ -13,7 +13,8 @@ Printed (one JSON line): value = algorithmic bytes per step / time per step, whe
 algorithmic bytes are the K and V bytes of every cached key of every KV head plus q, out,
 lse and the CSR metadata the kernel reads (the RoPE table and norm weights are constants
 served from cache and are not counted).  The roofline entry divides the same bytes by the
-decode kernel's average duration, measured with HIP events recorded on the launch stream.
+decode call's average time from one pair of HIP events recorded on the launch stream around
+the timed calls.
 The chunked-prefill workload (B=4 x 512-query chunks after prefixes 0/1024/2048/3584,
 Hq=32, Hkv=8) is reported alongside with its algorithmic FLOPs (QK^T and PV over the
 causally visible pairs) per call.  The full-prefill backward
@@ -21,7 +22,7 @@ causally visible pairs) per call.  The full-prefill backward
 FLOPs (five products over the causal pairs).  The CPU oracle is timed on a bounded sample on
 the host.
 
-Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
+Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 2000]
        python bench.py --profile-copy     # plain copy of a known size, for counter scaling
        python bench.py --ingest-counters FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
            # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results of the decode run and of the copy
