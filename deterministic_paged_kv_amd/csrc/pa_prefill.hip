@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256 * H) __attribute__((amdgpu_waves_per_eu(2 * H, 
   for (int t = 0; t < kQBlock / 16; ++t) {
     const int i = qb * kQBlock + 16 * t + r;
     qp_blk[t] = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
-    if (qp_blk[t] >= P.table_rows) { poison = 1; qp_blk[t] = -1; }
+    if (i < Sq && (qp_blk[t] < 0 || qp_blk[t] >= P.table_rows)) { poison = 1; qp_blk[t] = -1; }
   }
   int qp[kQT];
   int i_of[kQT];

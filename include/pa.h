@@ -43,10 +43,13 @@
  *   - Errors are negative pa_status codes; nothing falls back to another algorithm.
  *   - pa_decode / pa_prefill never allocate, never synchronise and never read device
  *     memory from the host, so they may be recorded into a HIP graph.  They check host
- *     scalars only.  The kernels additionally bounds-check every page index, row length
- *     and position they read; a row whose metadata is out of range gets NaN in out and
- *     lse (the launch still succeeds).  Call pa_validate_metadata first to get a precise
- *     error instead.
+ *     scalars only.  The kernels additionally bounds-check every page index, row extent,
+ *     last_page_len and query position they read, and never access memory through an
+ *     out-of-range value: a row whose indptr extent or last_page_len is out of range gets
+ *     NaN in all its out and lse; an out-of-range page index or query position gets NaN in
+ *     every output computed from it (decode: the whole row; prefill: each block of 32
+ *     queries that reads that page or holds that query).  The launch still succeeds.  Call
+ *     pa_validate_metadata first to get a precise error instead.
  */
 #ifndef PA_H_
 #define PA_H_
