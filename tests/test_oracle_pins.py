@@ -442,3 +442,97 @@ def test_paged_canaries_never_reach_the_result():
     out, lse = _run(b)
     assert np.all(np.isfinite(lse))
     assert not np.any(np.isnan(oracle.f32_from_bf16_bits(out)))
+
+
+# ---------------------------------------------------------------------------------------------
+# The prologue's composition at non-zero positions.  "WS2 Attention Cross-Configuration
+# Integration", section "H100 Attention input and projection boundary": inside the attention
+# boundary the order is Q/K RMSNorm, then RoPE; "[WS2][PR7][Attention] Add FlashInfer
+# RoPE-fused paged attention scaffold", section "Scope": both sides share the post-RoPE BF16
+# boundary.  RMSNorm's scale factor is rotation-invariant, so what these pins catch is where
+# the per-dimension weight sits: applied before the rotation (correct), after it, or the two
+# operations swapped, all differ as soon as w_i != w_{i+64}.
+# ---------------------------------------------------------------------------------------------
+
+def _independent_prologue64(x_bits, w, pos):
+    """RMSNorm by torch's float64 rms_norm (with the weight), then the rotation as a complex
+    product (y_i + i y_{i+64}) * exp(i pos theta^(-2i/128)); float64, no rounding."""
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    if w is not None:
+        x = torch.nn.functional.rms_norm(x, (D,), torch.from_numpy(np.asarray(w, np.float64)), 1e-6)
+    freq = torch.tensor([1e6 ** (-2.0 * i / D) for i in range(D // 2)], dtype=torch.float64)
+    ang = torch.from_numpy(np.asarray(pos, np.float64))[:, None] * freq[None, :]
+    z = torch.complex(x[:, :D // 2], x[:, D // 2:]) * torch.polar(torch.ones_like(ang), ang)
+    return torch.cat([z.real, z.imag], dim=-1).numpy()
+
+
+def _bf16_half_ulp(v):
+    """Half a BF16 ulp at |v| (the rounding error the post-RoPE cast may add)."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return 0.5 * np.exp2(np.floor(np.log2(a)) - 7)
+
+
+@pytest.mark.parametrize("with_weight", [True, False])
+def test_prologue_matches_independent_norm_then_rotation(with_weight):
+    """oracle.prologue at random positions up to 131,071 equals the independent float64
+    construction rounded to BF16: within half a BF16 ulp plus FP32 evaluation slack."""
+    rng = _rng(31)
+    n = 600
+    bits = workloads.bf16_normal(rng, (n, D))
+    w = rng.uniform(0.5, 1.5, D).astype(np.float32) if with_weight else None
+    pos = np.concatenate([rng.integers(1, 131072, n - 4), [1, 4095, 65536, 131071]])
+    got = oracle.prologue(bits, w, pos, 1e-6, 1e6, 1.0).astype(np.float64)
+    ref = _independent_prologue64(bits, w, pos)
+    # FP32 slack: the prologue's few float32 roundings and the float32 cos/sin, relative to
+    # the pair's magnitude
+    pair = np.sqrt(ref[:, :64] ** 2 + ref[:, 64:] ** 2)
+    slack = 2.0 ** -20 * np.concatenate([pair, pair], axis=-1)
+    assert np.all(np.abs(got - ref) <= _bf16_half_ulp(ref) + slack)
+    # the planted mistakes: the weight after the rotation, and the two operations swapped
+    if with_weight:
+        x = oracle.f32_from_bf16_bits(bits)
+        c, s = oracle.rope_cos_sin(pos, D, 1e6, 1.0)
+        w_after = oracle.bf16_round(oracle.rope_fp32(oracle.rmsnorm_fp32(x, np.ones(D, np.float32), 1e-6), c, s) * w)
+        swapped = oracle.bf16_round(oracle.rmsnorm_fp32(oracle.rope_fp32(x, c, s), w, 1e-6))
+        for wrong in (w_after, swapped):
+            assert np.max(np.abs(wrong.astype(np.float64) - ref)) > 0.05
+
+
+def test_prologue_one_hot_closed_form():
+    """x = a e_i (one-hot at dim i < 64) at position p: RMSNorm gives y_i = w_i a r with
+    r = 1/sqrt(a^2/128 + eps) and zero elsewhere, and the rotation sends it to dims i and i+64
+    as (y_i cos, y_i sin) of frequency i.  The weight of dim i+64 must not appear."""
+    rng = _rng(32)
+    w = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    for i, p, a in ((0, 1, 1.5), (7, 1000, -2.0), (40, 77777, 0.75), (63, 131071, 3.0)):
+        x = np.zeros((1, D), np.float32)
+        x[0, i] = a
+        bits = oracle.bf16_bits_from_f32(x)
+        got = oracle.prologue(bits, w, np.array([p]), 1e-6, 1e6, 1.0)[0].astype(np.float64)
+        r = 1.0 / math.sqrt(a * a / D + 1e-6)
+        ang = p * 1e6 ** (-2.0 * i / D)
+        want_i = float(w[i]) * a * r * math.cos(ang)
+        want_j = float(w[i]) * a * r * math.sin(ang)
+        for got_v, want in ((got[i], want_i), (got[i + 64], want_j)):
+            assert abs(got_v - want) <= _bf16_half_ulp(np.array(want)) + 2.0 ** -20 * abs(a * r * 1.5)
+        assert np.count_nonzero(got) == 2 - (got[i + 64] == 0) - (got[i] == 0)
+
+
+def test_backward_exact_prologue_matches_independent_construction():
+    """oracle/backward.py's exact-arithmetic prologue (the function its gradients
+    differentiate) against the same independent float64 construction, at non-zero positions.
+    Its cos/sin are the float32 ones, so agreement is to ~2^-23 of the pair magnitude."""
+    from oracle.backward import _norm_rope_forward
+
+    rng = _rng(33)
+    n = 200
+    bits = workloads.bf16_normal(rng, (n, D))
+    w = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    pos = rng.integers(1, 131072, n)
+    x = oracle.f32_from_bf16_bits(bits).astype(np.float64)
+    c, s = (a.astype(np.float64) for a in oracle.rope_cos_sin(pos, D, 1e6, 1.0))
+    for wt in (w, None):
+        got, _ = _norm_rope_forward(x, None if wt is None else wt.astype(np.float64), c, s, 1e-6)
+        ref = _independent_prologue64(bits, wt, pos)
+        pair = np.sqrt(ref[:, :64] ** 2 + ref[:, 64:] ** 2)
+        np.testing.assert_array_less(np.abs(got - ref), 2.0 ** -21 * np.concatenate([pair, pair], -1) + 1e-300)
