@@ -35,10 +35,12 @@ SIGNATURES = {
     "pa_plan_destroy": (_i32, [_p]),
     "pa_validate_metadata": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                                     ctypes.POINTER(ValidationReport)]),
-    "pa_decode": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "pa_decode": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
+                         _p]),
     "pa_decode_workspace_size": (_i32, [_p, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill_workspace_size": (_i32, [_p, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
-    "pa_prefill": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "pa_prefill": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
+                          _p]),
     "pa_build_csr": (_i32, [_i32, _i32, _p, _p, _p, _p, _p, _p]),
     "pa_prefill_backward_workspace_size": (_i32, [_p, _i32, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill_backward": (_i32, [_p, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -155,7 +157,8 @@ class Plan:
             pass
 
 
-def _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, query_position_ids):
+def _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, cache_position,
+              query_position_ids, key_position_ids):
     import torch
 
     _need(q, "q", torch.bfloat16, 4)
@@ -169,8 +172,11 @@ def _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len
     _need(kv_indptr, "kv_indptr", torch.int32, shape=(B + 1,))
     _need(kv_indices, "kv_indices", torch.int32, 1)
     _need(kv_last_page_len, "kv_last_page_len", torch.int32, shape=(B,))
+    _need(cache_position, "cache_position", torch.int32, shape=(B, Sq))
     _need(query_position_ids, "query_position_ids", torch.int32, shape=(B, Sq))
-    return B, Sq, int(k_cache.shape[0]), int(kv_indices.shape[0])
+    nnz = int(kv_indices.shape[0])
+    _need(key_position_ids, "key_position_ids", torch.int32, shape=(nnz * PAGE_SIZE,))
+    return B, Sq, int(k_cache.shape[0]), nnz
 
 
 def validate_metadata(plan: Plan, *, batch: int, q_len: int, num_pages: int, kv_indptr, kv_indices,
@@ -210,8 +216,9 @@ def decode_workspace(plan: Plan, batch: int, device="cuda"):
     return torch.empty(decode_workspace_size(plan, batch), dtype=torch.uint8, device=device)
 
 
-def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, query_position_ids,
-           q_norm_weight=None, k_norm_weight=None, out=None, lse=None, workspace=None, stream=None):
+def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, cache_position,
+           query_position_ids, key_position_ids, q_norm_weight=None, k_norm_weight=None, out=None, lse=None,
+           workspace=None, stream=None):
     """pa_decode.  q [B, Hq, 1, 128] bf16; returns (out [B, Hq, 1, 128] bf16, lse [B, Hq, 1] fp32).
 
     workspace: None for the one-workgroup-per-(row, KV head) schedule, or a uint8 device tensor
@@ -219,7 +226,7 @@ def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_
     import torch
 
     B, Sq, num_pages, nnz = _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len,
-                                      query_position_ids)
+                                      cache_position, query_position_ids, key_position_ids)
     if q_norm_weight is not None:
         _need(q_norm_weight, "q_norm_weight", torch.float32, shape=(HEAD_DIM,))
     if k_norm_weight is not None:
@@ -235,7 +242,8 @@ def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_
         _need(workspace, "workspace", torch.uint8, 1)
         ws_bytes = int(workspace.numel())
     _check(load().pa_decode(plan.handle, B, Sq, num_pages, nnz, _ptr(kv_indptr), _ptr(kv_indices),
-                            _ptr(kv_last_page_len), _ptr(query_position_ids), _ptr(q), _ptr(k_cache),
+                            _ptr(kv_last_page_len), _ptr(cache_position), _ptr(query_position_ids),
+                            _ptr(key_position_ids), _ptr(q), _ptr(k_cache),
                             _ptr(v_cache), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(out), _ptr(lse),
                             _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
     return out, lse
@@ -248,13 +256,14 @@ def prefill_workspace_size(plan: Plan, batch: int, q_len: int, num_indices: int)
     return int(n.value)
 
 
-def prefill(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, query_position_ids,
-            q_norm_weight=None, k_norm_weight=None, out=None, lse=None, workspace=None, stream=None):
+def prefill(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, cache_position,
+            query_position_ids, key_position_ids, q_norm_weight=None, k_norm_weight=None, out=None, lse=None,
+            workspace=None, stream=None):
     """pa_prefill.  q [B, Hq, Sq, 128] bf16; returns (out [B, Hq, Sq, 128] bf16, lse [B, Hq, Sq] fp32)."""
     import torch
 
     B, Sq, num_pages, nnz = _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len,
-                                      query_position_ids)
+                                      cache_position, query_position_ids, key_position_ids)
     if q_norm_weight is not None:
         _need(q_norm_weight, "q_norm_weight", torch.float32, shape=(HEAD_DIM,))
     if k_norm_weight is not None:
@@ -269,7 +278,8 @@ def prefill(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page
         workspace = torch.empty(prefill_workspace_size(plan, B, Sq, nnz), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8, 1)
     _check(load().pa_prefill(plan.handle, B, Sq, num_pages, nnz, _ptr(kv_indptr), _ptr(kv_indices),
-                             _ptr(kv_last_page_len), _ptr(query_position_ids), _ptr(q), _ptr(k_cache),
+                             _ptr(kv_last_page_len), _ptr(cache_position), _ptr(query_position_ids),
+                             _ptr(key_position_ids), _ptr(q), _ptr(k_cache),
                              _ptr(v_cache), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(out), _ptr(lse),
                              _ptr(workspace), int(workspace.numel()), _stream(stream)), "pa_prefill")
     return out, lse

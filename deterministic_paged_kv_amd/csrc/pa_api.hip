@@ -56,15 +56,17 @@ std::vector<float> rope_table(int rows, double theta, double scale) {
 // Host-scalar checks shared by pa_decode and pa_prefill.
 pa_status check_launch(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
                        const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
-                       const int32_t* query_position_ids, const void* q, const void* k_cache,
+                       const int32_t* cache_position, const int32_t* query_position_ids,
+                       const int32_t* key_position_ids, const void* q, const void* k_cache,
                        const void* v_cache, const void* out, const float* lse) {
   if (!plan_ok(plan)) return PA_ERR_INVALID_ARGUMENT;
   if (batch < 0 || q_len < 1 || num_pages < 1 || num_indices < 0) return PA_ERR_INVALID_ARGUMENT;
   if (batch > plan->max_batch || q_len > plan->max_q_len) return PA_ERR_CAPACITY;
   if (batch == 0) return PA_OK;
-  if (!kv_indptr || !kv_last_page_len || !query_position_ids || !q || !k_cache || !v_cache || !out || !lse)
+  if (!kv_indptr || !kv_last_page_len || !cache_position || !query_position_ids || !q || !k_cache || !v_cache ||
+      !out || !lse)
     return PA_ERR_INVALID_ARGUMENT;
-  if (num_indices > 0 && !kv_indices) return PA_ERR_INVALID_ARGUMENT;
+  if (num_indices > 0 && (!kv_indices || !key_position_ids)) return PA_ERR_INVALID_ARGUMENT;
   return check_device(plan);
 }
 
@@ -242,13 +244,20 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
   return finish(st);
 }
 
-pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
-                    const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
-                    const int32_t* query_position_ids, const void* q, const void* k_cache, const void* v_cache,
-                    const float* q_norm_weight, const float* k_norm_weight, void* out, float* lse,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Body of pa_decode: `workspace` is the caller's buffer, or NULL (one workgroup per unit).
+pa_status decode_call(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
+                      const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                      const int32_t* cache_position, const int32_t* query_position_ids,
+                      const int32_t* key_position_ids, const void* q, const void* k_cache, const void* v_cache,
+                      const float* q_norm_weight, const float* k_norm_weight, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_launch(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices,
-                              kv_last_page_len, query_position_ids, q, k_cache, v_cache, out, lse);
+                              kv_last_page_len, cache_position, query_position_ids, key_position_ids, q,
+                              k_cache, v_cache, out, lse);
   if (st != PA_OK || batch == 0) return st;
   if (q_len != 1) return PA_ERR_INVALID_ARGUMENT;
   const size_t need = decode_workspace_bytes(batch, plan->num_kv_heads, plan->group, plan->split_chunk_pages,
@@ -267,7 +276,9 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
   p.indptr = kv_indptr;
   p.indices = kv_indices;
   p.last_page_len = kv_last_page_len;
+  p.cache_position = cache_position;
   p.qpos = query_position_ids;
+  p.kpos = key_position_ids;
   p.q = (const uint16_t*)q;
   p.k_cache = (const uint16_t*)k_cache;
   p.v_cache = (const uint16_t*)v_cache;
@@ -280,6 +291,21 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
   p.chunk_pages = plan->split_chunk_pages;
   p.num_cus = plan->num_cus;
   return launch_decode(p, workspace, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
+                    const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                    const int32_t* cache_position, const int32_t* query_position_ids,
+                    const int32_t* key_position_ids, const void* q, const void* k_cache, const void* v_cache,
+                    const float* q_norm_weight, const float* k_norm_weight, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices, kv_last_page_len,
+                     cache_position, query_position_ids, key_position_ids, q, k_cache, v_cache, q_norm_weight,
+                     k_norm_weight, out, lse, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_workspace_size(pa_plan_t plan, int32_t batch, size_t* bytes) {
@@ -300,11 +326,13 @@ pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len
 
 pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
                      const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
-                     const int32_t* query_position_ids, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_position, const int32_t* query_position_ids,
+                     const int32_t* key_position_ids, const void* q, const void* k_cache, const void* v_cache,
                      const float* q_norm_weight, const float* k_norm_weight, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_launch(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices,
-                              kv_last_page_len, query_position_ids, q, k_cache, v_cache, out, lse);
+                              kv_last_page_len, cache_position, query_position_ids, key_position_ids, q,
+                              k_cache, v_cache, out, lse);
   if (st != PA_OK || batch == 0) return st;
   if (plan->split_policy != PA_SPLIT_DISABLED) return PA_ERR_UNSUPPORTED;  // prefill: one pass per row only
   const size_t need = prefill_workspace_bytes(plan->num_q_heads, plan->num_kv_heads, batch, q_len, num_indices);
@@ -322,7 +350,9 @@ pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_p
   p.indptr = kv_indptr;
   p.indices = kv_indices;
   p.last_page_len = kv_last_page_len;
+  p.cache_position = cache_position;
   p.qpos = query_position_ids;
+  p.kpos = key_position_ids;
   p.q = (const uint16_t*)q;
   p.k_cache = (const uint16_t*)k_cache;
   p.v_cache = (const uint16_t*)v_cache;

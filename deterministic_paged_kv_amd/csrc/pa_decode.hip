@@ -67,21 +67,24 @@ struct RowInfo {
   size_t head0;  // index of the group's first query head in [B * Hq]
 };
 
-// From the row's four metadata values (indptr[b], indptr[b + 1], last_page_len[b], qpos[b]).
-__device__ __forceinline__ RowInfo row_info_of(const DecodeParams& P, int b, int hk, int p0, int p1, int lpl, int qp) {
+// From the row's five metadata values (indptr[b], indptr[b + 1], last_page_len[b], qpos[b],
+// cache_position[b]).  A cache position that differs from the query position breaks the rule
+// cache_position == query_position_ids and makes the row bad, like an out-of-range value.
+__device__ __forceinline__ RowInfo row_info_of(const DecodeParams& P, int b, int hk, int p0, int p1, int lpl, int qp,
+                                               int cp) {
   RowInfo ri;
   ri.p0 = p0;
   ri.n = p1 - ri.p0;
   ri.qp = qp;
   ri.bad = ri.p0 < 0 || ri.n < 0 || p1 > P.num_indices || ri.n > P.max_pages_per_row || ri.qp < 0 ||
-           ri.qp >= P.table_rows || (ri.n > 0 && (lpl < 1 || lpl > kPageSize));
+           ri.qp >= P.table_rows || cp != qp || (ri.n > 0 && (lpl < 1 || lpl > kPageSize));
   ri.L = (ri.n > 0 && !ri.bad) ? (ri.n - 1) * kPageSize + lpl : 0;
   ri.head0 = (size_t)b * P.num_q_heads + (size_t)hk * P.group;
   return ri;
 }
 
 __device__ __forceinline__ RowInfo row_info(const DecodeParams& P, int b, int hk) {
-  return row_info_of(P, b, hk, P.indptr[b], P.indptr[b + 1], P.last_page_len[b], P.qpos[b]);
+  return row_info_of(P, b, hk, P.indptr[b], P.indptr[b + 1], P.last_page_len[b], P.qpos[b], P.cache_position[b]);
 }
 
 // Output of a row with no keys (0, -inf) or with out-of-range metadata (NaN, NaN).
@@ -366,6 +369,15 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
   };
   // position of key r of walk step t (steps past the end read the last page's)
   auto key_pos = [&](int t) { return min(first + t * stride, n - 1) * kPageSize + r; };
+  // key_position_ids entry of key r of walk step t: the rotation above uses the logical index,
+  // which is what the entry must hold; it is loaded with the page and checked when the page is
+  // scored (live keys of the walk's own steps only)
+  auto kpos_of = [&](int t) { return P.kpos[(size_t)p0 * kPageSize + key_pos(t)]; };
+  auto check_kpos = [&](int t, int kp) {
+    const int j = key_pos(t);
+    const bool wrong = t < steps && j < L && kp != j;
+    st[0].poison |= __builtin_amdgcn_ballot_w64(wrong) != 0 ? 1 : 0;
+  };
 
   // q^ of the group's heads in the operand layout (vector r = head r < G), before any page
   // load is issued: when every wavefront of the grid starts at once, the query's few bytes
@@ -375,8 +387,12 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
   __builtin_amdgcn_sched_barrier(0);
 
   PageIn in[R];
+  int kp[R];
 #pragma unroll
-  for (int k = 0; k < R; ++k) issue_page(in[k], P, phys_at(k), hk, r, g);
+  for (int k = 0; k < R; ++k) {
+    issue_page(in[k], P, phys_at(k), hk, r, g);
+    kp[k] = kpos_of(k);
+  }
   csrc.start(P, key_pos);
 
 #pragma unroll
@@ -394,6 +410,7 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
     StreamState& sk = st[k % NS];
     const Scored sc =
         score_page(in[k], csrc.template get<k>(), first + t * stride, sk, qop, kw, knorm, P.eps, L, qp, r, g, sv);
+    check_kpos(t, kp[k]);
     csrc.template after_score<k>(P, key_pos, t);
     // refill the slot with step t + R; a new block of page numbers is due when t + R
     // enters the next one
@@ -407,6 +424,7 @@ __device__ __forceinline__ void run_walk(const DecodeParams& P, const RowInfo& r
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
     issue_page(in[k], P, phys_at(u), hk, r, g);
+    kp[k] = kpos_of(u);
     wave_lds_sync();
     pv_page(sc, sk, r, g, sv);
     wave_lds_sync();
@@ -558,6 +576,7 @@ __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int ip1 = lv ? P.indptr[lane + 1] : 0;
     const int lpl = lv ? P.last_page_len[lane] : 0;
     const int qpl = lv ? P.qpos[lane] : 0;
+    const int cpl = lv ? P.cache_position[lane] : 0;
     const int my = lv ? ip1 - ip0 : -1;
     int rk = 0;
     for (int j = 0; j < P.batch; ++j) {
@@ -567,7 +586,8 @@ __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const unsigned long long hit = __builtin_amdgcn_ballot_w64(lv && rk == rank);
     b = hit ? (int)__builtin_ctzll(hit) : rank;
     ri = row_info_of(P, b, hk, __builtin_amdgcn_readlane(ip0, b), __builtin_amdgcn_readlane(ip1, b),
-                     __builtin_amdgcn_readlane(lpl, b), __builtin_amdgcn_readlane(qpl, b));
+                     __builtin_amdgcn_readlane(lpl, b), __builtin_amdgcn_readlane(qpl, b),
+                     __builtin_amdgcn_readlane(cpl, b));
   } else {
     ri = row_info(P, b, hk);
   }

@@ -262,7 +262,9 @@ struct DecodeParams {
   const int32_t* indptr;
   const int32_t* indices;
   const int32_t* last_page_len;
-  const int32_t* qpos;
+  const int32_t* cache_position;  // [B, Sq]; must equal qpos
+  const int32_t* qpos;            // [B, Sq]
+  const int32_t* kpos;            // [nnz * 16]; key j of row b at indptr[b] * 16 + j, must be j
   const uint16_t* q;
   const uint16_t* k_cache;
   const uint16_t* v_cache;
@@ -304,7 +306,9 @@ struct PrefillParams {
   const int32_t* indptr;
   const int32_t* indices;
   const int32_t* last_page_len;
-  const int32_t* qpos;
+  const int32_t* cache_position;  // [B, Sq]; must equal qpos
+  const int32_t* qpos;            // [B, Sq]
+  const int32_t* kpos;            // [nnz * 16]; key j of row b at indptr[b] * 16 + j, must be j
   const uint16_t* q;
   const uint16_t* k_cache;
   const uint16_t* v_cache;

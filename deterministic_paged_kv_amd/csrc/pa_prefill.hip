@@ -78,6 +78,16 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// True iff kv_indptr[0..b+1] is non-decreasing.  Rows whose extents lie in such a prefix
+// never share an index slot (and so never share k^ workspace rows); a row past a decrease
+// could overlap another row's extent and is treated as bad by both kernels.  Every thread of
+// the workgroup must call it (it ends with a workgroup-wide AND).
+__device__ __forceinline__ bool indptr_prefix_monotone(const int32_t* indptr, int b, int tid, int nthreads) {
+  int ok = 1;
+  for (int i = tid; i <= b; i += nthreads) ok &= indptr[i] <= indptr[i + 1] ? 1 : 0;
+  return __syncthreads_and(ok) != 0;
+}
+
 // ---------------------------------------------------------------------------------------
 // 1. k^ for every cached key
 // ---------------------------------------------------------------------------------------
@@ -95,7 +105,8 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
   const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
   const int n = p1 - p0;
   const int lpl = P.last_page_len[b];
-  const bool row_ok = p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && lpl >= 1 &&
+  const bool mono = indptr_prefix_monotone(P.indptr, b, threadIdx.x, blockDim.x);
+  const bool row_ok = mono && p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && lpl >= 1 &&
                       lpl <= kPageSize;
   if (!row_ok) return;  // the attention kernel treats such a row as empty or poisoned
   const int L = (n - 1) * kPageSize + lpl;
@@ -119,8 +130,11 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
     float4 cs[8];
     load_cos_sin(P.rope, live ? j : 0, g, cs);  // depends on the position only: goes out first
     int phys = P.indices[p0 + pr];
-    const bool page_ok = phys >= 0 && phys < P.num_pages;
-    if (!page_ok) phys = 0;
+    // the key's key_position_ids entry must be its logical index (the rotation uses j); a
+    // wrong one, like an out-of-range page, makes the key NaN for every query that sees it
+    const int kp = live ? P.kpos[(size_t)(p0 + pr) * kPageSize + r] : j;
+    const bool key_ok = phys >= 0 && phys < P.num_pages && kp == j;
+    if (phys < 0 || phys >= P.num_pages) phys = 0;
     // the HG heads of slot r are contiguous: HG * 256 bytes
     const size_t src = (((size_t)phys * kPageSize + r) * Hkv + hk0) * kHeadDim + 8 * g;
     uint4 raw[HG][4];
@@ -135,7 +149,7 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
       uint16_t* dst =
           kh + ((size_t)(hk0 + h) * P.num_indices * kPageSize + (size_t)(p0 + pr) * kPageSize + r) * kHeadDim + 8 * g;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !page_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
+      for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !key_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
     }
   }
 }
@@ -276,7 +290,8 @@ __global__ __launch_bounds__(256 * H) __attribute__((amdgpu_waves_per_eu(2 * H, 
   const int p1 = P.indptr[b + 1];
   const int n = p1 - p0;
   const int lpl = P.last_page_len[b];
-  const bool bad = p0 < 0 || n < 0 || p1 > P.num_indices || n > P.max_pages_per_row ||
+  const bool mono = indptr_prefix_monotone(P.indptr, b, tid, kAttendThreads);
+  const bool bad = !mono || p0 < 0 || n < 0 || p1 > P.num_indices || n > P.max_pages_per_row ||
                    (n > 0 && (lpl < 1 || lpl > kPageSize));
   const int L = (n > 0 && !bad) ? (n - 1) * kPageSize + lpl : 0;
 
@@ -289,7 +304,8 @@ __global__ __launch_bounds__(256 * H) __attribute__((amdgpu_waves_per_eu(2 * H, 
   for (int t = 0; t < kQBlock / 16; ++t) {
     const int i = qb * kQBlock + 16 * t + r;
     qp_blk[t] = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
-    if (i < Sq && (qp_blk[t] < 0 || qp_blk[t] >= P.table_rows)) { poison = 1; qp_blk[t] = -1; }
+    const int cp = i < Sq ? P.cache_position[(size_t)b * Sq + i] : -1;
+    if (i < Sq && (qp_blk[t] < 0 || qp_blk[t] >= P.table_rows || cp != qp_blk[t])) { poison = 1; qp_blk[t] = -1; }
   }
   int qp[kQT];
   int i_of[kQT];
@@ -384,7 +400,9 @@ __global__ __launch_bounds__(256 * H) __attribute__((amdgpu_waves_per_eu(2 * H, 
     for (int u = 0; u < kRowsPerThread; ++u) {
       const int ro = kTileRows * u + rt;  // row of the tile; its page is the tile's half ro / 16
       int phys = __builtin_amdgcn_readlane(pv, __builtin_amdgcn_readfirstlane(ro >> 4));
-      if (phys < 0 || phys >= P.num_pages) { poison = 1; phys = 0; }
+      // only the block's own tiles count: the ring also loads up to three tiles past the
+      // last one, whose results are thrown away
+      if (phys < 0 || phys >= P.num_pages) { poison |= t < ntiles ? 1 : 0; phys = 0; }
       const int j = min(t * kKT + ro, L - 1);  // logical key (clamped)
       tr.k[u] = ldg16(kh_row0 + (uint32_t)j * kHeadDim + col * 8);
       tr.v[u] = ldg16(P.v_cache + (size_t)phys * page_elems + ((uint32_t)(j & (kPageSize - 1)) * Hkv * kHeadDim + v_lane_off));

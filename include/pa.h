@@ -43,13 +43,21 @@
  *   - Errors are negative pa_status codes; nothing falls back to another algorithm.
  *   - pa_decode / pa_prefill never allocate, never synchronise and never read device
  *     memory from the host, so they may be recorded into a HIP graph.  They check host
- *     scalars only.  The kernels additionally bounds-check every page index, row extent,
- *     last_page_len and query position they read, and never access memory through an
- *     out-of-range value: a row whose indptr extent or last_page_len is out of range gets
- *     NaN in all its out and lse; an out-of-range page index or query position gets NaN in
- *     every output computed from it (decode: the whole row; prefill: each block of 32
- *     queries that reads that page or holds that query).  The launch still succeeds.  Call
- *     pa_validate_metadata first to get a precise error instead.
+ *     scalars only.  The kernels additionally check every metadata value they read and
+ *     never access memory through an out-of-range value; broken metadata fails closed with
+ *     NaN instead ([XCFG] "Fail closed, never substitute"; [PR162] "Code audit"):
+ *       - a row whose indptr extent or last_page_len is out of range, or (prefill) whose
+ *         extent is not part of a non-decreasing indptr prefix, gets NaN in all its out and
+ *         lse;
+ *       - an out-of-range page index, a query position outside [0, table rows) or a
+ *         cache_position that differs from its query_position_ids entry gets NaN in every
+ *         output computed from it (decode: the whole row; prefill: each block of 32 queries
+ *         that reads that page or holds that query);
+ *       - a key whose key_position_ids entry is not its logical index gets NaN in every
+ *         output that attends to it (decode: the whole row; prefill: every query that sees
+ *         the key).
+ *     The launch still succeeds.  Call pa_validate_metadata first to get a precise error
+ *     instead.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -172,7 +180,14 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
  *   q                bf16 [B, Hq, 1, 128]   pre-norm, pre-RoPE.
  *   k_cache, v_cache bf16 [num_pages, 16, Hkv, 128] (NHD); K pre-norm, pre-RoPE.
  *   q_norm_weight, k_norm_weight  fp32 [128], or NULL to skip that RMSNorm.
- *   query_position_ids int32 [B, 1]; key positions are the logical indices 0..L_b-1.
+ *   kv_indptr, kv_indices, kv_last_page_len, cache_position, query_position_ids,
+ *   key_position_ids   the metadata as for pa_validate_metadata, with Sq = 1 ([PR7]
+ *                    "Original PR7 Requirements": the page table, cache_position,
+ *                    query_position_ids and key_position_ids are the adapter's inputs).  The
+ *                    query sits at query_position_ids[b]; key j of row b sits at
+ *                    key_position_ids[kv_indptr[b] * 16 + j], which must be j (logical
+ *                    order, [PR7] "Current Implementation"): RoPE rotates key j by j and the
+ *                    kernels check the entry (see the conventions above).
  *   out              bf16 [B, Hq, 1, 128]   written.
  *   lse              fp32 [B, Hq, 1]        written; natural log of the sum of
  *                                           exp(scaled scores) ([PR7] "Original PR7
@@ -193,7 +208,8 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
  * Asynchronous on `stream`; requires q_len == 1 and batch <= plan capacity. */
 pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
                     int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
-                    const int32_t* kv_last_page_len, const int32_t* query_position_ids,
+                    const int32_t* kv_last_page_len, const int32_t* cache_position,
+                    const int32_t* query_position_ids, const int32_t* key_position_ids,
                     const void* q, const void* k_cache, const void* v_cache,
                     const float* q_norm_weight, const float* k_norm_weight,
                     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
@@ -217,7 +233,8 @@ pa_status pa_prefill_workspace_size(pa_plan_t plan, int32_t batch, int32_t q_len
  * (query block, head); a plan whose policy is not PA_SPLIT_DISABLED gets PA_ERR_UNSUPPORTED. */
 pa_status pa_prefill(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
                      int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
-                     const int32_t* kv_last_page_len, const int32_t* query_position_ids,
+                     const int32_t* kv_last_page_len, const int32_t* cache_position,
+                     const int32_t* query_position_ids, const int32_t* key_position_ids,
                      const void* q, const void* k_cache, const void* v_cache,
                      const float* q_norm_weight, const float* k_norm_weight,
                      void* out, float* lse, void* workspace, size_t workspace_bytes,

@@ -40,7 +40,17 @@ class DeviceBatch:
 
     def args(self):
         return (self.q, self.k_cache, self.v_cache, self.kv_indptr, self.kv_indices, self.kv_last_page_len,
-                self.query_position_ids, self.q_norm_weight, self.k_norm_weight)
+                self.cache_position, self.query_position_ids, self.key_position_ids, self.q_norm_weight,
+                self.k_norm_weight)
+
+
+def key_positions_for(b, num_indices, device=DEV):
+    """key_position_ids for a CSR with b's indptr but num_indices index slots (e.g. the
+    device-built CSR, whose index array has B * width slots): key j of row r at
+    indptr[r] * 16 + j, zeros elsewhere."""
+    kp = np.zeros(num_indices * 16, dtype=np.int32)
+    kp[:b.key_position_ids.size] = b.key_position_ids
+    return i32(kp, device)
 
 
 def make_plan(b, max_pages_per_row=None, max_batch=None, max_q_len=None, chunk_tokens=0):

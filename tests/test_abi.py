@@ -39,6 +39,18 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
         assert name in binding.SIGNATURES, name
 
 
+def test_binding_argument_counts_match_the_header():
+    """Every binding signature takes as many arguments as the header's declaration lists."""
+    from deterministic_paged_kv_amd import binding
+
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, params in re.findall(r"\b(pa_[a-z_]+)\s*\(([^;{]*?)\)\s*;", text):
+        if name not in binding.SIGNATURES:
+            continue
+        n = 0 if params.strip() in ("", "void") else params.count(",") + 1
+        assert len(binding.SIGNATURES[name][1]) == n, (name, n, len(binding.SIGNATURES[name][1]))
+
+
 def test_status_strings(lib):
     from deterministic_paged_kv_amd import binding
 
@@ -80,9 +92,9 @@ def test_plan_fails_closed_on_host_arguments(lib):
 
 def test_calls_without_a_plan_fail_closed(lib):
     null = None
-    assert lib.pa_decode(null, 1, 1, 1, 0, *([null] * 12), 0, null) == -1
+    assert lib.pa_decode(null, 1, 1, 1, 0, *([null] * 14), 0, null) == -1
     assert lib.pa_decode_workspace_size(null, 1, ctypes.byref(ctypes.c_size_t())) == -1
-    assert lib.pa_prefill(null, 1, 1, 1, 0, *([null] * 12), 0, null) == -1
+    assert lib.pa_prefill(null, 1, 1, 1, 0, *([null] * 14), 0, null) == -1
     from deterministic_paged_kv_amd import binding
 
     rep = binding.ValidationReport()
@@ -141,3 +153,4 @@ def test_backward_without_a_plan_fails_closed(lib):
                                    p, 1 << 20, None) == -1
     n = ctypes.c_size_t()
     assert lib.pa_prefill_backward_workspace_size(None, 1, 1, ctypes.byref(n)) == -1
+

@@ -44,8 +44,9 @@ def _forward(plan, q, k, v, wq, wk, pos):
     indices = np.arange(B * npg, dtype=np.int32)
     last = np.full(B, S - (npg - 1) * 16, dtype=np.int32)
     f = lambda a: None if a is None else torch.from_numpy(a).cuda()
+    kpos = np.tile(np.arange(npg * 16, dtype=np.int32), B)  # key j of row b at b * npg * 16 + j
     out, lse = pa.prefill(plan, bf16_tensor(q), bf16_tensor(kc), bf16_tensor(vc), i32(indptr), i32(indices), i32(last),
-                          i32(pos), f(wq), f(wk))
+                          i32(pos), i32(pos), i32(kpos), f(wq), f(wk))
     return out, lse
 
 

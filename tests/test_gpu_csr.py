@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads
 import deterministic_paged_kv_amd as pa
-from _paged import DeviceBatch, i32, make_plan, same_bits, to_numpy
+from _paged import DeviceBatch, i32, key_positions_for, make_plan, same_bits, to_numpy
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,7 @@ def test_device_csr_drives_attention_bitwise(gpu, kind):
     indptr, indices, last = pa.build_csr(i32(table), i32(lens))
     args = list(db.args())
     args[3], args[4], args[5] = indptr, indices, last
+    args[8] = key_positions_for(b, int(indices.numel()))
     got = to_numpy(*fn(plan, *args))
     assert same_bits(got, ref), kind
     print(f"[csr] {kind} over the device-built CSR: bitwise equal", flush=True)
@@ -124,6 +125,7 @@ def test_unrepresentable_length_fails_loudly(gpu):
     db = DeviceBatch(b)
     args = list(db.args())
     args[3], args[4], args[5] = indptr, indices, last
+    args[8] = key_positions_for(b, int(indices.numel()))
     out, lse = to_numpy(*pa.decode(plan, *args))
     assert np.all(np.isnan(lse[1])) and np.all(np.isfinite(lse[0]))
     nnz = int(indptr[-1].item())
@@ -152,10 +154,12 @@ def test_build_and_decode_in_one_graph(gpu):
     out = torch.empty_like(static.q)
     lse = torch.empty(static.q.shape[:3], dtype=torch.float32, device="cuda")
 
+    kpos = key_positions_for(a, a.batch * width)
+
     def call():
         pa.build_csr(table, lens, indptr, indices, last)
         args = list(static.args())
-        args[3], args[4], args[5] = indptr, indices, last
+        args[3], args[4], args[5], args[8] = indptr, indices, last, kpos
         pa.decode(plan, *args, out=out, lse=lse)
 
     side = torch.cuda.Stream()
@@ -173,8 +177,10 @@ def test_build_and_decode_in_one_graph(gpu):
         t, l = _dense_from(host, width)
         table.copy_(i32(t))
         lens.copy_(i32(l))
-        for name in ("q", "k_cache", "v_cache", "query_position_ids", "q_norm_weight", "k_norm_weight"):
+        for name in ("q", "k_cache", "v_cache", "cache_position", "query_position_ids", "q_norm_weight",
+                     "k_norm_weight"):
             getattr(static, name).copy_(getattr(dev, name))
+        kpos.copy_(key_positions_for(host, a.batch * width))
         for rep in range(3):
             out.fill_(float("nan"))
             indices.fill_(12345)

@@ -1,5 +1,7 @@
 """pa_decode on the GPU against the CPU oracle, and its bitwise invariances."""
 
+import functools
+
 import numpy as np
 import pytest
 
@@ -30,21 +32,25 @@ def test_tiny_decode_parity(gpu):
     check_full(workloads.tiny_decode(), "tiny decode")
 
 
-@pytest.mark.parametrize("schedule", ["unit", "multi_cu"])
-def test_qwen3_8b_decode_parity_sampled(gpu, schedule):
-    """Full Qwen3-8B per-GPU shape (B=32, Hq=16, Hkv=4, L ~ U[512, 4096]); oracle on sampled rows.
-    Both schedules: one workgroup per (row, KV head), and the multi-CU one (stream kernel +
-    combine, the launch configuration the benchmark times)."""
+@functools.lru_cache(maxsize=1)
+def _qwen3_8b():
+    """The Qwen3-8B per-GPU batch and its oracle result over every row and head (computed once)."""
     b = workloads.qwen3_8b_decode()
+    return b, oracle_ref(b)
+
+
+@pytest.mark.parametrize("schedule", ["unit", "multi_cu", "fixed_1024"])
+def test_qwen3_8b_decode_parity_full(gpu, schedule):
+    """Full Qwen3-8B per-GPU shape (B=32, Hq=16, Hkv=4, L ~ U[512, 4096]) against the oracle on
+    every row and query head.  Three schedules: one workgroup per (row, KV head), the multi-CU
+    one (stream kernel + combine, the launch configuration the benchmark times), and the
+    fixed-chunk policy with 1,024-token chunks."""
+    b, (ref_out, ref_lse) = _qwen3_8b()
     db = DeviceBatch(b)
-    plan = make_plan(b, max_pages_per_row=256)
-    ws = pa.decode_workspace(plan, b.batch) if schedule == "multi_cu" else None
+    plan = make_plan(b, max_pages_per_row=256, chunk_tokens=1024 if schedule == "fixed_1024" else 0)
+    ws = pa.decode_workspace(plan, b.batch) if schedule != "unit" else None
     out, lse = run("decode", plan, db, workspace=ws)
-    rows = [0, 5, 17, 31, int(np.argmax(b.lengths)), int(np.argmin(b.lengths))]
-    ref_out, ref_lse = oracle_ref(b, rows=rows)
-    assert_parity(out[rows], lse[rows], ref_out, ref_lse, f"qwen3-8b decode ({schedule}) rows {rows}")
-    # every row finite
-    assert np.all(np.isfinite(lse))
+    assert_parity(out, lse, ref_out, ref_lse, f"qwen3-8b decode ({schedule}), all 32 rows x 16 heads")
 
 
 @pytest.mark.parametrize("lengths", [
@@ -136,12 +142,35 @@ def test_batch_and_plan_width_invariance(gpu):
     assert_parity(ref_o[None], ref_l[None], ref_out, ref_lse, "1500-token row")
 
 
-@pytest.mark.parametrize("batch,length,schedule", [(1, 131072, "unit"), (1, 131072, "multi_cu"),
-                                                    (2, 32768, "unit"), (4, 32768, "multi_cu")])
+@functools.lru_cache(maxsize=1)
+def _long(batch, length):
+    return workloads.long_decode(batch, length, num_pages=batch * length // 16 + 512)
+
+
+@pytest.mark.parametrize("batch,length", [(b, L) for b in (1, 2, 4) for L in (32768, 65536, 131072)])
+def test_long_context_grid_parity_all_heads(gpu, batch, length):
+    """Every point of the long-context grid the benchmark times (B in {1, 2, 4} x L in {32K, 64K,
+    128K}, Hq=32, Hkv=8), under both policies it times (the 16-stream tree on the multi-CU
+    schedule, and fixed 1,024-token chunks): all 32 query heads of the batch's last row against
+    the oracle."""
+    b = _long(batch, length)
+    db = DeviceBatch(b)
+    ref_out, ref_lse = oracle_ref(b, rows=[batch - 1])
+    for chunk in (0, 1024):
+        plan = make_plan(b, max_pages_per_row=length // 16, chunk_tokens=chunk)
+        ws = pa.decode_workspace(plan, batch)
+        out, lse = run("decode", plan, db, workspace=ws)
+        policy = f"fixed:{chunk}" if chunk else "tree"
+        assert_parity(out[[batch - 1]], lse[[batch - 1]], ref_out, ref_lse,
+                      f"long decode B={batch} L={length} ({policy}), all heads of row {batch - 1}")
+    del db
+
+
+@pytest.mark.parametrize("batch,length,schedule", [(1, 131072, "unit"), (2, 32768, "unit")])
 def test_long_context_decode_sampled(gpu, batch, length, schedule):
-    """Long-context low-batch decode (Hq=32, Hkv=8): oracle on one row and two heads per KV group edge."""
-    pages = batch * length // 16
-    b = workloads.long_decode(batch, length, num_pages=pages + 512)
+    """Long-context low-batch decode (Hq=32, Hkv=8) on the one-workgroup schedule: oracle on one
+    row and two heads per KV group edge."""
+    b = _long(batch, length)
     db = DeviceBatch(b)
     plan = make_plan(b, max_pages_per_row=length // 16)
     ws = pa.decode_workspace(plan, batch) if schedule == "multi_cu" else None

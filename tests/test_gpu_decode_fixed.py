@@ -38,16 +38,7 @@ def test_tiny_and_ragged_parity(gpu, chunk):
         assert_parity(out, lse, ref_out, ref_lse, f"fixed:{chunk} {label}")
 
 
-def test_qwen3_8b_parity_sampled(gpu):
-    b = workloads.qwen3_8b_decode()
-    plan = make_plan(b, max_pages_per_row=256, chunk_tokens=1024)
-    out, lse = run_fixed(plan, DeviceBatch(b), b.batch)
-    rows = [0, 9, 31, int(np.argmax(b.lengths)), int(np.argmin(b.lengths))]
-    ref_out, ref_lse = oracle_ref(b, rows=rows)
-    assert_parity(out[rows], lse[rows], ref_out, ref_lse, f"fixed:1024 qwen3-8b rows {rows}")
-
-
-@pytest.mark.parametrize("batch,length,chunk", [(1, 131072, 2048), (4, 32768, 1024)])
+@pytest.mark.parametrize("batch,length,chunk", [(1, 131072, 2048)])
 def test_long_context_parity_sampled(gpu, batch, length, chunk):
     """The long-context low-batch shape the fixed policy is for (Hq=32, Hkv=8)."""
     b = workloads.long_decode(batch, length, num_pages=batch * length // 16 + 512)

@@ -1,8 +1,10 @@
 """pa_decode and pa_prefill captured in a HIP graph (torch.cuda.CUDAGraph drives hipStreamBeginCapture).
 
 The pages ask that graph replay be bitwise equal to eager execution and that no host
-synchronisation be needed when the block table changes between calls ("[RL-Kernel] Rollout
-Attention Backend Investigation", the FlashInfer diagnostics and the graph-replay findings).
+synchronisation be needed when the block table changes between calls ("flashinfer_fa2 backend
+for NVIDIA Ada (SM89)", "Design notes": CSR metadata built on the device with a fixed shape and
+no host synchronisation, graph replay equal to eager; the author's reply to the maintainer
+review confirms the replay-vs-eager equality).
 The calls read every piece of metadata from device memory and allocate nothing, so a graph
 captured once serves any block table of the same shapes.
 
@@ -23,8 +25,8 @@ from _paged import DeviceBatch, make_plan, same_bits, to_numpy
 
 pytestmark = pytest.mark.gpu
 
-_FIELDS = ("q", "k_cache", "v_cache", "kv_indptr", "kv_indices", "kv_last_page_len", "query_position_ids",
-           "q_norm_weight", "k_norm_weight")
+_FIELDS = ("q", "k_cache", "v_cache", "kv_indptr", "kv_indices", "kv_last_page_len", "cache_position",
+           "query_position_ids", "key_position_ids", "q_norm_weight", "k_norm_weight")
 
 
 def _load_into(dst: DeviceBatch, src: DeviceBatch):
@@ -99,3 +101,50 @@ def test_prefill_graph_replay(gpu):
     ws = torch.empty(pa.prefill_workspace_size(plan, a.batch, a.q_len, a.nnz), dtype=torch.uint8,
                      device="cuda")
     _replay_and_check("prefill", plan, (a, b), workspace=ws)
+
+
+def test_decode_plan_width_switches_inside_one_graph(gpu):
+    """Plans of width 64, 65 and 128 pages called back to back inside one captured graph (a host
+    synchronisation anywhere in the calls would abort the capture), each writing its own out and
+    lse.  Every replay, with new metadata copied in between, gives the three results bitwise equal
+    to each other and to eager calls: the plan width is capacity only ("flashinfer_fa2 backend
+    for NVIDIA Ada (SM89)", "Design notes": plans keyed by a power-of-two width bucket, no host
+    synchronisation when the width changes)."""
+    a, b = _two_batches(37, [300, 17, 0, 1000, 64], q_len=1, num_q_heads=16, num_kv_heads=4, num_pages=160)
+    plans = [make_plan(a, max_pages_per_row=w) for w in (64, 65, 128)]
+    static = DeviceBatch(a)
+    ws = [pa.decode_workspace(p, a.batch) for p in plans]
+    outs = [torch.empty_like(static.q) for _ in plans]
+    lses = [torch.empty(static.q.shape[:3], dtype=torch.float32, device="cuda") for _ in plans]
+
+    def calls():
+        for i, p in enumerate(plans):
+            # the middle plan runs the one-workgroup schedule, the others the multi-CU one
+            pa.decode(p, *static.args(), out=outs[i], lse=lses[i], workspace=None if i == 1 else ws[i])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for i, host in enumerate((a, b)):
+        dev = DeviceBatch(host)
+        ref = to_numpy(*pa.decode(plans[2], *dev.args()))
+        if i > 0:
+            _load_into(static, dev)
+            torch.cuda.synchronize()
+        for rep in range(3):
+            for o, l in zip(outs, lses):
+                o.fill_(float("nan"))
+                l.fill_(float("nan"))
+            graph.replay()
+            pa.decode(plans[0], *dev.args())  # an eager call of another width between replays
+            for w, o, l in zip((64, 65, 128), outs, lses):
+                assert same_bits(to_numpy(o, l), ref), f"width {w}, metadata set {i}, replay {rep}"
+            print(f"[graph] widths 64/65/128 in one graph, metadata set {i} replay {rep}: bitwise equal", flush=True)
+    del graph

@@ -51,6 +51,8 @@ def _cases(b, table_rows):
         ("indptr past the index array", "kv_indptr", 3, int(ip[3]) + 1, 2),
         ("query position past the RoPE table", "query_position_ids", 0, table_rows, 0),
         ("negative query position", "query_position_ids", 0, -1, 0),
+        ("cache position not the query position", "cache_position", 0, int(b.query_position_ids[0, -1]) + 3, 0),
+        ("key position not the logical index", "key_position_ids", int(ip[1]) * 16 + 7, 8, 1),
     ]
 
 
@@ -77,8 +79,44 @@ def test_prefill_out_of_range_metadata_poisons_its_row(gpu):
     table_rows = plan.max_pages_per_row * 16 + 1
     for label, field, idx, value, row in _cases(b, table_rows):
         print(f"[poison] prefill: {label}", flush=True)
-        if field == "query_position_ids":
-            idx = 5  # query 5 of row 0
+        if field in ("query_position_ids", "cache_position"):
+            idx = 5  # query 5 of row 0 (every query of the row sees key 7 of row 1)
         db = DeviceBatch(b)
         _corrupt(db, field, idx, value)
         _check(clean, run("prefill", plan, db), row, f"prefill, {label}")
+
+
+def test_prefill_non_monotone_indptr_poisons_every_row_after_the_decrease(gpu):
+    """indptr that decreases after row 0: row 1's extent is negative and row 2's lies inside
+    row 0's, so two rows would write k^ into the same workspace rows.  Every row from the
+    decrease on comes out NaN; row 0 is bitwise what a clean call gives."""
+    b = workloads.make_batch(63, [64, 48, 40, 33], q_len=20, num_q_heads=8, num_kv_heads=2, num_pages=64,
+                             query_mode="prefill")
+    plan = make_plan(b, max_pages_per_row=16)  # row 2's broken extent (9 pages) fits the plan
+    clean = run("prefill", plan, DeviceBatch(b))
+    db = DeviceBatch(b)
+    _corrupt(db, "kv_indptr", 2, 1)  # [0, 4, 1, ...]: row 1 = [4, 1), row 2 = [1, ...)
+    out, lse = run("prefill", plan, db)
+    assert np.array_equal(out[0], clean[0][0]) and np.array_equal(lse[0].view(np.uint32), clean[1][0].view(np.uint32))
+    for r in range(1, b.batch):
+        assert np.all(np.isnan((out[r].astype(np.uint32) << 16).view(np.float32))), f"row {r} out"
+        assert np.all(np.isnan(lse[r])), f"row {r} lse"
+
+
+def test_prefill_bad_page_past_a_block_leaves_that_block_clean(gpu):
+    """A page that only later queries see: the queries whose visible keys end before it are
+    bitwise unchanged (no NaN from tiles loaded ahead and thrown away), the queries that see it
+    are NaN.  One row of 256 new tokens (no prefix), the last page (keys 240..255) out of the
+    pool: queries 0..191 lie in blocks that end before key 240 for any block of 32 or 64
+    queries."""
+    b = workloads.make_batch(64, [256], q_len=256, num_q_heads=8, num_kv_heads=2, num_pages=32,
+                             query_mode="prefill")
+    plan = make_plan(b)
+    clean = run("prefill", plan, DeviceBatch(b))
+    db = DeviceBatch(b)
+    _corrupt(db, "kv_indices", 15, b.num_pages + 3)
+    out, lse = run("prefill", plan, db)
+    assert np.array_equal(out[0, :, :192], clean[0][0, :, :192])
+    assert np.array_equal(lse[0, :, :192].view(np.uint32), clean[1][0, :, :192].view(np.uint32))
+    assert np.all(np.isnan(lse[0, :, 240:]))
+    assert np.all(np.isnan((out[0, :, 240:].astype(np.uint32) << 16).view(np.float32)))
