@@ -46,6 +46,7 @@ ROTATIONS = 4
 PREFILL_ROTATIONS = 8
 # untimed calls before each secondary workload (long-context decode, prefill, backward)
 SETTLE_MS = 60.0
+PREFILL_KERNELS = "key_prologue_kernel + attend_kernel"
 
 
 def decode_bytes(b) -> int:
@@ -212,6 +213,47 @@ def time_calls(fn, sets, steps, warmup, settle_ms=0.0):
     return wall_ms, launch_ms
 
 
+def measured_read_ceiling(device, nbytes, sets=4, reps=20):
+    """Best rate of a plain streaming read (libpa_probe.so) of `nbytes` bytes, rotating over
+    `sets` separate buffers so that no read finds its data in the Infinity Cache; several grid
+    sizes, best kept.  Returns (GB/s, description)."""
+    import torch
+
+    from deterministic_paged_kv_amd import probe
+
+    n = (nbytes + 15) // 16 * 16
+    bufs = [torch.randint(0, 255, (n,), dtype=torch.uint8, device=device) for _ in range(sets)]
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    sink = torch.zeros(16 * cus, dtype=torch.int32, device=device)
+    best = (0.0, 0)
+    for blocks in (4 * cus, 8 * cus, 16 * cus):
+        _, ms = time_calls(lambda buf: probe.read(buf, blocks, sink), bufs, reps, 8, settle_ms=SETTLE_MS)
+        best = max(best, (n / (ms * 1e-3) / 1e9, blocks))
+    del bufs
+    return round(best[0], 1), (f"plain 16-byte-load read of {n} bytes ({sets} buffers rotated, so every read "
+                               f"comes from HBM), best of 4/8/16 workgroups per CU ({best[1]} workgroups)")
+
+
+def measured_mfma_rate(device, reps=10):
+    """Rate of independent bf16 MFMAs (libpa_probe.so), 8 wavefronts per CU, for both tile
+    shapes; the better is the measured matrix-core ceiling.  Returns (TFLOP/s, description)."""
+    import torch
+
+    from deterministic_paged_kv_amd import probe
+
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    sink = torch.zeros(2 * cus, dtype=torch.float32, device=device)
+    rates = {}
+    for shape in (16, 32):
+        flops = []
+        _, ms = time_calls(lambda _: flops.append(probe.mfma(2 * cus, 4096, shape, sink)), [None], reps, 2,
+                           settle_ms=SETTLE_MS)
+        rates[shape] = flops[-1] / (ms * 1e-3) / 1e12
+    best = max(rates, key=rates.get)
+    return round(rates[best], 1), (f"independent bf16 MFMAs, 8 wavefronts per CU: 16x16x32 "
+                                   f"{rates[16]:.0f} TFLOP/s, 32x32x16 {rates[32]:.0f} TFLOP/s")
+
+
 def backward_flops(batch, seq, num_q_heads) -> int:
     """Five products over the causally visible pairs of every query head (S = QK^T recomputed,
     dP = dO V^T, dV += P^T dO, dQ = dS K, dK += dS^T Q): 10 * D * Hq * pairs."""
@@ -240,7 +282,8 @@ def bench_backward(device, steps, warmup, batch=4, seq=2048, hq=32, hkv=8):
     last = i32(torch.full((batch,), 16))
     pos = i32(torch.arange(seq).repeat(batch, 1)).contiguous()
     plan = pa.Plan(hq, hkv, max_batch=batch, max_q_len=seq, max_pages_per_row=npg, rms_eps=1e-6)
-    out, lse = pa.prefill(plan, q, pages(k), pages(v), indptr, indices, last, pos, wq, wk)
+    kpos = i32(torch.arange(npg * 16).repeat(batch))  # key j of row b at b * npg * 16 + j
+    out, lse = pa.prefill(plan, q, pages(k), pages(v), indptr, indices, last, pos, pos, kpos, wq, wk)
     ws = torch.empty(pa.prefill_backward_workspace_size(plan, batch, seq), dtype=torch.uint8, device=device)
     grads = (torch.empty(q.shape, dtype=torch.float32, device=device),
              torch.empty(k.shape, dtype=torch.float32, device=device),
@@ -264,39 +307,69 @@ def bench_backward(device, steps, warmup, batch=4, seq=2048, hq=32, hkv=8):
                          "algorithmic_flops_per_call": flops, "avg_call_ms": round(b_launch, 5)}}
 
 
-def host_cores() -> int:
-    """Cores this process may run on (the CPU share of the machine), capped at 16."""
+def affinity_cores() -> int:
+    """Cores this process may run on (sched_getaffinity), uncapped."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
 
 
-def _time_oracle(b, min_seconds, max_reps):
-    """Median wall time of oracle.paged_attention on batch b, repeated until min_seconds of CPU
-    work have been spent (at least 3 runs, at most max_reps)."""
+def host_cores() -> int:
+    """Threads the CPU oracle uses: the cores this process may run on, at most 16 (one GPU's
+    share of the host's CPUs)."""
+    return max(1, min(16, affinity_cores()))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_info(cores) -> dict:
+    return {"cores_available": affinity_cores(), "cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "threads_used": cores}
+
+
+def _time_oracle(b, min_seconds, max_reps, threads=None, rows=None):
+    """Median wall time of oracle.paged_attention on batch b (or its `rows`), repeated until
+    min_seconds of CPU work have been spent (at least 3 runs, at most max_reps), with `threads`
+    BLAS threads (default: host_cores())."""
     from threadpoolctl import threadpool_limits
 
     import oracle
 
-    cores = host_cores()
+    cores = threads or host_cores()
     args, kwargs = b.oracle_args()
     times = []
     with threadpool_limits(limits=cores):
         while len(times) < 3 or (sum(times) < min_seconds and len(times) < max_reps):
             t0 = time.perf_counter()
-            oracle.paged_attention(*args, **kwargs)
+            oracle.paged_attention(*args, rows=rows, **kwargs)
             times.append(time.perf_counter() - t0)
     return sorted(times)[len(times) // 2], len(times), sum(times), cores
 
 
 def cpu_baseline_decode(base, alg_bytes):
-    """The CPU oracle (float64 numpy) on the whole decode batch, ~10 s of repeated runs."""
+    """The CPU oracle (float64 numpy) on the whole decode batch, ~10 s of repeated runs, plus a
+    single-thread run on four rows (scaled by those rows' own bytes)."""
     dt, reps, total, cores = _time_oracle(base, 10.0, 40)
+    rows = [0, 1, 2, 3]
+    sub = 4 * int(sum(base.lengths[r] for r in rows)) * base.num_kv_heads * 128 + \
+        4 * len(rows) * base.num_q_heads * 128 + 4 * len(rows) * base.num_q_heads
+    dt1, reps1, _, _ = _time_oracle(base, 3.0, 10, threads=1, rows=rows)
     return {"value": round(alg_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole B=32 decode batch (all rows and heads): median of {reps} runs "
-                      f"({dt:.2f} s each, {total:.1f} s in all), float64 numpy with {cores} BLAS threads"}
+                      f"({dt:.2f} s each, {total:.1f} s in all), float64 numpy with {cores} BLAS threads",
+            "single_thread": {"value": round(sub / dt1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"rows 0-3 of the same batch, median of {reps1} runs ({dt1:.2f} s each), "
+                                        f"one BLAS thread"},
+            **host_info(cores)}
 
 
 def cpu_baseline_prefill(b, flops):
@@ -304,7 +377,7 @@ def cpu_baseline_prefill(b, flops):
     dt, reps, total, cores = _time_oracle(b, 10.0, 20)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole chunked-prefill batch: median of {reps} runs ({dt:.2f} s each, "
-                      f"{total:.1f} s in all), float64 numpy with {cores} BLAS threads"}
+                      f"{total:.1f} s in all), float64 numpy with {cores} BLAS threads", **host_info(cores)}
 
 
 def profile_copy():
@@ -430,8 +503,12 @@ def main():
 
     print("[bench] timing decode", file=sys.stderr, flush=True)
     dsteps = 2 if args.prefill_only else args.steps
-    wall_ms, launch_ms = time_calls(step_multi, sets, dsteps, 0 if args.prefill_only else args.warmup)
-    unit_wall_ms, unit_launch_ms = time_calls(step, sets, dsteps, 0 if args.prefill_only else args.warmup)
+    # the W warmup steps, then untimed steps until SETTLE_MS have passed (the first tens of
+    # milliseconds of a new load run at a lower shader clock), then exactly K timed steps
+    wall_ms, launch_ms = time_calls(step_multi, sets, dsteps, 0 if args.prefill_only else args.warmup,
+                                    settle_ms=0.0 if args.prefill_only else SETTLE_MS)
+    unit_wall_ms, unit_launch_ms = time_calls(step, sets, dsteps, 0 if args.prefill_only else args.warmup,
+                                              settle_ms=0.0 if args.prefill_only else SETTLE_MS)
     alg = decode_bytes(base)
     value = alg / (wall_ms * 1e-3) / 1e9
     achieved = alg / (launch_ms * 1e-3) / 1e9
@@ -463,6 +540,13 @@ def main():
             "avg_launch_ms": round(unit_launch_ms, 5),
             "frac": round(alg / (unit_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+
+    if not args.prefill_only:
+        # the measured read ceiling at this call's size, beside the published peak
+        print("[bench] measuring the read ceiling", file=sys.stderr, flush=True)
+        ceil_gbs, ceil_how = measured_read_ceiling(device, alg)
+        result["roofline"].update({"peak_measured": ceil_gbs, "frac_measured": round(achieved / ceil_gbs, 4),
+                                   "peak_measured_how": ceil_how})
 
     if not args.decode_only and not args.prefill_only:
         # Long-context low-batch decode (B=1, L=131,072): the 16-stream tree against the
@@ -540,15 +624,20 @@ def main():
         _, p_warm = time_calls(pstep, [pdb], psteps, args.warmup, settle_ms=SETTLE_MS)
         del psets
         flops = prefill_flops(pb)
+        print("[bench] measuring the matrix-core rate", file=sys.stderr, flush=True)
+        mfma_rate, mfma_how = measured_mfma_rate(device)
+        p_ach = flops / (p_launch * 1e-3) / 1e12
         result["prefill"] = {
             "workload": "chunked_prefill", "batch": 4, "q_len": 512, "prefixes": [0, 1024, 2048, 3584],
             "num_q_heads": 32, "num_kv_heads": 8, "steps": psteps, "input_rotation": PREFILL_ROTATIONS,
             "warm_avg_call_ms": round(p_warm, 5), "ms_per_call": round(p_wall, 5),
             "value": round(flops / (p_wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "roofline": {"bound": "mfma", "achieved": round(flops / (p_launch * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "achieved": round(p_ach, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(flops / (p_launch * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "prologue_kernel + attend_kernel (whole call)",
+                         "frac": round(p_ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "peak_measured": mfma_rate, "frac_measured": round(p_ach / mfma_rate, 4),
+                         "peak_measured_how": mfma_how,
+                         "traffic": None, "kernel": PREFILL_KERNELS + " (whole call)",
                          "algorithmic_flops_per_call": flops, "avg_call_ms": round(p_launch, 5)},
         }
         print("[bench] timing the full-prefill backward", file=sys.stderr, flush=True)

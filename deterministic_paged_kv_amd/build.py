@@ -1,4 +1,6 @@
-"""Compile the HIP library libpa.so in-tree for gfx950 (hipcc; no GPU needed to build)."""
+"""Compile the HIP libraries in-tree for gfx950 (hipcc; no GPU needed to build): libpa.so (the
+attention library of include/pa.h) and libpa_probe.so (the measurement kernels of
+include/pa_probe.h that the benchmark reports ceilings with)."""
 
 from __future__ import annotations
 
@@ -13,6 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_api.hip", "pa_validate.hip", "pa_decode.hip", "pa_prefill.hip", "pa_csr.hip", "pa_backward.hip"]
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
+PROBE_SOURCES = ["pa_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -25,6 +29,7 @@ EXTRA = {
     "pa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "pa_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "pa_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
@@ -36,17 +41,20 @@ def _run(cmd):
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile every source and link libpa.so next to this file; returns its path."""
+    """Compile every source and link libpa.so and libpa_probe.so next to this file; returns the
+    path of libpa.so."""
     os.makedirs(BUILD, exist_ok=True)
-    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    srcs = SOURCES + PROBE_SOURCES
+    objs = {s: os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in srcs}
+    cmds = [[HIPCC, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", objs[s]] for s in srcs]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for r in ex.map(_run, cmds):
             if verbose and r.stderr:
                 sys.stderr.write(r.stderr)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[objs[s] for s in names], "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -154,3 +154,25 @@ def test_backward_without_a_plan_fails_closed(lib):
     n = ctypes.c_size_t()
     assert lib.pa_prefill_backward_workspace_size(None, 1, 1, ctypes.byref(n)) == -1
 
+
+def test_probe_library_exports_its_header():
+    """libpa_probe.so (the measurement kernels of include/pa_probe.h) exports every declared
+    symbol with the binding's argument count, and rejects bad host arguments before any launch."""
+    from deterministic_paged_kv_amd import probe
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pa_probe.h")).read(), flags=re.S)
+    decls = re.findall(r"\b(pa_[a-z_]+)\s*\(([^;{]*?)\)\s*;", text)
+    assert {n for n, _ in decls} == set(probe.SIGNATURES)
+    plib = probe.load()
+    for name, params in decls:
+        assert hasattr(plib, name)
+        assert len(probe.SIGNATURES[name][1]) == params.count(",") + 1, name
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its host checks
+    assert plib.pa_probe_read(p, 0, 1, p, None) == -1          # no bytes
+    assert plib.pa_probe_read(p, 24, 1, p, None) == -1         # not a multiple of 16
+    assert plib.pa_probe_read(p, 32, 0, p, None) == -1         # no workgroups
+    assert plib.pa_probe_read(None, 32, 1, p, None) == -1
+    assert plib.pa_probe_mfma(1, 1, 8, p, None) == -1          # unknown shape
+    assert plib.pa_probe_mfma(0, 1, 16, p, None) == -1
+    assert plib.pa_probe_mfma(1, 0, 16, p, None) == -1
+    assert plib.pa_probe_mfma(1, 1, 16, None, None) == -1
