@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     Plan,
     build_csr,
     decode,
+    decode_no_alloc,
     decode_workspace,
     decode_workspace_size,
     load,

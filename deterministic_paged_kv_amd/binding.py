@@ -37,6 +37,8 @@ SIGNATURES = {
                                     ctypes.POINTER(ValidationReport)]),
     "pa_decode": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
                          _p]),
+    "pa_decode_no_alloc": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                  _p]),
     "pa_decode_workspace_size": (_i32, [_p, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill_workspace_size": (_i32, [_p, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "pa_prefill": (_i32, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
@@ -246,6 +248,30 @@ def decode(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_
                             _ptr(key_position_ids), _ptr(q), _ptr(k_cache),
                             _ptr(v_cache), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(out), _ptr(lse),
                             _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
+    return out, lse
+
+
+def decode_no_alloc(plan: Plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, cache_position,
+                    query_position_ids, key_position_ids, q_norm_weight=None, k_norm_weight=None, *, out, lse,
+                    stream=None):
+    """pa_decode_no_alloc: the multi-compute-unit decode with the library's own scratch (no
+    workspace, no allocation).  out and lse must be given (nothing is allocated here either);
+    calls that overlap in time on one device race on the shared scratch."""
+    import torch
+
+    B, Sq, num_pages, nnz = _metadata(plan, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len,
+                                      cache_position, query_position_ids, key_position_ids)
+    if q_norm_weight is not None:
+        _need(q_norm_weight, "q_norm_weight", torch.float32, shape=(HEAD_DIM,))
+    if k_norm_weight is not None:
+        _need(k_norm_weight, "k_norm_weight", torch.float32, shape=(HEAD_DIM,))
+    _need(out, "out", torch.bfloat16, shape=q.shape)
+    _need(lse, "lse", torch.float32, shape=q.shape[:3])
+    _check(load().pa_decode_no_alloc(plan.handle, B, Sq, num_pages, nnz, _ptr(kv_indptr), _ptr(kv_indices),
+                                     _ptr(kv_last_page_len), _ptr(cache_position), _ptr(query_position_ids),
+                                     _ptr(key_position_ids), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(out), _ptr(lse),
+                                     _stream(stream)), "pa_decode_no_alloc")
     return out, lse
 
 

@@ -3,14 +3,40 @@
 // and enqueue work: no allocation, no synchronisation, no device reads.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "pa_internal.h"
 
+// Scratch of pa_decode_no_alloc: the multi-compute-unit decode workspace (per-stream or
+// per-chunk softmax states and poison flags) in a file-scope device array, for callers that
+// cannot allocate.  Each device holds its own copy until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it only stands for the symbol): its device
+// address is looked up once per device and kept in g_scratch below.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 using namespace pa;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};  // device address of `scratch` on each device, once looked up
+
+// The device address of `scratch` on `device`, which must be current; looked up on the first
+// call for that device.  nullptr if the lookup fails.
+void* scratch_on(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[device] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[device] = ptr;
+  }
+  return g_scratch[device];
+}
 
 bool plan_ok(pa_plan_t plan) { return plan != nullptr && plan->d_rope != nullptr; }
 
@@ -139,6 +165,8 @@ pa_status pa_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, i
     delete p;
     return PA_ERR_HIP;
   }
+  // set-up of pa_decode_no_alloc's scratch on this device (the device is current here)
+  if (scratch_on(p->device) == nullptr) { delete p; return PA_ERR_HIP; }
   const std::vector<float> table = rope_table(p->table_rows, (double)rope_theta, (double)rope_scale);
   const size_t bytes = table.size() * sizeof(float);
   if (hipMalloc(&p->d_rope, bytes) != hipSuccess) { delete p; return PA_ERR_HIP; }
@@ -248,7 +276,8 @@ pa_status pa_validate_metadata(pa_plan_t plan, int32_t batch, int32_t q_len, int
 
 namespace {
 
-// Body of pa_decode: `workspace` is the caller's buffer, or NULL (one workgroup per unit).
+// Shared body of pa_decode and pa_decode_no_alloc: `workspace` is the caller's buffer, the
+// scratch array's device address, or NULL (one workgroup per unit).
 pa_status decode_call(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
                       const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
                       const int32_t* cache_position, const int32_t* query_position_ids,
@@ -306,6 +335,24 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
   return decode_call(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices, kv_last_page_len,
                      cache_position, query_position_ids, key_position_ids, q, k_cache, v_cache, q_norm_weight,
                      k_norm_weight, out, lse, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_no_alloc(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages, int32_t num_indices,
+                             const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                             const int32_t* cache_position, const int32_t* query_position_ids,
+                             const int32_t* key_position_ids, const void* q, const void* k_cache,
+                             const void* v_cache, const float* q_norm_weight, const float* k_norm_weight,
+                             void* out, float* lse, void* stream) {
+  if (!plan_ok(plan)) return PA_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || batch > plan->max_batch) return batch < 0 ? PA_ERR_INVALID_ARGUMENT : PA_ERR_CAPACITY;
+  if (decode_workspace_bytes(batch, plan->num_kv_heads, plan->group, plan->split_chunk_pages,
+                             plan->max_pages_per_row) > kNoAllocScratchBytes)
+    return PA_ERR_CAPACITY;
+  void* ws = scratch_on(plan->device);
+  if (ws == nullptr) return PA_ERR_HIP;
+  return decode_call(plan, batch, q_len, num_pages, num_indices, kv_indptr, kv_indices, kv_last_page_len,
+                     cache_position, query_position_ids, key_position_ids, q, k_cache, v_cache, q_norm_weight,
+                     k_norm_weight, out, lse, ws, kNoAllocScratchBytes, stream);
 }
 
 pa_status pa_decode_workspace_size(pa_plan_t plan, int32_t batch, size_t* bytes) {

@@ -214,6 +214,25 @@ pa_status pa_decode(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pa
                     const float* q_norm_weight, const float* k_norm_weight,
                     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode's multi-compute-unit schedule (or, under a PA_SPLIT_FIXED plan, its fixed-chunk
+ * schedule) without a caller workspace and without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, results and bits as pa_decode with a workspace; the
+ * stream states live in a library-owned scratch array of 16 MiB per device instead (set up on
+ * the device by pa_plan, held until the process ends).  A batch whose workspace
+ * (pa_decode_workspace_size) exceeds 16 MiB returns PA_ERR_CAPACITY; for Hq = 16, Hkv = 4 under
+ * PA_SPLIT_DISABLED that is any batch above 125 rows.  The scratch needs no initialisation
+ * (every call writes what it reads), but all calls on one device share it: calls that overlap
+ * in time on the same device (several streams, several threads) race and must not be issued.
+ * No allocation, no synchronisation, no memset: asynchronous on `stream`. */
+pa_status pa_decode_no_alloc(pa_plan_t plan, int32_t batch, int32_t q_len, int32_t num_pages,
+                             int32_t num_indices, const int32_t* kv_indptr, const int32_t* kv_indices,
+                             const int32_t* kv_last_page_len, const int32_t* cache_position,
+                             const int32_t* query_position_ids, const int32_t* key_position_ids,
+                             const void* q, const void* k_cache, const void* v_cache,
+                             const float* q_norm_weight, const float* k_norm_weight,
+                             void* out, float* lse, void* stream);
+
 /* Workspace bytes of pa_decode's multi-compute-unit schedule for `batch` rows under this
  * plan's split policy (host arithmetic only; a PA_SPLIT_FIXED plan needs room for
  * ceil(max_pages_per_row * 16 / N) chunk states per (row, KV head)). */
