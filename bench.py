@@ -640,8 +640,9 @@ def main():
                          "traffic": None, "kernel": PREFILL_KERNELS + " (whole call)",
                          "algorithmic_flops_per_call": flops, "avg_call_ms": round(p_launch, 5)},
         }
-        print("[bench] timing the full-prefill backward", file=sys.stderr, flush=True)
-        result["prefill_backward"] = bench_backward(device, max(10, args.steps // 10), 3)
+        if not args.prefill_only:
+            print("[bench] timing the full-prefill backward", file=sys.stderr, flush=True)
+            result["prefill_backward"] = bench_backward(device, max(10, args.steps // 10), 3)
         if not args.no_cpu_baseline:
             print("[bench] timing the CPU oracle (decode, then prefill)", file=sys.stderr, flush=True)
             result["cpu_baseline"] = cpu_baseline_decode(base, alg)

@@ -324,10 +324,12 @@ struct PrefillParams {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Prefill workspace: k^ [Hkv][nnz * 16][128] bf16.
+// Prefill workspace: k^ [Hkv][nnz * 16][128] bf16, then 32 rows of padding (the attention
+// kernel loads whole 32-key tiles; the rows past a row's keys are masked, and the padding
+// keeps the last row's tile in bounds).
 inline size_t prefill_workspace_bytes(int hq, int hkv, int batch, int q_len, int num_indices) {
   (void)hq; (void)batch; (void)q_len;
-  return align256((size_t)hkv * num_indices * kPageSize * kHeadDim * 2);
+  return align256(((size_t)hkv * num_indices * kPageSize + 32) * kHeadDim * 2);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

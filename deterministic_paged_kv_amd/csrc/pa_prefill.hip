@@ -12,42 +12,28 @@
 //     to the workspace, [Hkv][nnz * 16][128], key j of row b at (kv_indptr[b] * 16 + j);
 //     slots past a row's length are written as zeros.
 //  2. attend_kernel: one workgroup per (block of 32 queries, row, KV head, group of up to 4
-//     query heads); wavefront w handles one query head of the KV head's GQA group and runs
-//     the prologue of its own queries.  Key tiles of 32 (2 pages) are visited in ascending
-//     order up to the block's last visible key; the workgroup stages each tile's k^ and V in
-//     LDS once for all its heads, with two tiles' loads in flight, and the step is software-
-//     pipelined (the scores of the next tile on the matrix cores during this tile's softmax).
-//     Long and short items are paired on compute units.  Per tile: S^T = K^ Q^T (bf16 MFMA, FP32 accumulation), causal mask on logical
-//     positions (key j visible to a query at position p iff j <= p) on tiles that cross the
-//     diagonal, FP32 online softmax with a fixed reduction order, O^T += V^T P^T (P rounded
-//     to bf16 for the MFMA, FP32 accumulation).  The softmax reference of a query follows its
-//     running maximum lazily (moved only when exceeded by more than 2^8 in probability), which
-//     leaves out = sum(p v) / sum(p) and the LSE unchanged up to rounding.
+//     query heads); each wavefront holds 16 queries of two query heads of the KV head's GQA
+//     group and runs the prologue of its own queries.  Key tiles of 32 (2 pages) are split
+//     into two fixed streams (even and odd tiles) walked in ascending order up to the block's
+//     last visible key and merged at the end in stream order; the workgroup stages each tile's
+//     k^ and V in LDS once for all its heads, with loads two to three steps ahead, and each
+//     step overlaps the scores of the next tile and P.V of the previous one with the softmax
+//     of the current one.  Long items are placed first.  Per tile: S^T = K^ Q^T (bf16 MFMA,
+//     FP32 accumulation), causal mask on logical positions (key j visible to a query at
+//     position p iff j <= p) on tiles that cross the diagonal, FP32 online softmax with a
+//     fixed reduction order, O^T += V^T P^T (P rounded to bf16 for the MFMA, FP32
+//     accumulation).  The softmax reference of a query follows its running maximum lazily
+//     (moved only when exceeded by more than 2^8 in probability), which leaves
+//     out = sum(p v) / sum(p) and the LSE unchanged up to rounding.
 //  The tiling is a constant of the library, so each row's reduction order depends only on
 //  the row itself, never on the batch or the plan width.
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
 
 namespace {
-
-constexpr int kQBlock = 32;          // queries per work item (two 16-row MFMA tiles)
-constexpr int kKT = 32;              // keys per tile (2 pages)
-constexpr int kRow = kHeadDim + 16;  // LDS row, padded by 32 bytes (conflict-free transposed reads)
-// Workgroup shape: H wavefronts per query head, each taking 32 / H of the item's 32 queries
-// (H = 1: one wavefront per head with both 16-query tiles; H = 2: two wavefronts per head with
-// one tile each).  Every query's arithmetic is the same either way (the bits are identical);
-// H = 2 doubles the wavefronts that walk one item's keys, which shortens the longest items.
-template <int H>
-struct Shape {
-  static constexpr int kQT = kQBlock / 16 / H;         // 16-query MFMA tiles per wavefront
-  static constexpr int kThreads = 256 * H;             // 4 query heads x H wavefronts
-  static constexpr int kTileRows = kThreads / 16;      // tile rows one pass of the threads covers
-  static constexpr int kRowsPerThread = 32 / kTileRows;  // key rows of a 32-key tile per thread
-};
-// A query's softmax reference is moved only when a tile's scaled score exceeds it by more
-// than this (log2 domain), so probabilities stay below 2^8 and rescaling is rare.
-constexpr float kLazyMax = 8.0f;
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(uint16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -96,8 +82,15 @@ __device__ __forceinline__ bool indptr_prefix_monotone(const int32_t* indptr, in
 // and issues the K loads of all HG heads before the first prologue, so the 16 positions' cos/sin
 // (512 B each) are fetched once per HG heads.  Only the keys of valid rows are written; nothing
 // reads the other slots.
+//
+// Workspace layout: per KV head, one 4 KB block per index slot (kv_indptr[b] + page), holding
+// the page's 16 keys transposed, [128 dims][16 keys]; the attention kernel copies a tile's two
+// blocks to LDS as they are and reads its k^ operands with transposed LDS reads.  The wavefront
+// transposes each block through 4.5 KB of LDS of its own.
+constexpr int kTRow = kHeadDim + 16;  // row of the transposing buffer, padded by 32 bytes
 template <int HG>
 __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh) {
+  __shared__ __attribute__((aligned(16))) uint16_t tr_buf[4][kPageSize][kTRow];
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
@@ -142,14 +135,26 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P
     for (int h = 0; h < HG; ++h)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) raw[h][kb] = live ? ldg16(P.k_cache + src + h * kHeadDim + 32 * kb) : zero4;
+    uint16_t(&tb)[kPageSize][kTRow] = tr_buf[threadIdx.x >> 6];
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
       bf16x8 op[4];
       prologue_operand(raw[h], kw, knorm, P.eps, cs, op);
-      uint16_t* dst =
-          kh + ((size_t)(hk0 + h) * P.num_indices * kPageSize + (size_t)(p0 + pr) * kPageSize + r) * kHeadDim + 8 * g;
+      // key r's 128 values into row r of the transposing buffer, then out as [dim][key]: a
+      // transposed read gives lane (G, i) = (lane / 16, lane % 16) keys 4 G .. 4 G + 3 of dim
+      // 16 c + i, 8 contiguous bytes of the block's row for that dim
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) stg16(dst + 32 * kb, !key_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
+      for (int kb = 0; kb < 4; ++kb)
+        *reinterpret_cast<uint4*>(&tb[r][32 * kb + 8 * g]) = !key_ok ? nan4 : (live ? as_u4(op[kb]) : zero4);
+      wave_lds_sync();
+      uint16_t* blk = kh + ((size_t)(hk0 + h) * P.num_indices + (size_t)(p0 + pr)) * kPageSize * kHeadDim;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(&tb[4 * g + ((lane & 15) >> 2)][16 * c + 4 * (lane & 3)]));
+        *reinterpret_cast<i16x4*>(blk + (16 * c + (lane & 15)) * kPageSize + 4 * g) = v;
+      }
+      wave_lds_sync();
     }
   }
 }
@@ -165,10 +170,96 @@ void launch_key_prologue(const PrefillParams& p, uint16_t* kh, hipStream_t strea
 // ---------------------------------------------------------------------------------------
 // 2. causal attention: q^ made here, k^ from the workspace, V from the pages
 // ---------------------------------------------------------------------------------------
-struct AttendSmem {
-  uint16_t k[3][kKT][kRow];
-  uint16_t v[3][kKT][kRow];
+// Work item: (row b, KV head hk, group hg of up to 4 query heads of hk's GQA group, block of
+// 32 queries).  Eight wavefronts, two per SIMD.  Wavefront w holds 32 query rows: the 16
+// queries 16 qg .. 16 qg + 15 of the block (qg = (w >> 1) & 1) of the two head slots
+// 2 hp, 2 hp + 1 (hp = w >> 2), the GQA group packed into the matrix N dimension, and walks
+// key stream st = w & 1 of the item: stream 0 takes the 32-key tiles 0, 2, 4, ..., stream 1
+// the tiles 1, 3, 5, ...  Each stream is an FP32 online softmax over its tiles in ascending
+// order; at the end the two streams of each query row are merged in the order stream 0,
+// stream 1.  The split depends only on the row (its tile count), never on the batch or the
+// plan.
+//
+// Per tile and wavefront (v_mfma_f32_32x32x16_bf16; lane l holds MFMA column n = l % 32 and
+// half hh = l / 32):
+//   S^T [32 keys x 32 query rows] = K^ Q^T     8 MFMAs (8 dim steps)
+//   softmax on S^T                              lane (n, hh) holds 16 keys of query row n
+//   O^T [128 dims x 32 rows] += V^T P^T          8 MFMAs (4 dim blocks x 2 key steps)
+// Column n is query 16 qg + n % 16 of head slot 2 hp + n / 16.  S^T register i of lane
+// (n, hh) is key 8 (i / 4) + 4 hh + i % 4 of the tile; rounded to BF16 those registers are
+// directly the B operand of the P.V MFMA, with V^T's k-slots read from LDS in the same key
+// order (two transposed 4-key reads per operand).
+//
+// The walk is software-pipelined in every wavefront: between two workgroup barriers (step t)
+// a wavefront computes S of tile t + 1 and adds P.V of tile t - 1 on the matrix cores while
+// its vector units run the softmax of tile t; the three do not depend on one another, so the
+// matrix cores and the vector units overlap.  hp only picks which loads the wavefront issues
+// (hp = 0: k^ tiles, three steps ahead; hp = 1: V pages, two steps ahead).
+constexpr int kQB = 32;              // queries per work item
+constexpr int kKT = 32;              // keys per tile (2 pages)
+constexpr int kStreams = 2;          // key streams per item
+constexpr int kBufs = 4;             // LDS tile buffers per stream
+constexpr int kAttendThreads = 512;
+// A query row's softmax reference moves only when a tile's probabilities, taken against the
+// current reference, sum past 2^kLazyMax in one lane (or the reference is still unset): the
+// fix-up then moves it to the row maximum if that exceeds it by more than kLazyMax (log2
+// domain), so every probability stays below 2^kLazyMax and rescaling is rare.
+constexpr float kLazyMax = 8.0f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One tile of one stream in LDS.  k^: the tile's two page blocks as the key prologue wrote
+// them, each [128 dims][16 keys].  V: 32 rows of 256 bytes at a pitch of 320 bytes (the
+// padding keeps the transposed V reads free of bank conflicts).  Both layouts were chosen by
+// measurement: transposed reads of these shapes run at about twice the rate of 16-byte row
+// reads of k^.
+constexpr int kVRow = kHeadDim + 32;         // V row pitch (elements)
+constexpr int kVRowChunks = kVRow / 8;       // 16-byte chunks per V row (16 data + 4 padding)
+struct alignas(16) TileBuf {
+  uint16_t k[2][kHeadDim][kPageSize];
+  uint16_t v[kKT][kVRow];
 };
+
+struct alignas(16) AttendSmem {
+  union {
+    TileBuf tiles[kStreams][kBufs];            // the walk (144 KB + 8 KB)
+    uint16_t qx[8][32][kHeadDim];              // q^ from the prologue layout to the operand layout
+    float merge[4][2 + 64][64];                // stream 1's states, read by stream 0 at the end
+  } u;
+};
+
+// LDS byte address of a shared-memory pointer (the direct-to-LDS loads take it in M0).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
+}
+
+// One wave-wide direct-to-LDS load: lane l reads the 16 bytes at base + voff (voff per lane)
+// and they land at LDS byte lds + 16 l.  Issued as inline assembly so that the compiler's
+// own wait-count tracking, which cannot tell these writes from the LDS reads of other
+// buffers and would wait for every load in flight before any LDS read, leaves them alone:
+// completion is waited for explicitly (s_waitcnt vmcnt) before the workgroup barrier that
+// publishes a tile.  No other vector-memory load is in flight in the walk.
+// lds and base are wave-uniform; readfirstlane keeps them in scalar registers even where the
+// compiler's divergence analysis cannot tell.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const void* base, uint32_t voff) {
+  // (readfirstlane returns a signed int: each half goes through uint32_t before it is widened,
+  // or the low half would be sign-extended into the high one)
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(bs)
+               : "memory");
+}
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Work placement: tiles per unit, and the unit picked.
 constexpr int kMaxRankUnits = 512;
@@ -176,28 +267,6 @@ struct RankSmem {
   int tiles[kMaxRankUnits];
   int sel;
 };
-
-// The tile's share of one thread: k^ and V rows rt + kTileRows u of the tile (rt = tid / 16),
-// 16 bytes each at column chunk tid % 16.  Keys past the row's end read the row's last key, so
-// every load is in bounds and finite (their scores are masked and their probabilities are 0).
-template <int H>
-struct TileRegs {
-  uint4 k[Shape<H>::kRowsPerThread];
-  uint4 v[Shape<H>::kRowsPerThread];
-};
-
-template <int H>
-__device__ __forceinline__ void store_tile(const TileRegs<H>& tr, AttendSmem& sm, int buf, int tid) {
-  constexpr int kTileRows = Shape<H>::kTileRows;
-  constexpr int kRowsPerThread = Shape<H>::kRowsPerThread;
-  const int rt = tid >> 4;
-  const int col = tid & 15;
-#pragma unroll
-  for (int u = 0; u < kRowsPerThread; ++u) {
-    *reinterpret_cast<uint4*>(&sm.k[buf][kTileRows * u + rt][col * 8]) = tr.k[u];
-    *reinterpret_cast<uint4*>(&sm.v[buf][kTileRows * u + rt][col * 8]) = tr.v[u];
-  }
-}
 
 // Units (row b, query block qb) are numbered u = (nqb - 1 - qb) * batch + b.  The key tiles a
 // unit visits: its row's keys up to the last query's position (the block's last query stands
@@ -211,7 +280,7 @@ __device__ int unit_tiles(const PrefillParams& P, int nqb, int u) {
   const bool bad = p0 < 0 || n < 0 || p1 > P.num_indices || n > P.max_pages_per_row ||
                    (n > 0 && (lpl < 1 || lpl > kPageSize));
   const int L = (n > 0 && !bad) ? (n - 1) * kPageSize + lpl : 0;
-  const int i_last = min(qb * kQBlock + kQBlock - 1, P.q_len - 1);
+  const int i_last = min(qb * kQB + kQB - 1, P.q_len - 1);
   int qlast = P.qpos[(size_t)b * P.q_len + i_last];
   if (qlast < 0 || qlast >= P.table_rows) qlast = -1;
   const int kend = min(L, qlast + 1);
@@ -237,336 +306,424 @@ __device__ int unit_of_rank(const PrefillParams& P, int nqb, int U, int target, 
   return rs.sel;
 }
 
-template <int H>
-__global__ __launch_bounds__(256 * H) __attribute__((amdgpu_waves_per_eu(2 * H, 2 * H))) void attend_kernel(
+__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_kernel(
     const PrefillParams P, const uint16_t* __restrict__ kh) {
-  constexpr int kQT = Shape<H>::kQT;
-  constexpr int kAttendThreads = Shape<H>::kThreads;
-  constexpr int kTileRows = Shape<H>::kTileRows;
-  constexpr int kRowsPerThread = Shape<H>::kRowsPerThread;
   __shared__ AttendSmem sm;
   __shared__ RankSmem sched;
   const int G = P.group;
   const int Hkv = P.num_kv_heads;
   const int Sq = P.q_len;
-  const int nqb = (Sq + kQBlock - 1) / kQBlock;
+  const int nqb = (Sq + kQB - 1) / kQB;
   const int nhg = (G + 3) / 4;
   const int tid = threadIdx.x;
   // This workgroup's item: a unit (row b, query block qb) and a head slot (KV head hk, group
-  // of query heads hg).  The order only places work; every item's arithmetic is the same
+  // hg of query heads).  Consecutive workgroups take consecutive head slots of the same rank,
+  // so the dispatch's round robin over the XCDs keeps each head slot's k^ and V in few L2s;
+  // ranks go longest first.  The order only places work; every item's arithmetic is the same
   // wherever it runs.
   const int HH = Hkv * nhg;
   const int U = P.batch * nqb;
-  const int N = U * HH;
-  int unit, head;
-  if (N > P.num_cus && N <= 2 * P.num_cus && U <= kMaxRankUnits) {
-    // One dispatch round that puts workgroups i and i + num_cus on the same compute unit:
-    // give them the items of ranks k and N-1-k of the longest-first order (ranked by the
-    // number of key tiles each unit visits), so every compute unit holds one long and one
-    // short item.
-    const int rank = (int)blockIdx.x < P.num_cus ? (int)blockIdx.x : N - 1 - ((int)blockIdx.x - P.num_cus);
-    unit = unit_of_rank(P, nqb, U, rank / HH, tid, kAttendThreads, sched);
-    head = rank % HH;
-  } else {
-    // Otherwise longest first in launch order: the last query blocks of every row see the
-    // most keys.
-    unit = (int)blockIdx.x / HH;
-    head = (int)blockIdx.x % HH;
-  }
+  const int rank = (int)blockIdx.x / HH;
+  const int head = (int)blockIdx.x % HH;
+  const int unit = U <= kMaxRankUnits ? unit_of_rank(P, nqb, U, rank, tid, kAttendThreads, sched) : rank;
   const int qb = nqb - 1 - unit / P.batch;
   const int b = unit % P.batch;
   const int hg = head % nhg;
   const int hk = head / nhg;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = wave >> 2;         // which 32 / H queries of the block (0 when H = 1)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int st = w & 1;         // key stream
+  const int qg = (w >> 1) & 1;  // query group: queries 16 qg .. 16 qg + 15 of the block
+  const int hp = w >> 2;        // head pair: slots 2 hp, 2 hp + 1; also the step phase
+  const int role = 2 * hp + qg; // which part of the stream's tile loads this wavefront issues
   const int lane = tid & 63;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int gi = hg * 4 + (wave & 3);  // head within the GQA group
-  const bool head_live = gi < G;      // trailing waves of a partial group only help stage tiles
-  const int h = hk * G + (head_live ? gi : 0);
+  const int n = lane & 31;
+  const int hh = lane >> 5;
 
   const int p0 = P.indptr[b];
   const int p1 = P.indptr[b + 1];
-  const int n = p1 - p0;
+  const int nidx = p1 - p0;
   const int lpl = P.last_page_len[b];
   const bool mono = indptr_prefix_monotone(P.indptr, b, tid, kAttendThreads);
-  const bool bad = !mono || p0 < 0 || n < 0 || p1 > P.num_indices || n > P.max_pages_per_row ||
-                   (n > 0 && (lpl < 1 || lpl > kPageSize));
-  const int L = (n > 0 && !bad) ? (n - 1) * kPageSize + lpl : 0;
+  const bool bad = !mono || p0 < 0 || nidx < 0 || p1 > P.num_indices || nidx > P.max_pages_per_row ||
+                   (nidx > 0 && (lpl < 1 || lpl > kPageSize));
+  const int L = (nidx > 0 && !bad) ? (nidx - 1) * kPageSize + lpl : 0;
 
-  // positions of the block's queries (-1: past the chunk, sees nothing): every wavefront takes
-  // the first and last key positions over all 32 (the tile walk is the block's, the same in
-  // every wavefront), then keeps those of its own 16
-  int qp_blk[kQBlock / 16];
+  // Positions of the block's 32 queries (-1: past the chunk, sees nothing).  Every wavefront
+  // takes the first and last positions over all 32 (the tile walk is the block's, the same in
+  // every wavefront), then keeps the one of its lane's query.
   int poison = bad;
-#pragma unroll
-  for (int t = 0; t < kQBlock / 16; ++t) {
-    const int i = qb * kQBlock + 16 * t + r;
-    qp_blk[t] = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
+  int qp_all;
+  {
+    const int i = qb * kQB + n;  // lanes n and n + 32 read the same query
+    qp_all = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
     const int cp = i < Sq ? P.cache_position[(size_t)b * Sq + i] : -1;
-    if (i < Sq && (qp_blk[t] < 0 || qp_blk[t] >= P.table_rows || cp != qp_blk[t])) { poison = 1; qp_blk[t] = -1; }
+    if (i < Sq && (qp_all < 0 || qp_all >= P.table_rows || cp != qp_all)) { poison = 1; qp_all = -1; }
   }
-  int qp[kQT];
-  int i_of[kQT];
+  int qmax = qp_all, qmin = qp_all < 0 ? INT32_MAX : qp_all;
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) {
-    i_of[t] = qb * kQBlock + 16 * (half * kQT + t) + r;
-    qp[t] = half == 0 ? qp_blk[t] : qp_blk[kQT + t];
-  }
-  int qmax = qp_blk[0], qmin = qp_blk[0] < 0 ? INT32_MAX : qp_blk[0];
-#pragma unroll
-  for (int t = 1; t < kQBlock / 16; ++t) {
-    qmax = max(qmax, qp_blk[t]);
-    if (qp_blk[t] >= 0) qmin = min(qmin, qp_blk[t]);
-  }
-#pragma unroll
-  for (int sh = 1; sh < 16; sh <<= 1) {
+  for (int sh = 1; sh < 32; sh <<= 1) {
     qmax = max(qmax, __shfl_xor(qmax, sh));
     qmin = min(qmin, __shfl_xor(qmin, sh));
   }
-  // identical in every lane after the exchange: make them wave-uniform (scalar)
   qmax = __builtin_amdgcn_readfirstlane(qmax);
   qmin = __builtin_amdgcn_readfirstlane(qmin);
   const int kend = min(L, qmax + 1);
   const int ntiles = kend > 0 ? (kend + kKT - 1) / kKT : 0;
+  const int nsteps = (ntiles + kStreams - 1) / kStreams;
   // tiles ending at or before this key need no mask: every key is < L and <= every query
   const int free_end = min(L, qmin == INT32_MAX ? 0 : qmin + 1);
+  // this lane's query (column n: query 16 qg + n % 16) and the last key it may see + 1
+  const int qi = qb * kQB + 16 * qg + (n & 15);
+  const int qp = __shfl(qp_all, 16 * qg + (n & 15));
+  const int lim = min(L, qp + 1);
 
-  // q^ of this wavefront's queries, in the operand layout (vector r = query 16t + r)
-  bf16x8 qop[kQT][4];
+  // ---- q^ of the wavefront's 32 query rows, in the B-operand layout of the S MFMAs
+  // The shared prologue runs in its own layout (lane r + 16 g: query r, dims 32 kb + 8 g ..),
+  // once per head slot; the results go through LDS to lane (n, hh): row n, dims 16 s + 8 hh ..
+  // +7 for s = 0..7.
+  bf16x8 qop[8];
   {
+    const int r = lane & 15;
+    const int g = lane >> 4;
     const bool qnorm = P.q_norm != nullptr;
-    float w[32];
+    float wq[32];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
+      for (int e = 0; e < 8; ++e) wq[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
+    const int qi_r = qb * kQB + 16 * qg + r;
+    const int qp_r = __shfl(qp_all, 16 * qg + r);
+    float4 cs[8];
+    load_cos_sin(P.rope, max(qp_r, 0), g, cs);
 #pragma unroll
-    for (int t = 0; t < kQT; ++t) {
+    for (int k = 0; k < 2; ++k) {
+      const int gi = hg * 4 + 2 * hp + k;
+      const bool live = gi < G && qi_r < Sq;
       uint4 raw[4];
-      const bool live = head_live && i_of[t] < Sq;
-      const size_t off = (((size_t)b * P.num_q_heads + h) * Sq + (live ? i_of[t] : 0)) * kHeadDim + 8 * g;
+      const size_t off = (((size_t)b * P.num_q_heads + hk * G + (gi < G ? gi : 0)) * Sq + (qi_r < Sq ? qi_r : 0)) *
+                             kHeadDim + 8 * g;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.q + off + 32 * kb) : make_uint4(0, 0, 0, 0);
-      float4 cs[8];
-      load_cos_sin(P.rope, max(qp[t], 0), g, cs);
-      prologue_operand(raw, w, qnorm, P.eps, cs, qop[t]);
-    }
-  }
-
-  // Per query: reference m (log2 domain, scaled), m_neg = -m (0 while m is -inf), and this
-  // lane's partial sum of p over its own key slots (the four lanes of a query are summed once,
-  // in a fixed order, at the end).
-  float m_run[kQT], m_neg[kQT], l_part[kQT];
-  f32x4 acc[kQT][8];
-#pragma unroll
-  for (int t = 0; t < kQT; ++t) {
-    m_run[t] = -__builtin_inff();
-    m_neg[t] = 0.0f;
-    l_part[t] = 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const uint16_t* kh_row0 = kh + ((size_t)hk * P.num_indices + p0) * kPageSize * kHeadDim;  // key 0 of the row
-  const int jr = 4 * g + (r >> 2);  // transposed-read row within a 16-key subtile
-  const int jc = 4 * (r & 3);
-
-  // Software pipeline over 32-key tiles: three LDS buffers and a ring of three register sets.
-  // At the start of step kt, tiles kt and kt+1 are in LDS (buffers kt % 3 and (kt+1) % 3),
-  // S(kt) is in registers and tile kt+2 is in flight or in registers.  Step kt:
-  //   A. S(kt+1) = K^(kt+1) Q^T on the matrix cores while the vector unit runs the softmax of
-  //      S(kt) with the current references (straight-line code); a rare fix-up follows when
-  //      some query's reference has to move.
-  //   B. the loads of tile kt+3 are issued, O^T += V(kt)^T P(kt)^T, tile kt+2 goes to LDS
-  //      buffer (kt+2) % 3 (free since the barrier that ended step kt-1), barrier.
-  // Tiles past the block's last one are loaded, stored and multiplied all the same (keys and
-  // pages clamped to the row's last key, so every access is in bounds and finite); their
-  // results are never used.  Page numbers come through vector loads (one per tile, lane u
-  // holding the page of the tile's half u), so no scalar load shares a counter with the LDS
-  // reads.
-  constexpr int kRing = 3;
-  TileRegs<H> ring[kRing];
-  const int32_t* row_idx = P.indices + p0;
-  const size_t page_elems = (size_t)kPageSize * Hkv * kHeadDim;
-  const int rt = tid >> 4;
-  const int col = tid & 15;
-  const uint32_t v_lane_off = (uint32_t)hk * kHeadDim + col * 8;
-  static_assert(kTileRows % 16 == 0 || kRowsPerThread * kTileRows == 32, "tile rows must split into pages");
-  // page numbers of tile t (lane u: page min(2t + u, n - 1)); only called with n >= 1
-  auto page_vec = [&](int t) -> int { return row_idx[min(2 * t + (lane & 1), n - 1)]; };
-  auto load = [&](TileRegs<H>& tr, int t, int pv) {
-#pragma unroll
-    for (int u = 0; u < kRowsPerThread; ++u) {
-      const int ro = kTileRows * u + rt;  // row of the tile; its page is the tile's half ro / 16
-      int phys = __builtin_amdgcn_readlane(pv, __builtin_amdgcn_readfirstlane(ro >> 4));
-      // only the block's own tiles count: the ring also loads up to three tiles past the
-      // last one, whose results are thrown away
-      if (phys < 0 || phys >= P.num_pages) { poison |= t < ntiles ? 1 : 0; phys = 0; }
-      const int j = min(t * kKT + ro, L - 1);  // logical key (clamped)
-      tr.k[u] = ldg16(kh_row0 + (uint32_t)j * kHeadDim + col * 8);
-      tr.v[u] = ldg16(P.v_cache + (size_t)phys * page_elems + ((uint32_t)(j & (kPageSize - 1)) * Hkv * kHeadDim + v_lane_off));
-    }
-  };
-  // S^T = K^ Q^T for the two 16-key subtiles of the tile in LDS buffer `buf`
-  auto scores = [&](int buf, f32x4 (&out)[kQT][2]) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 ka[4];
+      bf16x8 op[4];
+      prologue_operand(raw, wq, qnorm, P.eps, cs, op);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
-#pragma unroll
-      for (int t = 0; t < kQT; ++t) {
-        out[t][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          out[t][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[t][kb], out[t][ks], 0, 0, 0);
-      }
+        *reinterpret_cast<uint4*>(&sm.u.qx[w][16 * k + r][32 * kb + 8 * g]) = as_u4(op[kb]);
     }
-  };
-  // last key position + 1 each query may see (0: none)
-  int lim[kQT];
+    wave_lds_sync();
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) lim[t] = min(L, qp[t] + 1);
-
-  int pv_next = 0;
-  if (ntiles > 0) {
-    const int pv0 = page_vec(0), pv1 = page_vec(1), pv2 = page_vec(2);
-    load(ring[0], 0, pv0);
-    load(ring[1], 1, pv1);
-    load(ring[2], 2, pv2);
-    pv_next = page_vec(3);
-    store_tile<H>(ring[0], sm, 0, tid);
-    store_tile<H>(ring[1], sm, 1, tid);
+    for (int s = 0; s < 8; ++s)
+      qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.u.qx[w][n][16 * s + 8 * hh]));
   }
-  __syncthreads();
-  f32x4 sc[kQT][2];
-  if (ntiles > 0) scores(0, sc);
+  __syncthreads();  // the q^ exchange area becomes tile buffers
 
-  // p = 2^(s c - m) of a query's 8 scores in this lane, their sum (in key order) and BF16 copy
-  auto tile_p = [&](const f32x4 (&s_)[2], float mneg, float& sum, i16x4 (&pbt)[2]) {
-    float p[2][4];
+  // ---- the walk
+  float m_run = -__builtin_inff(), m_neg = 0.0f, l_part = 0.0f;
+  f32x16 acc[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[ks][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[ks][i], kScoreScaleLog2, mneg));
-    sum = p[0][0];
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+  TileBuf(&tb)[kBufs] = sm.u.tiles[st];
+  // Direct-to-LDS loads of the stream's tiles.  One load instruction writes 1 KB of
+  // contiguous LDS, lane l the 16 bytes at 16 l.  k^: the tile's two page blocks are 8 KB of
+  // contiguous workspace copied as they are (8 instructions; the second block of a row's last
+  // tile may lie past the row: its keys are masked, and the workspace is padded so the copy
+  // stays in bounds).  V: LDS chunk p = 64 u + l of the tile (10 instructions) is row p / 20,
+  // chunk p % 20 (chunks 16-19 are the row's padding and get a copy of chunk 15); rows 0-15
+  // are page 2 kt (instructions 0-4), rows 16-31 page 2 kt + 1 (instructions 5-9), slot = row
+  // % 16; keys past the row's end read its last key, so every value read is finite (their
+  // probabilities are 0).  The stream's four wavefronts split them by role: 0 and 1 issue k^
+  // 0-3 and 4-7, 2 and 3 issue the first and second page of V.
+  const char* kh_plane = (const char*)(kh + ((size_t)hk * P.num_indices + p0) * kPageSize * kHeadDim);
+  const uint32_t v_row_bytes = (uint32_t)Hkv * kHeadDim * 2u;
+  constexpr int kDma = 5;                       // most load instructions of one role per step
+  const int dma_n = role < 2 ? 4 : 5;           // instructions issued per step
+  const int dma_u0 = role < 2 ? 4 * role : 5 * (role - 2);  // its first instruction
+  uint32_t doff[kDma];  // roles 0, 1: byte offset in the tile's k^; roles 2, 3: byte offset in the page
 #pragma unroll
-    for (int e = 1; e < 8; ++e) sum += p[e >> 2][e & 3];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) pbt[ks] = pack_bf16(p[ks][0], p[ks][1], p[ks][2], p[ks][3]);
+  for (int i = 0; i < kDma; ++i) {
+    const int pc = 64 * (dma_u0 + i) + lane;
+    const int row = pc / kVRowChunks;
+    const int ch = min(pc - row * kVRowChunks, 15);
+    doff[i] = role < 2 ? 16u * pc : (uint32_t)(row & 15) * v_row_bytes + 16u * ch;
+  }
+  // The walk is written once per phase (HP = hp: 0 loads k^ and computes S at the start of a
+  // step, 1 loads V and computes S at its end), so neither path branches on its role.
+  // Physical page of this wavefront's half of the stream's tile at step t (clamped to the
+  // row); phase 0 needs none.
+  auto page_of = [&](auto hpc, int t) -> int {
+    constexpr int HP = decltype(hpc)::value;
+    const int kt = kStreams * t + st;
+    if constexpr (HP == 0) return 0;
+    else return nidx > 0 ? load_uniform(P.indices, p0 + min(2 * kt + qg, nidx - 1)) : 0;
   };
-  auto step = [&](const int kt, TileRegs<H>& to_load, TileRegs<H>& to_store) {
-    // ---- A: causal mask (tiles that reach past the block's first query), then S(kt+1) and
-    // the softmax of S(kt)
-    if ((kt + 1) * kKT > free_end) {
+  auto issue = [&](auto hpc, int t, int buf, int phys) {
+    constexpr int HP = decltype(hpc)::value;
+    const int kt = kStreams * t + st;
+    if constexpr (HP == 0) {
+      const char* kb = kh_plane + (size_t)min(kt, ntiles - 1) * 2 * kPageSize * kHeadDim * 2;
+      const uint32_t dst = lds_address(&tb[buf].k[0][0][0]) + 1024u * dma_u0;
 #pragma unroll
-      for (int t = 0; t < kQT; ++t) {
-        const int d = lim[t] - kt * kKT - 4 * g;  // key 16 ks + 4 g + i is visible iff 16 ks + i < d
+      for (int i = 0; i < 4; ++i) lds_dma16(dst + 1024u * i, kb, doff[i]);
+    } else {
+      // only the item's own tiles count: the walk also loads for steps past a stream's end
+      if (phys < 0 || phys >= P.num_pages) { poison |= kt < ntiles ? 1 : 0; phys = 0; }
+      const char* vb = (const char*)(P.v_cache + ((size_t)phys * kPageSize * Hkv + hk) * kHeadDim);
+      const uint32_t dst = lds_address(&tb[buf].v[0][0]) + 1024u * dma_u0;
+      // the last slot of the page holding a key of the row (15 unless the page reaches the
+      // row's end): the slots after it read that one
+      const int smax = 2 * kt + qg >= nidx - 1 ? lpl - 1 : 15;
+      if (smax == 15) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int i = 0; i < 5; ++i) lds_dma16(dst + 1024u * i, vb, doff[i]);
+      } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[t][ks][i] = 16 * ks + i < d ? sc[t][ks][i] : -__builtin_inff();
-      }
-    }
-    f32x4 sn[kQT][2];
-    scores((kt + 1) % 3, sn);
-    float mx[kQT], lp[kQT];
-    i16x4 pb[kQT][2];
-    bool need = false;
-#pragma unroll
-    for (int t = 0; t < kQT; ++t) {
-      // raw-score maximum of this lane's keys (the scale c > 0 commutes with max)
-      mx[t] = max3f(max3f(max3f(sc[t][0][0], sc[t][0][1], sc[t][0][2]), max3f(sc[t][0][3], sc[t][1][0], sc[t][1][1]),
-                          sc[t][1][2]),
-                    sc[t][1][3], sc[t][1][3]);
-      need |= mx[t] * kScoreScaleLog2 > m_run[t] + kLazyMax;
-      // p = 2^(s c - m) with the current reference (0 for masked keys, and while m is -inf)
-      tile_p(sc[t], m_neg[t], lp[t], pb[t]);
-    }
-    // Fix-up, rare: a query whose tile maximum exceeds its reference by more than kLazyMax
-    // (the test is exact per query: a lane's keys are a subset of the query's) moves its
-    // reference to the tile's scaled maximum, rescales what it has summed so far, and
-    // recomputes the tile's p.
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int t = 0; t < kQT; ++t) {
-        const float rowmax = pair32_max(pair16_max(mx[t])) * kScoreScaleLog2;
-        if (rowmax > m_run[t] + kLazyMax) {
-          const float alpha = m_run[t] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run[t] - rowmax);
-          m_run[t] = rowmax;
-          m_neg[t] = -rowmax;
-          l_part[t] *= alpha;
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) acc[t][nb] = acc[t][nb] * alpha;
-          tile_p(sc[t], m_neg[t], lp[t], pb[t]);
+        for (int i = 0; i < 5; ++i) {
+          const int pc = 64 * (dma_u0 + i) + lane;
+          const int row = pc / kVRowChunks;
+          const int ch = min(pc - row * kVRowChunks, 15);
+          lds_dma16(dst + 1024u * i, vb, (uint32_t)min(row & 15, smax) * v_row_bytes + 16u * ch);
         }
       }
     }
-#pragma unroll
-    for (int t = 0; t < kQT; ++t) l_part[t] += lp[t];
-    // ---- B: loads of tile kt+3, P.V of tile kt, tile kt+2 to LDS
-    const int pv = pv_next;
-    pv_next = page_vec(kt + 4);
-    load(to_load, kt + 3, pv);
-    // O^T += V^T P^T over the tile's 32 keys in one K=32 MFMA per (query tile, column block):
-    // k-slot 8g+e holds key 4g+e for e < 4 and key 16+4g+(e-4) for e >= 4, in both operands.
-    // V^T comes from two transposed LDS reads (one per 16-key subtile).
-    const int buf = kt % 3;
-    bf16x8 pk[kQT];
-#pragma unroll
-    for (int t = 0; t < kQT; ++t) pk[t] = __builtin_bit_cast(bf16x8, concat4(pb[t][0], pb[t][1]));
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][jr][16 * nb + jc]));
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.v[buf][16 + jr][16 * nb + jc]));
-      const bf16x8 va = __builtin_bit_cast(bf16x8, concat4(v0, v1));
-#pragma unroll
-      for (int t = 0; t < kQT; ++t)
-        acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t], acc[t][nb], 0, 0, 0);
+  };
+  // End of step t: step t + 1 computes the scores of tile t + 2 and adds P.V of tile t, so
+  // k^ of step t + 2 (issued at step t - 1) and V of step t (issued at step t - 2) must have
+  // landed.  The loads issued after them may stay in flight: k^ of step t + 3 (4 instructions),
+  // V of steps t + 1 and t + 2 (5 each).  Loads complete in issue order.
+  auto wait_end = [&](auto hpc, int t) {
+    constexpr int HP = decltype(hpc)::value;
+    if constexpr (HP == 0) {
+      if (t + 3 < nsteps) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+    } else {
+      if (t + 2 < nsteps) wait_vmcnt<10>();
+      else if (t + 1 < nsteps) wait_vmcnt<5>();
+      else wait_vmcnt<0>();
     }
+  };
+  // The k^ operand of dim step s, lane (n, hh): key n, dims 16 s + 8 hh .. +7, two transposed
+  // reads of the block holding key n (lane group G = lane / 16 reads dims 16 s + 8 (G / 2) +
+  // 4 x .. +3 of keys 16 (G % 2) .. +15 of that block, and lane i of the group gets key
+  // 16 (G % 2) + i).
+  const int kg = lane >> 4;
+  const int k_row = 8 * (kg >> 1) + ((lane & 15) >> 2);
+  const int k_col = 4 * (lane & 3);
+  auto read_k = [&](int buf, bf16x8 (&ka)[8]) {
 #pragma unroll
-    for (int t = 0; t < kQT; ++t)
+    for (int s = 0; s < 8; ++s) {
+      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].k[kg & 1][16 * s + k_row][k_col]));
+      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].k[kg & 1][16 * s + 4 + k_row][k_col]));
+      ka[s] = __builtin_bit_cast(bf16x8, concat4(a0, a1));
+    }
+  };
+  // S^T = k^ q^T of one tile
+  auto mma_s = [&](const bf16x8 (&ka)[8], f32x16& s_out) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) sc[t][ks] = sn[t][ks];
-    store_tile<H>(to_store, sm, (kt + 2) % 3, tid);
+    for (int i = 0; i < 16; ++i) s_out[i] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qop[s], s_out, 0, 0, 0);
+  };
+  // transposed V reads, operand 2 db + ks: key rows 16 ks + vr (+ 8), dims 32 db + vc .. +3
+  const int vr = 4 * hh + ((lane & 15) >> 2);
+  const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto read_v = [&](int buf, bf16x8 (&va)[8]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].v[16 * ks + vr][32 * db + vc]));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].v[16 * ks + 8 + vr][32 * db + vc]));
+        va[2 * db + ks] = __builtin_bit_cast(bf16x8, concat4(v0, v1));
+      }
+  };
+
+  const int key_of = 4 * hh;  // S^T register i of this lane is key 8 (i / 4) + 4 hh + i % 4 of the tile
+  // p = 2^(s C - m) of the lane's 16 keys, their sum (in register order) and the BF16 B
+  // operands of the two P.V key steps
+  auto tile_p = [&](const f32x16& sc, float mneg, float& sum, bf16x8 (&pb)[2]) {
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], kScoreScaleLog2, mneg));
+    sum = p[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) sum += p[i];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const i16x4 lo = pack_bf16(p[8 * ks + 0], p[8 * ks + 1], p[8 * ks + 2], p[8 * ks + 3]);
+      const i16x4 hi = pack_bf16(p[8 * ks + 4], p[8 * ks + 5], p[8 * ks + 6], p[8 * ks + 7]);
+      pb[ks] = __builtin_bit_cast(bf16x8, concat4(lo, hi));
+    }
+  };
+
+  // P.V of one tile: O^T += V^T P^T
+  auto mma_pv = [&](const bf16x8 (&va)[8], const bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * db + ks], pb[ks], acc[db], 0, 0, 0);
+  };
+
+  // One step of a stream's walk, between two workgroup barriers.  Tile k's k^ is loaded three
+  // steps ahead (at step k - 3) and its V two steps ahead; at the start of step t, k^ of steps t
+  // + 1 and V of steps t - 1 and t are in LDS, s_cur holds the scores of step t and pb_prev the
+  // probabilities of step t - 1.  The step computes the scores of step t + 1 and adds P.V of
+  // step t - 1 on the matrix cores while the vector units run the softmax of step t: none of the
+  // three depends on another, so the matrix cores and the vector units overlap.  A lazy
+  // reference move at step t rescales the accumulator after P.V of step t - 1 (relative to the
+  // old reference) has been added.  On a stream's last step the scores of the next buffer are
+  // computed but never used (no load into that buffer is then in flight).
+  auto step = [&](auto hpc, const int t, const int b_k, const int b_v, const int b_kload, const int b_vload,
+                  int& phys_next, f32x16& s_cur, f32x16& s_nxt, bf16x8 (&pb_prev)[2]) {
+    constexpr int HP = decltype(hpc)::value;
+    const int kt = kStreams * t + st;
+    // k^ of step t + 3 (phase 0) or V of step t + 2 (phase 1), into the buffer freed at the
+    // previous barrier
+    const int ld = HP == 0 ? t + 3 : t + 2;
+    if (ld < nsteps) {
+      const int phys = phys_next;
+      phys_next = page_of(hpc, ld + 1);
+      issue(hpc, ld, HP == 0 ? b_kload : b_vload, phys);
+    }
+    // causal mask on tiles that reach past the block's first query, and on tiles past the
+    // item's last one (a stream with one tile fewer than the other runs that step masked)
+    if (kt >= ntiles || (kt + 1) * kKT > free_end) {
+      const int d = (kt < ntiles ? lim : 0) - kt * kKT - key_of;  // key 8 (i/4) + key_of + i%4 visible iff < lim
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_cur[i] = 8 * (i >> 2) + (i & 3) < d ? s_cur[i] : -__builtin_inff();
+    }
+    bf16x8 ka[8], va[8];
+    read_k(b_k, ka);
+    read_v(b_v, va);
+    mma_pv(va, pb_prev);
+    mma_s(ka, s_nxt);
+    float lp;
+    tile_p(s_cur, m_neg, lp, pb_prev);
+    // the fix-up below runs when the probabilities against the current reference sum past
+    // 2^kLazyMax (or overflow, or are NaN), or when the reference is unset and a key is visible
+    const bool need = m_run == -__builtin_inff() ? lp != 0.0f : !(lp <= 256.0f);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      float mx = s_cur[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s_cur[i]);
+      const float rowmax = pair32_max(mx) * kScoreScaleLog2;
+      if (rowmax > m_run + kLazyMax || (m_run == -__builtin_inff() && rowmax > -__builtin_inff())) {
+        const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - rowmax);
+        m_run = rowmax;
+        m_neg = -rowmax;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = acc[db] * alpha;
+        tile_p(s_cur, m_neg, lp, pb_prev);
+      }
+    }
+    l_part += lp;
+    wait_end(hpc, t);
     __syncthreads();
   };
-  // whole rounds of the ring, then the last one or two tiles (no exit from inside a round)
-  int kt = 0;
-  for (; kt + kRing <= ntiles; kt += kRing) {
-    step(kt, ring[0], ring[2]);
-    step(kt + 1, ring[1], ring[0]);
-    step(kt + 2, ring[2], ring[1]);
-  }
-  if (kt < ntiles) step(kt, ring[0], ring[2]);
-  if (kt + 1 < ntiles) step(kt + 1, ring[1], ring[0]);
 
-  // any out-of-range page index seen by any thread poisons the whole block's output
-  const bool out_poison = __syncthreads_or(poison) != 0;
-  float l_run[kQT];
-#pragma unroll
-  for (int t = 0; t < kQT; ++t) l_run[t] = pair32_sum(pair16_sum(l_part[t]));
-#pragma unroll
-  for (int t = 0; t < kQT; ++t) {
-    const int i = i_of[t];
-    if (i >= Sq || !head_live) continue;
-    const size_t row = ((size_t)b * P.num_q_heads + h) * Sq + i;
-    const bool empty = l_run[t] == 0.0f;
-    const float inv = empty ? 0.0f : 1.0f / l_run[t];
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      uint2 w;
-      float o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = out_poison ? __builtin_nanf("") : acc[t][nb][e] * inv;
-      w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[1]) << 16);
-      w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[3]) << 16);
-      *reinterpret_cast<uint2*>(P.out + row * kHeadDim + 16 * nb + 4 * g) = w;
+  auto walk = [&](auto hpc) {
+    constexpr int HP = decltype(hpc)::value;
+    // k^ of steps 0-2 (phase 0) or V of steps 0-1 (phase 1) in flight; k^ of steps 0 and 1 has
+    // landed before the walk starts.  V buffer 3 stands in for the tile of step -1: zeros, so
+    // the first step's P.V adds nothing.
+    int phys_next = 0;
+    if (nsteps > 0) {
+      if constexpr (HP == 0) {
+        issue(hpc, 0, 0, 0);
+        issue(hpc, 1, 1, 0);
+        issue(hpc, 2, 2, 0);
+        wait_vmcnt<4>();
+      } else {
+        issue(hpc, 0, 0, page_of(hpc, 0));
+        issue(hpc, 1, 1, page_of(hpc, 1));
+        phys_next = page_of(hpc, 2);
+      }
     }
-    if (g == 0) {
-      float lse = empty ? -__builtin_inff() : (m_run[t] + __builtin_log2f(l_run[t])) * kLn2;
+    {
+      uint32_t* z = reinterpret_cast<uint32_t*>(&tb[3].v[0][0]);
+      constexpr int kWords = kKT * kVRow / 2;
+      for (int i = (w >> 1) * 64 + lane; i < kWords; i += 256) z[i] = 0u;  // the stream's four wavefronts
+    }
+    __syncthreads();
+    f32x16 s0, s1;
+    bf16x8 pb[2];
+    pb[0] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    pb[1] = pb[0];
+    if (nsteps > 0) {
+      bf16x8 ka[8];
+      read_k(0, ka);
+      mma_s(ka, s0);
+    }
+    // whole rounds of the four buffers, then the last steps (no exit inside a round); buffer
+    // of step k is k % 4 for both k^ and V
+    int t = 0;
+    for (; t + kBufs <= nsteps; t += kBufs) {
+      step(hpc, t, 1, 3, 3, 2, phys_next, s0, s1, pb);
+      step(hpc, t + 1, 2, 0, 0, 3, phys_next, s1, s0, pb);
+      step(hpc, t + 2, 3, 1, 1, 0, phys_next, s0, s1, pb);
+      step(hpc, t + 3, 0, 2, 2, 1, phys_next, s1, s0, pb);
+    }
+    if (t < nsteps) step(hpc, t, 1, 3, 3, 2, phys_next, s0, s1, pb);
+    if (t + 1 < nsteps) step(hpc, t + 1, 2, 0, 0, 3, phys_next, s1, s0, pb);
+    if (t + 2 < nsteps) step(hpc, t + 2, 3, 1, 1, 0, phys_next, s0, s1, pb);
+    // P.V of the last step (its V landed before the last barrier)
+    if (nsteps > 0) {
+      bf16x8 va[8];
+      read_v((nsteps - 1) & 3, va);
+      mma_pv(va, pb);
+    }
+  };
+  if (hp == 0) walk(std::integral_constant<int, 0>{});
+  else walk(std::integral_constant<int, 1>{});
+
+  // ---- merge the two streams of each query row (stream 0, then stream 1) and write out
+  const bool out_poison = __syncthreads_or(poison) != 0;  // also: every wavefront is done with the tiles
+  const int pair = w >> 1;  // wavefronts 2 pair and 2 pair + 1 hold the same rows, streams 0 and 1
+  if (st == 1) {
+    sm.u.merge[pair][0][lane] = m_run;
+    sm.u.merge[pair][1][lane] = l_part;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.u.merge[pair][2 + 16 * db + i][lane] = acc[db][i];
+  }
+  __syncthreads();
+  if (st == 1) return;
+  {
+#pragma clang fp contract(off)
+    const float m1 = sm.u.merge[pair][0][lane];
+    const float l1 = sm.u.merge[pair][1][lane];
+    const float mx = fmaxf(m_run, m1);
+    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx);
+    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
+    const float l = pair32_sum(l_part * a0 + l1 * a1);
+    const int gi = hg * 4 + 2 * hp + (n >> 4);  // head within the GQA group
+    const bool live = gi < G && qi < Sq;
+    const bool empty = l == 0.0f;
+    const float inv = empty ? 0.0f : 1.0f / l;
+    const size_t row = ((size_t)b * P.num_q_heads + hk * G + (gi < G ? gi : 0)) * Sq + (qi < Sq ? qi : 0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          const float v = acc[db][i] * a0 + sm.u.merge[pair][2 + 16 * db + i][lane] * a1;
+          o[e] = out_poison ? __builtin_nanf("") : v * inv;
+        }
+        if (live) {
+          const i16x4 pk = pack_bf16(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<i16x4*>(P.out + row * kHeadDim + 32 * db + 8 * q4 + 4 * hh) = pk;
+        }
+      }
+    }
+    if (live && hh == 0) {
+      float lse = empty ? -__builtin_inff() : (mx + __builtin_log2f(l)) * kLn2;
       if (out_poison) lse = __builtin_nanf("");
       P.lse[row] = lse;
     }
@@ -583,18 +740,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     if (p.num_kv_heads % 2 == 0) launch_key_prologue<2>(p, kh, stream);
     else launch_key_prologue<1>(p, kh, stream);
   }
-  const unsigned nqb = (unsigned)((p.q_len + kQBlock - 1) / kQBlock);
+  const unsigned nqb = (unsigned)((p.q_len + kQB - 1) / kQB);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
   const unsigned grid = nqb * (unsigned)p.batch * (unsigned)p.num_kv_heads * nhg;
-  if (grid > 0) {
-    // Two wavefronts per query head when the items fit one dispatch round (the longest-first
-    // pairing on compute units is in use and the longest items decide the time); one otherwise.
-    const unsigned U = nqb * (unsigned)p.batch;
-    if (grid > (unsigned)p.num_cus && grid <= 2u * (unsigned)p.num_cus && U <= (unsigned)kMaxRankUnits)
-      hipLaunchKernelGGL(attend_kernel<2>, dim3(grid), dim3(Shape<2>::kThreads), 0, stream, p, kh);
-    else
-      hipLaunchKernelGGL(attend_kernel<1>, dim3(grid), dim3(Shape<1>::kThreads), 0, stream, p, kh);
-  }
+  if (grid > 0) hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh);
   return hipGetLastError();
 }
 

@@ -82,17 +82,16 @@ def test_prefill_row_alone_equals_row_in_batch(gpu):
     assert np.array_equal(l_p[0].view(np.uint32), l_full[r].view(np.uint32))
 
 
-def test_two_wavefronts_per_head_shape(gpu):
-    """A batch whose work items fit one dispatch round (320 items) runs the two-wavefronts-per-
-    head shape: ragged query blocks (Sq = 300), a partial group of query heads (Hq = 24, Hkv = 4,
-    groups of 4 + 2), parity with the oracle and a row alone (one wavefront per head) bitwise
-    equal to the same row in the batch."""
+def test_prefill_partial_head_group_ragged_blocks(gpu):
+    """Ragged query blocks (Sq = 300), a partial group of query heads (Hq = 24, Hkv = 4, groups of
+    4 + 2), rows of different lengths: parity with the oracle, and a row alone bitwise equal to
+    the same row in the batch."""
     full = workloads.make_batch(35, [300, 420, 555, 700], q_len=300, num_q_heads=24, num_kv_heads=4,
                                 num_pages=256, query_mode="prefill")
     plan = make_plan(full)
     o_full, l_full = run("prefill", plan, DeviceBatch(full))
     ref_out, ref_lse = oracle_ref(full)
-    assert_parity(o_full, l_full, ref_out, ref_lse, "prefill, two wavefronts per head", kind="prefill")
+    assert_parity(o_full, l_full, ref_out, ref_lse, "prefill, partial head group", kind="prefill")
     r = 1
     lo, hi = int(full.kv_indptr[r]), int(full.kv_indptr[r + 1])
     alone = workloads.PagedBatch(**{**full.__dict__,
