@@ -46,7 +46,7 @@ ROTATIONS = 4
 PREFILL_ROTATIONS = 8
 # untimed calls before each secondary workload (long-context decode, prefill, backward)
 SETTLE_MS = 60.0
-PREFILL_KERNELS = "key_prologue_kernel + attend_kernel"
+PREFILL_KERNELS = "prologue_kernel + attend_kernel"
 
 
 def decode_bytes(b) -> int:

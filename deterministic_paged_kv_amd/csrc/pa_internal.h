@@ -324,12 +324,26 @@ struct PrefillParams {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Prefill workspace: k^ [Hkv][nnz * 16][128] bf16, then 32 rows of padding (the attention
-// kernel loads whole 32-key tiles; the rows past a row's keys are masked, and the padding
-// keeps the last row's tile in bounds).
-inline size_t prefill_workspace_bytes(int hq, int hkv, int batch, int q_len, int num_indices) {
-  (void)hq; (void)batch; (void)q_len;
+// Prefill workspace, three regions written by the prologue kernel and read by the attention
+// kernel of the same call:
+//   k^     [Hkv][nnz * 16][128] bf16, then 32 rows of padding (the attention kernel loads whole
+//          32-key tiles; rows past a row's keys are masked, and the padding keeps the last
+//          row's tile in bounds);
+//   q^     [B][Hq][Sq][128] bf16;
+//   order  one int32 per work unit (row, block of kPrefillQB queries): the units, longest
+//          first.
+constexpr int kPrefillQB = 32;  // queries per work unit of the attention kernel
+inline size_t prefill_kh_bytes(int hkv, int num_indices) {
   return align256(((size_t)hkv * num_indices * kPageSize + 32) * kHeadDim * 2);
+}
+inline size_t prefill_qh_bytes(int hq, int batch, int q_len) {
+  return align256((size_t)batch * hq * q_len * kHeadDim * 2);
+}
+inline size_t prefill_order_bytes(int batch, int q_len) {
+  return align256((size_t)batch * ((q_len + kPrefillQB - 1) / kPrefillQB) * 4);
+}
+inline size_t prefill_workspace_bytes(int hq, int hkv, int batch, int q_len, int num_indices) {
+  return prefill_kh_bytes(hkv, num_indices) + prefill_qh_bytes(hq, batch, q_len) + prefill_order_bytes(batch, q_len);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

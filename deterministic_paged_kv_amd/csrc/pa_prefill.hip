@@ -7,13 +7,14 @@
 // K/V order before arithmetic, Split-KV disabled, FP32 LSE, same post-RoPE boundary).
 //
 // Two kernels per call.
-//  1. key_prologue_kernel: every cached key of every KV head of every valid row goes once
-//     through the shared Q/K prologue (RMSNorm, RoPE, BF16); k^ is written in logical order
-//     to the workspace, [Hkv][nnz * 16][128], key j of row b at (kv_indptr[b] * 16 + j);
-//     slots past a row's length are written as zeros.
+//  1. prologue_kernel: every cached key of every KV head of every valid row, and every query
+//     vector, goes once through the shared Q/K prologue (RMSNorm, RoPE, BF16); k^ is written
+//     to the workspace in logical order, key j of row b at index slot kv_indptr[b] + j / 16
+//     (slots past a row's length are zeros), q^ as [B][Hq][Sq][128]; one workgroup writes the
+//     order of the attention kernel's work units, longest first.
 //  2. attend_kernel: one workgroup per (block of 32 queries, row, KV head, group of up to 4
 //     query heads); each wavefront holds 16 queries of two query heads of the KV head's GQA
-//     group and runs the prologue of its own queries.  Key tiles of 32 (2 pages) are split
+//     group.  Key tiles of 32 (2 pages) are split
 //     into two fixed streams (even and odd tiles) walked in ascending order up to the block's
 //     last visible key and merged at the end in stream order; the workgroup stages each tile's
 //     k^ and V in LDS once for all its heads, with loads two to three steps ahead, and each
@@ -75,100 +76,7 @@ __device__ __forceinline__ bool indptr_prefix_monotone(const int32_t* indptr, in
 }
 
 // ---------------------------------------------------------------------------------------
-// 1. k^ for every cached key
-// ---------------------------------------------------------------------------------------
-// Row b = blockIdx.y; its tasks are spread over the x blocks, 4 wavefronts each.  A task is
-// one page of the row and HG consecutive KV heads: the wavefront reads the page's RoPE rows once
-// and issues the K loads of all HG heads before the first prologue, so the 16 positions' cos/sin
-// (512 B each) are fetched once per HG heads.  Only the keys of valid rows are written; nothing
-// reads the other slots.
-//
-// Workspace layout: per KV head, one 4 KB block per index slot (kv_indptr[b] + page), holding
-// the page's 16 keys transposed, [128 dims][16 keys]; the attention kernel copies a tile's two
-// blocks to LDS as they are and reads its k^ operands with transposed LDS reads.  The wavefront
-// transposes each block through 4.5 KB of LDS of its own.
-constexpr int kTRow = kHeadDim + 16;  // row of the transposing buffer, padded by 32 bytes
-template <int HG>
-__global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh) {
-  __shared__ __attribute__((aligned(16))) uint16_t tr_buf[4][kPageSize][kTRow];
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int b = blockIdx.y;
-  const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
-  const int n = p1 - p0;
-  const int lpl = P.last_page_len[b];
-  const bool mono = indptr_prefix_monotone(P.indptr, b, threadIdx.x, blockDim.x);
-  const bool row_ok = mono && p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && lpl >= 1 &&
-                      lpl <= kPageSize;
-  if (!row_ok) return;  // the attention kernel treats such a row as empty or poisoned
-  const int L = (n - 1) * kPageSize + lpl;
-  const int Hkv = P.num_kv_heads;
-  const int groups = Hkv / HG;
-  const bool knorm = P.k_norm != nullptr;
-  float kw[32];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kw[kb * 8 + e] = knorm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
-  const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  const int tasks = n * groups;
-  const int stride = gridDim.x * (blockDim.x >> 6);
-  for (int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < tasks; t += stride) {
-    const int pr = t / groups;
-    const int hk0 = (t % groups) * HG;
-    const int j = pr * kPageSize + r;  // logical key index = key position
-    const bool live = j < L;
-    float4 cs[8];
-    load_cos_sin(P.rope, live ? j : 0, g, cs);  // depends on the position only: goes out first
-    int phys = P.indices[p0 + pr];
-    // the key's key_position_ids entry must be its logical index (the rotation uses j); a
-    // wrong one, like an out-of-range page, makes the key NaN for every query that sees it
-    const int kp = live ? P.kpos[(size_t)(p0 + pr) * kPageSize + r] : j;
-    const bool key_ok = phys >= 0 && phys < P.num_pages && kp == j;
-    if (phys < 0 || phys >= P.num_pages) phys = 0;
-    // the HG heads of slot r are contiguous: HG * 256 bytes
-    const size_t src = (((size_t)phys * kPageSize + r) * Hkv + hk0) * kHeadDim + 8 * g;
-    uint4 raw[HG][4];
-#pragma unroll
-    for (int h = 0; h < HG; ++h)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) raw[h][kb] = live ? ldg16(P.k_cache + src + h * kHeadDim + 32 * kb) : zero4;
-    uint16_t(&tb)[kPageSize][kTRow] = tr_buf[threadIdx.x >> 6];
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      bf16x8 op[4];
-      prologue_operand(raw[h], kw, knorm, P.eps, cs, op);
-      // key r's 128 values into row r of the transposing buffer, then out as [dim][key]: a
-      // transposed read gives lane (G, i) = (lane / 16, lane % 16) keys 4 G .. 4 G + 3 of dim
-      // 16 c + i, 8 contiguous bytes of the block's row for that dim
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        *reinterpret_cast<uint4*>(&tb[r][32 * kb + 8 * g]) = !key_ok ? nan4 : (live ? as_u4(op[kb]) : zero4);
-      wave_lds_sync();
-      uint16_t* blk = kh + ((size_t)(hk0 + h) * P.num_indices + (size_t)(p0 + pr)) * kPageSize * kHeadDim;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(&tb[4 * g + ((lane & 15) >> 2)][16 * c + 4 * (lane & 3)]));
-        *reinterpret_cast<i16x4*>(blk + (16 * c + (lane & 15)) * kPageSize + 4 * g) = v;
-      }
-      wave_lds_sync();
-    }
-  }
-}
-
-template <int HG>
-void launch_key_prologue(const PrefillParams& p, uint16_t* kh, hipStream_t stream) {
-  // per row: up to max_pages_per_row * Hkv / HG tasks, 4 per block, at most 512 blocks per row
-  const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * (p.num_kv_heads / HG);
-  const unsigned bx = (unsigned)std::min<long long>((row_tasks + 3) / 4, 512);
-  hipLaunchKernelGGL(key_prologue_kernel<HG>, dim3(bx, (unsigned)p.batch), dim3(256), 0, stream, p, kh);
-}
-
-// ---------------------------------------------------------------------------------------
-// 2. causal attention: q^ made here, k^ from the workspace, V from the pages
+// Work items and tiles of the attention kernel
 // ---------------------------------------------------------------------------------------
 // Work item: (row b, KV head hk, group hg of up to 4 query heads of hk's GQA group, block of
 // 32 queries).  Eight wavefronts, two per SIMD.  Wavefront w holds 32 query rows: the 16
@@ -195,7 +103,7 @@ void launch_key_prologue(const PrefillParams& p, uint16_t* kh, hipStream_t strea
 // its vector units run the softmax of tile t; the three do not depend on one another, so the
 // matrix cores and the vector units overlap.  hp only picks which loads the wavefront issues
 // (hp = 0: k^ tiles, three steps ahead; hp = 1: V pages, two steps ahead).
-constexpr int kQB = 32;              // queries per work item
+constexpr int kQB = kPrefillQB;      // queries per work item
 constexpr int kKT = 32;              // keys per tile (2 pages)
 constexpr int kStreams = 2;          // key streams per item
 constexpr int kBufs = 4;             // LDS tile buffers per stream
@@ -222,8 +130,7 @@ struct alignas(16) TileBuf {
 
 struct alignas(16) AttendSmem {
   union {
-    TileBuf tiles[kStreams][kBufs];            // the walk (144 KB + 8 KB)
-    uint16_t qx[8][32][kHeadDim];              // q^ from the prologue layout to the operand layout
+    TileBuf tiles[kStreams][kBufs];            // the walk (144 KB)
     float merge[4][2 + 64][64];                // stream 1's states, read by stream 0 at the end
   } u;
 };
@@ -287,29 +194,174 @@ __device__ int unit_tiles(const PrefillParams& P, int nqb, int u) {
   return kend > 0 ? (kend + kKT - 1) / kKT : 0;
 }
 
-// The unit of rank `target` in the order: more tiles first, then lower unit number.
-// All threads of the workgroup call it; U <= kMaxRankUnits.
-__device__ int unit_of_rank(const PrefillParams& P, int nqb, int U, int target, int tid, int nthreads,
-                            RankSmem& rs) {
-  for (int u = tid; u < U; u += nthreads) rs.tiles[u] = unit_tiles(P, nqb, u);
+// The order of the units: more tiles first, then lower unit number (U <= kMaxRankUnits).
+// All threads of the workgroup call it.
+__device__ void unit_order(const PrefillParams& P, int nqb, int U, int32_t* __restrict__ order, RankSmem& rs) {
+  for (int u = threadIdx.x; u < U; u += blockDim.x) rs.tiles[u] = unit_tiles(P, nqb, u);
   __syncthreads();
-  for (int u = tid; u < U; u += nthreads) {
+  for (int u = threadIdx.x; u < U; u += blockDim.x) {
     const int c = rs.tiles[u];
     int rank = 0;
     for (int v = 0; v < U; ++v) {
       const int cv = rs.tiles[v];
       rank += (cv > c || (cv == c && v < u)) ? 1 : 0;
     }
-    if (rank == target) rs.sel = u;
+    order[rank] = u;
   }
-  __syncthreads();
-  return rs.sel;
 }
 
+// ---------------------------------------------------------------------------------------
+// 1. the prologue: k^ of every cached key, q^ of every query, the order of the work units
+// ---------------------------------------------------------------------------------------
+// One launch of 256-thread workgroups of three kinds:
+//   [0, B * kx)        k^: row b = id / kx; its tasks are spread over its kx workgroups, 4
+//                      wavefronts each.  A task is one page of the row and HG consecutive KV
+//                      heads: the wavefront reads the page's RoPE rows once and issues the K
+//                      loads of all HG heads before the first prologue, so the 16 positions'
+//                      cos/sin (512 B each) are fetched once per HG heads.  Only the keys of
+//                      valid rows are written; nothing reads the other slots.
+//   [B * kx, + nq)     q^: 16 query vectors per wavefront, (b, head, i) in [B][Hq][Sq] order,
+//                      written in that order, [B][Hq][Sq][128] bf16.
+//   the last one       the order of the work units, longest first.
+//
+// k^ layout: per KV head, one 4 KB block per index slot (kv_indptr[b] + page), holding the
+// page's 16 keys transposed, [128 dims][16 keys]; the attention kernel copies a tile's two
+// blocks to LDS as they are and reads its k^ operands with transposed LDS reads.  The wavefront
+// transposes each block through 4.5 KB of LDS of its own.
+constexpr int kTRow = kHeadDim + 16;  // row of the transposing buffer, padded by 32 bytes
+constexpr int kPrologueThreads = 256;
+union PrologueSmem {
+  uint16_t tr_buf[4][kPageSize][kTRow];
+  RankSmem rank;
+};
+
+template <int HG>
+__device__ void key_part(const PrefillParams& P, uint16_t* __restrict__ kh, int b, int xb, int kx,
+                         uint16_t (&tr_buf)[4][kPageSize][kTRow]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
+  const int n = p1 - p0;
+  const int lpl = P.last_page_len[b];
+  const bool mono = indptr_prefix_monotone(P.indptr, b, threadIdx.x, blockDim.x);
+  const bool row_ok = mono && p0 >= 0 && n > 0 && p1 <= P.num_indices && n <= P.max_pages_per_row && lpl >= 1 &&
+                      lpl <= kPageSize;
+  if (!row_ok) return;  // the attention kernel treats such a row as empty or poisoned
+  const int L = (n - 1) * kPageSize + lpl;
+  const int Hkv = P.num_kv_heads;
+  const int groups = Hkv / HG;
+  const bool knorm = P.k_norm != nullptr;
+  float kw[32];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kw[kb * 8 + e] = knorm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
+  const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  const int tasks = n * groups;
+  const int stride = kx * (blockDim.x >> 6);
+  for (int t = xb * (blockDim.x >> 6) + (threadIdx.x >> 6); t < tasks; t += stride) {
+    const int pr = t / groups;
+    const int hk0 = (t % groups) * HG;
+    const int j = pr * kPageSize + r;  // logical key index = key position
+    const bool live = j < L;
+    float4 cs[8];
+    load_cos_sin(P.rope, live ? j : 0, g, cs);  // depends on the position only: goes out first
+    int phys = P.indices[p0 + pr];
+    // the key's key_position_ids entry must be its logical index (the rotation uses j); a
+    // wrong one, like an out-of-range page, makes the key NaN for every query that sees it
+    const int kp = live ? P.kpos[(size_t)(p0 + pr) * kPageSize + r] : j;
+    const bool key_ok = phys >= 0 && phys < P.num_pages && kp == j;
+    if (phys < 0 || phys >= P.num_pages) phys = 0;
+    // the HG heads of slot r are contiguous: HG * 256 bytes
+    const size_t src = (((size_t)phys * kPageSize + r) * Hkv + hk0) * kHeadDim + 8 * g;
+    uint4 raw[HG][4];
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) raw[h][kb] = live ? ldg16(P.k_cache + src + h * kHeadDim + 32 * kb) : zero4;
+    uint16_t(&tb)[kPageSize][kTRow] = tr_buf[threadIdx.x >> 6];
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      bf16x8 op[4];
+      prologue_operand(raw[h], kw, knorm, P.eps, cs, op);
+      // key r's 128 values into row r of the transposing buffer, then out as [dim][key]: a
+      // transposed read gives lane (G, i) = (lane / 16, lane % 16) keys 4 G .. 4 G + 3 of dim
+      // 16 c + i, 8 contiguous bytes of the block's row for that dim
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        *reinterpret_cast<uint4*>(&tb[r][32 * kb + 8 * g]) = !key_ok ? nan4 : (live ? as_u4(op[kb]) : zero4);
+      wave_lds_sync();
+      uint16_t* blk = kh + ((size_t)(hk0 + h) * P.num_indices + (size_t)(p0 + pr)) * kPageSize * kHeadDim;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(&tb[4 * g + ((lane & 15) >> 2)][16 * c + 4 * (lane & 3)]));
+        *reinterpret_cast<i16x4*>(blk + (16 * c + (lane & 15)) * kPageSize + 4 * g) = v;
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+__device__ void query_part(const PrefillParams& P, uint16_t* __restrict__ qh, int qblk) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  // lanes r, r + 16, r + 32, r + 48 share vector v (dims 32 kb + 8 g .. +7 of block kb)
+  const long long nv = (long long)P.batch * P.num_q_heads * P.q_len;
+  const long long v = ((long long)qblk * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 16 + r;
+  const bool live = v < nv;
+  const long long vv = live ? v : 0;
+  const int i = (int)(vv % P.q_len);
+  const int b = (int)(vv / ((long long)P.num_q_heads * P.q_len));
+  int qp = P.qpos[(size_t)b * P.q_len + i];
+  if (qp < 0 || qp >= P.table_rows) qp = 0;  // the attention kernel poisons such a query's rows
+  float4 cs[8];
+  load_cos_sin(P.rope, qp, g, cs);
+  uint4 raw[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) raw[kb] = ldg16(P.q + (size_t)vv * kHeadDim + 32 * kb + 8 * g);
+  const bool qnorm = P.q_norm != nullptr;
+  float wq[32];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wq[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
+  bf16x8 op[4];
+  prologue_operand(raw, wq, qnorm, P.eps, cs, op);
+  if (live) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) stg16(qh + (size_t)v * kHeadDim + 32 * kb + 8 * g, as_u4(op[kb]));
+  }
+}
+
+template <int HG>
+__global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh,
+                                                                    uint16_t* __restrict__ qh,
+                                                                    int32_t* __restrict__ order, int kx, int nq) {
+  __shared__ PrologueSmem sm;
+  const int blk = (int)blockIdx.x;
+  const int nk = P.batch * kx;
+  if (blk < nk) {
+    key_part<HG>(P, kh, blk / kx, blk % kx, kx, sm.tr_buf);
+  } else if (blk < nk + nq) {
+    query_part(P, qh, blk - nk);
+  } else {
+    const int nqb = (P.q_len + kQB - 1) / kQB;
+    const int U = P.batch * nqb;
+    if (U <= kMaxRankUnits) unit_order(P, nqb, U, order, sm.rank);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 2. causal attention: q^ and k^ from the workspace, V from the pages
+// ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_kernel(
-    const PrefillParams P, const uint16_t* __restrict__ kh) {
+    const PrefillParams P, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ qh,
+    const int32_t* __restrict__ order) {
   __shared__ AttendSmem sm;
-  __shared__ RankSmem sched;
   const int G = P.group;
   const int Hkv = P.num_kv_heads;
   const int Sq = P.q_len;
@@ -325,7 +377,7 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   const int U = P.batch * nqb;
   const int rank = (int)blockIdx.x / HH;
   const int head = (int)blockIdx.x % HH;
-  const int unit = U <= kMaxRankUnits ? unit_of_rank(P, nqb, U, rank, tid, kAttendThreads, sched) : rank;
+  const int unit = U <= kMaxRankUnits ? load_uniform(order, rank) : rank;
   const int qb = nqb - 1 - unit / P.batch;
   const int b = unit % P.batch;
   const int hg = head % nhg;
@@ -377,45 +429,19 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   const int qp = __shfl(qp_all, 16 * qg + (n & 15));
   const int lim = min(L, qp + 1);
 
-  // ---- q^ of the wavefront's 32 query rows, in the B-operand layout of the S MFMAs
-  // The shared prologue runs in its own layout (lane r + 16 g: query r, dims 32 kb + 8 g ..),
-  // once per head slot; the results go through LDS to lane (n, hh): row n, dims 16 s + 8 hh ..
-  // +7 for s = 0..7.
+  // ---- q^ of the wavefront's 32 query rows, in the B-operand layout of the S MFMAs: lane
+  // (n, hh) holds row n (head slot 2 hp + n / 16, query 16 qg + n % 16), dims 16 s + 8 hh .. +7
+  // for s = 0..7.  Rows past the chunk or the group are zeros (their results are not stored).
   bf16x8 qop[8];
   {
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const bool qnorm = P.q_norm != nullptr;
-    float wq[32];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wq[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
-    const int qi_r = qb * kQB + 16 * qg + r;
-    const int qp_r = __shfl(qp_all, 16 * qg + r);
-    float4 cs[8];
-    load_cos_sin(P.rope, max(qp_r, 0), g, cs);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int gi = hg * 4 + 2 * hp + k;
-      const bool live = gi < G && qi_r < Sq;
-      uint4 raw[4];
-      const size_t off = (((size_t)b * P.num_q_heads + hk * G + (gi < G ? gi : 0)) * Sq + (qi_r < Sq ? qi_r : 0)) *
-                             kHeadDim + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) raw[kb] = live ? ldg16(P.q + off + 32 * kb) : make_uint4(0, 0, 0, 0);
-      bf16x8 op[4];
-      prologue_operand(raw, wq, qnorm, P.eps, cs, op);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        *reinterpret_cast<uint4*>(&sm.u.qx[w][16 * k + r][32 * kb + 8 * g]) = as_u4(op[kb]);
-    }
-    wave_lds_sync();
+    const int gi = hg * 4 + 2 * hp + (n >> 4);
+    const bool live = gi < G && qi < Sq;
+    const uint16_t* src =
+        qh + (((size_t)b * P.num_q_heads + hk * G + (live ? gi : 0)) * Sq + (live ? qi : 0)) * kHeadDim + 8 * hh;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.u.qx[w][n][16 * s + 8 * hh]));
+      qop[s] = __builtin_bit_cast(bf16x8, live ? ldg16(src + 16 * s) : make_uint4(0, 0, 0, 0));
   }
-  __syncthreads();  // the q^ exchange area becomes tile buffers
 
   // ---- the walk
   float m_run = -__builtin_inff(), m_neg = 0.0f, l_part = 0.0f;
@@ -440,13 +466,16 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int kDma = 5;                       // most load instructions of one role per step
   const int dma_n = role < 2 ? 4 : 5;           // instructions issued per step
   const int dma_u0 = role < 2 ? 4 * role : 5 * (role - 2);  // its first instruction
-  uint32_t doff[kDma];  // roles 0, 1: byte offset in the tile's k^; roles 2, 3: byte offset in the page
+  // roles 0, 1: doff = byte offset in the tile's k^; roles 2, 3: doff = byte offset of the
+  // slot's row in the page, dch = of the chunk in the row
+  uint32_t doff[kDma], dch[kDma];
 #pragma unroll
   for (int i = 0; i < kDma; ++i) {
     const int pc = 64 * (dma_u0 + i) + lane;
     const int row = pc / kVRowChunks;
     const int ch = min(pc - row * kVRowChunks, 15);
-    doff[i] = role < 2 ? 16u * pc : (uint32_t)(row & 15) * v_row_bytes + 16u * ch;
+    doff[i] = role < 2 ? 16u * pc : (uint32_t)(row & 15) * v_row_bytes;
+    dch[i] = 16u * ch;
   }
   // The walk is written once per phase (HP = hp: 0 loads k^ and computes S at the start of a
   // step, 1 loads V and computes S at its end), so neither path branches on its role.
@@ -472,36 +501,20 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
       const char* vb = (const char*)(P.v_cache + ((size_t)phys * kPageSize * Hkv + hk) * kHeadDim);
       const uint32_t dst = lds_address(&tb[buf].v[0][0]) + 1024u * dma_u0;
       // the last slot of the page holding a key of the row (15 unless the page reaches the
-      // row's end): the slots after it read that one
-      const int smax = 2 * kt + qg >= nidx - 1 ? lpl - 1 : 15;
-      if (smax == 15) {
+      // row's end): the slots after it read that one (no branch: the step stays one block)
+      const uint32_t smax_off = (uint32_t)(2 * kt + qg >= nidx - 1 ? lpl - 1 : 15) * v_row_bytes;
 #pragma unroll
-        for (int i = 0; i < 5; ++i) lds_dma16(dst + 1024u * i, vb, doff[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          const int pc = 64 * (dma_u0 + i) + lane;
-          const int row = pc / kVRowChunks;
-          const int ch = min(pc - row * kVRowChunks, 15);
-          lds_dma16(dst + 1024u * i, vb, (uint32_t)min(row & 15, smax) * v_row_bytes + 16u * ch);
-        }
-      }
+      for (int i = 0; i < 5; ++i) lds_dma16(dst + 1024u * i, vb, min(doff[i], smax_off) + dch[i]);
     }
   };
   // End of step t: step t + 1 computes the scores of tile t + 2 and adds P.V of tile t, so
   // k^ of step t + 2 (issued at step t - 1) and V of step t (issued at step t - 2) must have
   // landed.  The loads issued after them may stay in flight: k^ of step t + 3 (4 instructions),
   // V of steps t + 1 and t + 2 (5 each).  Loads complete in issue order.
-  auto wait_end = [&](auto hpc, int t) {
+  auto wait_end = [&](auto hpc) {
     constexpr int HP = decltype(hpc)::value;
-    if constexpr (HP == 0) {
-      if (t + 3 < nsteps) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-    } else {
-      if (t + 2 < nsteps) wait_vmcnt<10>();
-      else if (t + 1 < nsteps) wait_vmcnt<5>();
-      else wait_vmcnt<0>();
-    }
+    if constexpr (HP == 0) wait_vmcnt<4>();
+    else wait_vmcnt<10>();
   };
   // The k^ operand of dim step s, lane (n, hh): key n, dims 16 s + 8 hh .. +7, two transposed
   // reads of the block holding key n (lane group G = lane / 16 reads dims 16 s + 8 (G / 2) +
@@ -579,14 +592,6 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
                   int& phys_next, f32x16& s_cur, f32x16& s_nxt, bf16x8 (&pb_prev)[2]) {
     constexpr int HP = decltype(hpc)::value;
     const int kt = kStreams * t + st;
-    // k^ of step t + 3 (phase 0) or V of step t + 2 (phase 1), into the buffer freed at the
-    // previous barrier
-    const int ld = HP == 0 ? t + 3 : t + 2;
-    if (ld < nsteps) {
-      const int phys = phys_next;
-      phys_next = page_of(hpc, ld + 1);
-      issue(hpc, ld, HP == 0 ? b_kload : b_vload, phys);
-    }
     // causal mask on tiles that reach past the block's first query, and on tiles past the
     // item's last one (a stream with one tile fewer than the other runs that step masked)
     if (kt >= ntiles || (kt + 1) * kKT > free_end) {
@@ -598,6 +603,15 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     read_k(b_k, ka);
     read_v(b_v, va);
     mma_pv(va, pb_prev);
+    // k^ of step t + 3 (phase 0) or V of step t + 2 (phase 1), into the buffer freed at the
+    // previous barrier.  Issued on every step (past the stream's end the tile index is clamped
+    // and the loads land in buffers nothing reads), so the step has no branch around them.
+    {
+      const int ld = HP == 0 ? t + 3 : t + 2;
+      const int phys = phys_next;
+      phys_next = page_of(hpc, ld + 1);
+      issue(hpc, ld, HP == 0 ? b_kload : b_vload, phys);
+    }
     mma_s(ka, s_nxt);
     float lp;
     tile_p(s_cur, m_neg, lp, pb_prev);
@@ -620,7 +634,7 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
     l_part += lp;
-    wait_end(hpc, t);
+    wait_end(hpc);
     __syncthreads();
   };
 
@@ -669,13 +683,19 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     if (t < nsteps) step(hpc, t, 1, 3, 3, 2, phys_next, s0, s1, pb);
     if (t + 1 < nsteps) step(hpc, t + 1, 2, 0, 0, 3, phys_next, s1, s0, pb);
     if (t + 2 < nsteps) step(hpc, t + 2, 3, 1, 1, 0, phys_next, s0, s1, pb);
-    // P.V of the last step (its V landed before the last barrier)
+    // P.V of the last step (its V landed before the last barrier); the loads issued past the
+    // end drain before the tile buffers become the merge area
     if (nsteps > 0) {
       bf16x8 va[8];
       read_v((nsteps - 1) & 3, va);
       mma_pv(va, pb);
     }
+    wait_vmcnt<0>();
   };
+  // q^ has landed before the first tile load goes out.  The compiler does not count the
+  // direct-to-LDS loads (inline assembly), so without this wait it would place one for the q^
+  // loads inside the walk, where it would also drain every tile load in flight.
+  wait_vmcnt<0>();
   if (hp == 0) walk(std::integral_constant<int, 0>{});
   else walk(std::integral_constant<int, 1>{});
 
@@ -733,17 +753,28 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  uint16_t* kh = (uint16_t*)p.workspace;
-  if (p.num_indices > 0) {
-    // two KV heads per wavefront: half the cos/sin reads, still about two wavefronts per SIMD
-    // (four heads per wavefront leave too few wavefronts to hide the load latency)
-    if (p.num_kv_heads % 2 == 0) launch_key_prologue<2>(p, kh, stream);
-    else launch_key_prologue<1>(p, kh, stream);
-  }
+  char* ws = (char*)p.workspace;
+  uint16_t* kh = (uint16_t*)ws;
+  uint16_t* qh = (uint16_t*)(ws + prefill_kh_bytes(p.num_kv_heads, p.num_indices));
+  int32_t* order = (int32_t*)(ws + prefill_kh_bytes(p.num_kv_heads, p.num_indices) +
+                              prefill_qh_bytes(p.num_q_heads, p.batch, p.q_len));
+  // k^: per row up to max_pages_per_row * Hkv / HG tasks, 4 per workgroup, at most 512
+  // workgroups per row; two KV heads per wavefront (half the cos/sin reads) when Hkv is even.
+  // q^: 64 query vectors per workgroup.  Then one workgroup for the order of the units.
+  const int hg = p.num_kv_heads % 2 == 0 ? 2 : 1;
+  const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * (p.num_kv_heads / hg);
+  const int kx = (int)std::min<long long>((row_tasks + 3) / 4, 512);
+  const long long nv = (long long)p.batch * p.num_q_heads * p.q_len;
+  const int nq = (int)((nv + 63) / 64);
+  const unsigned pgrid = (unsigned)((long long)p.batch * kx + nq + 1);
+  if (hg == 2)
+    hipLaunchKernelGGL(prologue_kernel<2>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, kx, nq);
+  else
+    hipLaunchKernelGGL(prologue_kernel<1>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, kx, nq);
   const unsigned nqb = (unsigned)((p.q_len + kQB - 1) / kQB);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
   const unsigned grid = nqb * (unsigned)p.batch * (unsigned)p.num_kv_heads * nhg;
-  if (grid > 0) hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh);
+  if (grid > 0) hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh, qh, order);
   return hipGetLastError();
 }
 
