@@ -337,10 +337,70 @@ __device__ void query_part(const PrefillParams& P, uint16_t* __restrict__ qh, in
   }
 }
 
+// The record of work unit u (row b = u % B, query block qb = nqb - 1 - u / B): one half-
+// wavefront per unit, lane i for query qb * kQB + i.  Fields (int32):
+//   0 p0        kv_indptr[b]
+//   1 nidx      pages of the row
+//   2 lpl       kv_last_page_len[b]
+//   3 L         keys of the row (0 if the row is empty or bad)
+//   4 ntiles    32-key tiles up to the block's last visible key
+//   5 free_end  tiles ending at or before this key need no causal mask
+//   6 poison    1 if the row is bad (extent out of range, or past a decrease of kv_indptr) or a
+//               query of the block has a position out of the RoPE table or a cache_position
+//               that differs from it: every output of the unit is then NaN
+// A bad row's or query's position counts as -1 (sees nothing) in ntiles and free_end.
+enum { kUnitP0 = 0, kUnitNidx, kUnitLpl, kUnitL, kUnitTiles, kUnitFreeEnd, kUnitPoison };
+__device__ void unit_part(const PrefillParams& P, int32_t* __restrict__ units, int ublk) {
+  const int lane = threadIdx.x & 63;
+  const int i32 = lane & 31;
+  const int nqb = (P.q_len + kQB - 1) / kQB;
+  const int U = P.batch * nqb;
+  const int u = (ublk * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  const bool live_unit = u < U;
+  const int uu = live_unit ? u : 0;
+  const int b = uu % P.batch;
+  const int qb = nqb - 1 - uu / P.batch;
+  const int p0 = P.indptr[b], p1 = P.indptr[b + 1];
+  const int nidx = p1 - p0;
+  const int lpl = P.last_page_len[b];
+  // kv_indptr[0..b+1] non-decreasing (rows in such a prefix never share index slots)
+  int ok = 1;
+  for (int i = i32; i <= b; i += 32) ok &= P.indptr[i] <= P.indptr[i + 1] ? 1 : 0;
+  const uint64_t okm = __builtin_amdgcn_ballot_w64(ok != 0);
+  const uint32_t half = (uint32_t)(okm >> (lane & 32));
+  const bool mono = half == 0xFFFFFFFFu;
+  const bool bad = !mono || p0 < 0 || nidx < 0 || p1 > P.num_indices || nidx > P.max_pages_per_row ||
+                   (nidx > 0 && (lpl < 1 || lpl > kPageSize));
+  const int L = (nidx > 0 && !bad) ? (nidx - 1) * kPageSize + lpl : 0;
+  const int i = qb * kQB + i32;
+  int qp = i < P.q_len ? P.qpos[(size_t)b * P.q_len + i] : -1;
+  const int cp = i < P.q_len ? P.cache_position[(size_t)b * P.q_len + i] : -1;
+  const bool qbad = i < P.q_len && (qp < 0 || qp >= P.table_rows || cp != qp);
+  if (qbad) qp = -1;
+  int qmax = qp, qmin = qp < 0 ? INT32_MAX : qp;
+#pragma unroll
+  for (int sh = 1; sh < 32; sh <<= 1) {
+    qmax = max(qmax, __shfl_xor(qmax, sh));
+    qmin = min(qmin, __shfl_xor(qmin, sh));
+  }
+  const bool any_qbad = (uint32_t)(__builtin_amdgcn_ballot_w64(qbad) >> (lane & 32)) != 0u;
+  const int kend = min(L, qmax + 1);
+  const int rec[7] = {p0, nidx, lpl, L, kend > 0 ? (kend + kKT - 1) / kKT : 0,
+                      min(L, qmin == INT32_MAX ? 0 : qmin + 1), (bad || any_qbad) ? 1 : 0};
+  if (live_unit && i32 < 7) {
+    int v = rec[0];
+#pragma unroll
+    for (int f = 1; f < 7; ++f) v = i32 == f ? rec[f] : v;
+    units[(size_t)u * kUnitInts + i32] = v;
+  }
+}
+
 template <int HG>
 __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh,
                                                                     uint16_t* __restrict__ qh,
-                                                                    int32_t* __restrict__ order, int kx, int nq) {
+                                                                    int32_t* __restrict__ order,
+                                                                    int32_t* __restrict__ units, int kx, int nq,
+                                                                    int nu) {
   __shared__ PrologueSmem sm;
   const int blk = (int)blockIdx.x;
   const int nk = P.batch * kx;
@@ -348,6 +408,8 @@ __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const Prefil
     key_part<HG>(P, kh, blk / kx, blk % kx, kx, sm.tr_buf);
   } else if (blk < nk + nq) {
     query_part(P, qh, blk - nk);
+  } else if (blk < nk + nq + nu) {
+    unit_part(P, units, blk - nk - nq);
   } else {
     const int nqb = (P.q_len + kQB - 1) / kQB;
     const int U = P.batch * nqb;
@@ -360,7 +422,7 @@ __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const Prefil
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_kernel(
     const PrefillParams P, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ qh,
-    const int32_t* __restrict__ order) {
+    const int32_t* __restrict__ order, const int32_t* __restrict__ units) {
   __shared__ AttendSmem sm;
   const int G = P.group;
   const int Hkv = P.num_kv_heads;
@@ -391,47 +453,29 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   const int n = lane & 31;
   const int hh = lane >> 5;
 
-  const int p0 = P.indptr[b];
-  const int p1 = P.indptr[b + 1];
-  const int nidx = p1 - p0;
-  const int lpl = P.last_page_len[b];
-  const bool mono = indptr_prefix_monotone(P.indptr, b, tid, kAttendThreads);
-  const bool bad = !mono || p0 < 0 || nidx < 0 || p1 > P.num_indices || nidx > P.max_pages_per_row ||
-                   (nidx > 0 && (lpl < 1 || lpl > kPageSize));
-  const int L = (nidx > 0 && !bad) ? (nidx - 1) * kPageSize + lpl : 0;
-
-  // Positions of the block's 32 queries (-1: past the chunk, sees nothing).  Every wavefront
-  // takes the first and last positions over all 32 (the tile walk is the block's, the same in
-  // every wavefront), then keeps the one of its lane's query.
-  int poison = bad;
-  int qp_all;
-  {
-    const int i = qb * kQB + n;  // lanes n and n + 32 read the same query
-    qp_all = i < Sq ? P.qpos[(size_t)b * Sq + i] : -1;
-    const int cp = i < Sq ? P.cache_position[(size_t)b * Sq + i] : -1;
-    if (i < Sq && (qp_all < 0 || qp_all >= P.table_rows || cp != qp_all)) { poison = 1; qp_all = -1; }
-  }
-  int qmax = qp_all, qmin = qp_all < 0 ? INT32_MAX : qp_all;
-#pragma unroll
-  for (int sh = 1; sh < 32; sh <<= 1) {
-    qmax = max(qmax, __shfl_xor(qmax, sh));
-    qmin = min(qmin, __shfl_xor(qmin, sh));
-  }
-  qmax = __builtin_amdgcn_readfirstlane(qmax);
-  qmin = __builtin_amdgcn_readfirstlane(qmin);
-  const int kend = min(L, qmax + 1);
-  const int ntiles = kend > 0 ? (kend + kKT - 1) / kKT : 0;
+  // the unit's record (written by the prologue kernel) and this lane's query (column n: query
+  // 16 qg + n % 16) with the last key it may see + 1; a query whose position is out of range
+  // sees nothing (the unit is then poisoned anyway)
+  const int32_t* rec = units + (size_t)unit * kUnitInts;
+  const int p0 = load_uniform(rec, kUnitP0);
+  const int nidx = load_uniform(rec, kUnitNidx);
+  const int lpl = load_uniform(rec, kUnitLpl);
+  const int L = load_uniform(rec, kUnitL);
+  const int ntiles = load_uniform(rec, kUnitTiles);
+  const int free_end = load_uniform(rec, kUnitFreeEnd);
+  int poison = load_uniform(rec, kUnitPoison);
   const int nsteps = (ntiles + kStreams - 1) / kStreams;
-  // tiles ending at or before this key need no mask: every key is < L and <= every query
-  const int free_end = min(L, qmin == INT32_MAX ? 0 : qmin + 1);
-  // this lane's query (column n: query 16 qg + n % 16) and the last key it may see + 1
   const int qi = qb * kQB + 16 * qg + (n & 15);
-  const int qp = __shfl(qp_all, 16 * qg + (n & 15));
+  int qp = qi < Sq ? P.qpos[(size_t)b * Sq + qi] : -1;
+  if (qp < 0 || qp >= P.table_rows) qp = -1;
   const int lim = min(L, qp + 1);
 
   // ---- q^ of the wavefront's 32 query rows, in the B-operand layout of the S MFMAs: lane
   // (n, hh) holds row n (head slot 2 hp + n / 16, query 16 qg + n % 16), dims 16 s + 8 hh .. +7
-  // for s = 0..7.  Rows past the chunk or the group are zeros (their results are not stored).
+  // for s = 0..7.  A row past the chunk or the group takes the q^ of query 0 of the group's
+  // first head: its column computes on valid data and is never stored (columns are
+  // independent).  The loads are unconditional and nothing selects on them, so they stay in
+  // flight until the single wait before the walk.
   bf16x8 qop[8];
   {
     const int gi = hg * 4 + 2 * hp + (n >> 4);
@@ -439,8 +483,7 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     const uint16_t* src =
         qh + (((size_t)b * P.num_q_heads + hk * G + (live ? gi : 0)) * Sq + (live ? qi : 0)) * kHeadDim + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qop[s] = __builtin_bit_cast(bf16x8, live ? ldg16(src + 16 * s) : make_uint4(0, 0, 0, 0));
+    for (int s = 0; s < 8; ++s) qop[s] = __builtin_bit_cast(bf16x8, ldg16(src + 16 * s));
   }
 
   // ---- the walk
@@ -640,22 +683,25 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
 
   auto walk = [&](auto hpc) {
     constexpr int HP = decltype(hpc)::value;
-    // k^ of steps 0-2 (phase 0) or V of steps 0-1 (phase 1) in flight; k^ of steps 0 and 1 has
-    // landed before the walk starts.  V buffer 3 stands in for the tile of step -1: zeros, so
-    // the first step's P.V adds nothing.
+    // k^ of steps 0-2 (phase 0) or V of steps 0-1 (phase 1) go out right behind the q^ loads,
+    // and one wait covers both (a single memory latency before the walk).  The wait also tells
+    // the compiler, which does not count the direct-to-LDS loads (inline assembly), that q^ has
+    // landed on every path: otherwise it places a wait for q^ inside the walk, where it would
+    // drain every tile load in flight.  V buffer 3 stands in for the tile of step -1: zeros,
+    // so the first step's P.V adds nothing.
     int phys_next = 0;
     if (nsteps > 0) {
       if constexpr (HP == 0) {
         issue(hpc, 0, 0, 0);
         issue(hpc, 1, 1, 0);
         issue(hpc, 2, 2, 0);
-        wait_vmcnt<4>();
       } else {
         issue(hpc, 0, 0, page_of(hpc, 0));
         issue(hpc, 1, 1, page_of(hpc, 1));
         phys_next = page_of(hpc, 2);
       }
     }
+    wait_vmcnt<0>();
     {
       uint32_t* z = reinterpret_cast<uint32_t*>(&tb[3].v[0][0]);
       constexpr int kWords = kKT * kVRow / 2;
@@ -692,10 +738,6 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     }
     wait_vmcnt<0>();
   };
-  // q^ has landed before the first tile load goes out.  The compiler does not count the
-  // direct-to-LDS loads (inline assembly), so without this wait it would place one for the q^
-  // loads inside the walk, where it would also drain every tile load in flight.
-  wait_vmcnt<0>();
   if (hp == 0) walk(std::integral_constant<int, 0>{});
   else walk(std::integral_constant<int, 1>{});
 
@@ -754,27 +796,36 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   char* ws = (char*)p.workspace;
+  const size_t kh_bytes = prefill_kh_bytes(p.num_kv_heads, p.num_indices);
+  const size_t qh_bytes = prefill_qh_bytes(p.num_q_heads, p.batch, p.q_len);
+  const size_t order_bytes = prefill_order_bytes(p.batch, p.q_len);
   uint16_t* kh = (uint16_t*)ws;
-  uint16_t* qh = (uint16_t*)(ws + prefill_kh_bytes(p.num_kv_heads, p.num_indices));
-  int32_t* order = (int32_t*)(ws + prefill_kh_bytes(p.num_kv_heads, p.num_indices) +
-                              prefill_qh_bytes(p.num_q_heads, p.batch, p.q_len));
+  uint16_t* qh = (uint16_t*)(ws + kh_bytes);
+  int32_t* order = (int32_t*)(ws + kh_bytes + qh_bytes);
+  int32_t* units = (int32_t*)(ws + kh_bytes + qh_bytes + order_bytes);
   // k^: per row up to max_pages_per_row * Hkv / HG tasks, 4 per workgroup, at most 512
   // workgroups per row; two KV heads per wavefront (half the cos/sin reads) when Hkv is even.
-  // q^: 64 query vectors per workgroup.  Then one workgroup for the order of the units.
+  // q^: 64 query vectors per workgroup.  Unit records: 8 units per workgroup.  Then one
+  // workgroup for the order of the units.
   const int hg = p.num_kv_heads % 2 == 0 ? 2 : 1;
   const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * (p.num_kv_heads / hg);
   const int kx = (int)std::min<long long>((row_tasks + 3) / 4, 512);
   const long long nv = (long long)p.batch * p.num_q_heads * p.q_len;
   const int nq = (int)((nv + 63) / 64);
-  const unsigned pgrid = (unsigned)((long long)p.batch * kx + nq + 1);
+  const int nqb = (p.q_len + kQB - 1) / kQB;
+  const int U = p.batch * nqb;
+  const int nu = (U + 7) / 8;
+  const unsigned pgrid = (unsigned)((long long)p.batch * kx + nq + nu + 1);
   if (hg == 2)
-    hipLaunchKernelGGL(prologue_kernel<2>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, kx, nq);
+    hipLaunchKernelGGL(prologue_kernel<2>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, units, kx,
+                       nq, nu);
   else
-    hipLaunchKernelGGL(prologue_kernel<1>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, kx, nq);
-  const unsigned nqb = (unsigned)((p.q_len + kQB - 1) / kQB);
+    hipLaunchKernelGGL(prologue_kernel<1>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, units, kx,
+                       nq, nu);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
-  const unsigned grid = nqb * (unsigned)p.batch * (unsigned)p.num_kv_heads * nhg;
-  if (grid > 0) hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh, qh, order);
+  const unsigned grid = (unsigned)U * (unsigned)p.num_kv_heads * nhg;
+  if (grid > 0)
+    hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh, qh, order, units);
   return hipGetLastError();
 }
 
