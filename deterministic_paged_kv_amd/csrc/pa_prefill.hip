@@ -116,21 +116,25 @@ constexpr float kLazyMax = 8.0f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// One tile of one stream in LDS.  k^: the tile's two page blocks as the key prologue wrote
-// them, each [128 dims][16 keys].  V: 32 rows of 256 bytes at a pitch of 320 bytes (the
-// padding keeps the transposed V reads free of bank conflicts).  Both layouts were chosen by
-// measurement: transposed reads of these shapes run at about twice the rate of 16-byte row
-// reads of k^.
-constexpr int kVRow = kHeadDim + 32;         // V row pitch (elements)
-constexpr int kVRowChunks = kVRow / 8;       // 16-byte chunks per V row (16 data + 4 padding)
+// One tile of one stream in LDS, both halves read with transposed 8-byte reads (32 lanes per
+// LDS cycle, 64 banks of 4 bytes).
+//   k^: the tile's two page blocks as the prologue wrote them, each [128 dims][16 keys]
+//       (4 KB), the second one 128 bytes after the first one's end: a read's four 16-lane
+//       groups then cover all 64 banks (with the blocks 4 KB apart, groups 0 and 1 share banks
+//       and every read takes two cycles).
+//   V:  32 rows (keys) of 256 bytes; the 64-byte block j of row r holds dims 32 (j ^ (r % 4))
+//       .. +31.  A read's 32 lanes of one LDS cycle take 64 bytes of four consecutive rows at
+//       the same logical block, which the swizzle spreads over the four physical blocks.
+// Both layouts were checked free of bank conflicts with the LDS bank-conflict counter.
+constexpr int kKBlock = kHeadDim * kPageSize + 64;  // elements from one page block of k^ to the next
 struct alignas(16) TileBuf {
-  uint16_t k[2][kHeadDim][kPageSize];
-  uint16_t v[kKT][kVRow];
+  uint16_t k[2 * kKBlock];
+  uint16_t v[kKT][kHeadDim];
 };
 
 struct alignas(16) AttendSmem {
   union {
-    TileBuf tiles[kStreams][kBufs];            // the walk (144 KB)
+    TileBuf tiles[kStreams][kBufs];            // the walk (130 KB)
     float merge[4][2 + 64][64];                // stream 1's states, read by stream 0 at the end
   } u;
 };
@@ -494,31 +498,29 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
   TileBuf(&tb)[kBufs] = sm.u.tiles[st];
-  // Direct-to-LDS loads of the stream's tiles.  One load instruction writes 1 KB of
-  // contiguous LDS, lane l the 16 bytes at 16 l.  k^: the tile's two page blocks are 8 KB of
-  // contiguous workspace copied as they are (8 instructions; the second block of a row's last
-  // tile may lie past the row: its keys are masked, and the workspace is padded so the copy
-  // stays in bounds).  V: LDS chunk p = 64 u + l of the tile (10 instructions) is row p / 20,
-  // chunk p % 20 (chunks 16-19 are the row's padding and get a copy of chunk 15); rows 0-15
-  // are page 2 kt (instructions 0-4), rows 16-31 page 2 kt + 1 (instructions 5-9), slot = row
-  // % 16; keys past the row's end read its last key, so every value read is finite (their
-  // probabilities are 0).  The stream's four wavefronts split them by role: 0 and 1 issue k^
-  // 0-3 and 4-7, 2 and 3 issue the first and second page of V.
+  // Direct-to-LDS loads of the stream's tiles, four instructions per wavefront and step.  One
+  // instruction writes 1 KB of contiguous LDS, lane l the 16 bytes at 16 l, each lane from its
+  // own global address.
+  //   k^ (roles 0 and 1, page block `role` of the tile): 4 KB of contiguous workspace copied
+  //      as it is (the second block of a row's last tile may lie past the row: its keys are
+  //      masked, and the workspace is padded so the copy stays in bounds).
+  //   V (roles 2 and 3, page 2 kt + qg = rows 16 qg .. 16 qg + 15 of the tile): instruction i
+  //      writes rows 4 i .. 4 i + 3 of the page, lane l physical chunk l % 16 of row 4 i + l / 16,
+  //      which holds logical chunk 4 ((l % 16) / 4 ^ row % 4) + l % 4 of the row (the swizzle
+  //      above).  Slots past the row's end read its last key, so every value read is finite
+  //      (their probabilities are 0).
   const char* kh_plane = (const char*)(kh + ((size_t)hk * P.num_indices + p0) * kPageSize * kHeadDim);
   const uint32_t v_row_bytes = (uint32_t)Hkv * kHeadDim * 2u;
-  constexpr int kDma = 5;                       // most load instructions of one role per step
-  const int dma_n = role < 2 ? 4 : 5;           // instructions issued per step
-  const int dma_u0 = role < 2 ? 4 * role : 5 * (role - 2);  // its first instruction
-  // roles 0, 1: doff = byte offset in the tile's k^; roles 2, 3: doff = byte offset of the
-  // slot's row in the page, dch = of the chunk in the row
-  uint32_t doff[kDma], dch[kDma];
+  // k^: doff = byte offset in the page block; V: doff = byte offset of the slot's row in the
+  // page, dch = of the logical chunk in the row
+  uint32_t doff[4], dch[4];
 #pragma unroll
-  for (int i = 0; i < kDma; ++i) {
-    const int pc = 64 * (dma_u0 + i) + lane;
-    const int row = pc / kVRowChunks;
-    const int ch = min(pc - row * kVRowChunks, 15);
-    doff[i] = role < 2 ? 16u * pc : (uint32_t)(row & 15) * v_row_bytes;
-    dch[i] = 16u * ch;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + (lane >> 4);  // 0..15
+    const int pch = lane & 15;
+    const int lch = 4 * ((pch >> 2) ^ (row & 3)) + (pch & 3);
+    doff[i] = role < 2 ? 16u * (64 * i + lane) : (uint32_t)row * v_row_bytes;
+    dch[i] = 16u * lch;
   }
   // The walk is written once per phase (HP = hp: 0 loads k^ and computes S at the start of a
   // step, 1 loads V and computes S at its end), so neither path branches on its role.
@@ -534,30 +536,30 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int HP = decltype(hpc)::value;
     const int kt = kStreams * t + st;
     if constexpr (HP == 0) {
-      const char* kb = kh_plane + (size_t)min(kt, ntiles - 1) * 2 * kPageSize * kHeadDim * 2;
-      const uint32_t dst = lds_address(&tb[buf].k[0][0][0]) + 1024u * dma_u0;
+      const char* kb = kh_plane + ((size_t)min(kt, ntiles - 1) * 2 + qg) * kPageSize * kHeadDim * 2;
+      const uint32_t dst = lds_address(&tb[buf].k[kKBlock * qg]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_dma16(dst + 1024u * i, kb, doff[i]);
     } else {
       // only the item's own tiles count: the walk also loads for steps past a stream's end
       if (phys < 0 || phys >= P.num_pages) { poison |= kt < ntiles ? 1 : 0; phys = 0; }
       const char* vb = (const char*)(P.v_cache + ((size_t)phys * kPageSize * Hkv + hk) * kHeadDim);
-      const uint32_t dst = lds_address(&tb[buf].v[0][0]) + 1024u * dma_u0;
+      const uint32_t dst = lds_address(&tb[buf].v[16 * qg][0]);
       // the last slot of the page holding a key of the row (15 unless the page reaches the
       // row's end): the slots after it read that one (no branch: the step stays one block)
       const uint32_t smax_off = (uint32_t)(2 * kt + qg >= nidx - 1 ? lpl - 1 : 15) * v_row_bytes;
 #pragma unroll
-      for (int i = 0; i < 5; ++i) lds_dma16(dst + 1024u * i, vb, min(doff[i], smax_off) + dch[i]);
+      for (int i = 0; i < 4; ++i) lds_dma16(dst + 1024u * i, vb, min(doff[i], smax_off) + dch[i]);
     }
   };
   // End of step t: step t + 1 computes the scores of tile t + 2 and adds P.V of tile t, so
   // k^ of step t + 2 (issued at step t - 1) and V of step t (issued at step t - 2) must have
-  // landed.  The loads issued after them may stay in flight: k^ of step t + 3 (4 instructions),
-  // V of steps t + 1 and t + 2 (5 each).  Loads complete in issue order.
+  // landed.  The loads issued after them may stay in flight: k^ of step t + 3, V of steps
+  // t + 1 and t + 2 (4 instructions each).  Loads complete in issue order.
   auto wait_end = [&](auto hpc) {
     constexpr int HP = decltype(hpc)::value;
     if constexpr (HP == 0) wait_vmcnt<4>();
-    else wait_vmcnt<10>();
+    else wait_vmcnt<8>();
   };
   // The k^ operand of dim step s, lane (n, hh): key n, dims 16 s + 8 hh .. +7, two transposed
   // reads of the block holding key n (lane group G = lane / 16 reads dims 16 s + 8 (G / 2) +
@@ -569,8 +571,10 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   auto read_k = [&](int buf, bf16x8 (&ka)[8]) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].k[kg & 1][16 * s + k_row][k_col]));
-      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].k[kg & 1][16 * s + 4 + k_row][k_col]));
+      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(&tb[buf].k[kKBlock * (kg & 1) + (16 * s + k_row) * kPageSize + k_col]));
+      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(&tb[buf].k[kKBlock * (kg & 1) + (16 * s + 4 + k_row) * kPageSize + k_col]));
       ka[s] = __builtin_bit_cast(bf16x8, concat4(a0, a1));
     }
   };
@@ -589,8 +593,10 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].v[16 * ks + vr][32 * db + vc]));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].v[16 * ks + 8 + vr][32 * db + vc]));
+        // rows 16 ks + vr and 16 ks + 8 + vr are both = vr (mod 4): physical block db ^ (vr % 4)
+        const int col = 32 * (db ^ (vr & 3)) + vc;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].v[16 * ks + vr][col]));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tb[buf].v[16 * ks + 8 + vr][col]));
         va[2 * db + ks] = __builtin_bit_cast(bf16x8, concat4(v0, v1));
       }
   };
@@ -704,7 +710,7 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     wait_vmcnt<0>();
     {
       uint32_t* z = reinterpret_cast<uint32_t*>(&tb[3].v[0][0]);
-      constexpr int kWords = kKT * kVRow / 2;
+      constexpr int kWords = kKT * kHeadDim / 2;
       for (int i = (w >> 1) * 64 + lane; i < kWords; i += 256) z[i] = 0u;  // the stream's four wavefronts
     }
     __syncthreads();
