@@ -309,35 +309,52 @@ __device__ void key_part(const PrefillParams& P, uint16_t* __restrict__ kh, int 
   }
 }
 
+// 16 consecutive queries of one row and kQH consecutive query heads per wavefront (lane r +
+// 16 g: query i0 + r, dims 32 kb + 8 g .. +7): the queries' cos/sin are loaded once for the
+// kQH heads, and all the wavefront's loads go out before the first prologue.  (Measured on
+// the chunked-prefill workload: 2 heads per wavefront beat 1 and 4.)
+constexpr int kQH = 2;
 __device__ void query_part(const PrefillParams& P, uint16_t* __restrict__ qh, int qblk) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  // lanes r, r + 16, r + 32, r + 48 share vector v (dims 32 kb + 8 g .. +7 of block kb)
-  const long long nv = (long long)P.batch * P.num_q_heads * P.q_len;
-  const long long v = ((long long)qblk * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 16 + r;
-  const bool live = v < nv;
-  const long long vv = live ? v : 0;
-  const int i = (int)(vv % P.q_len);
-  const int b = (int)(vv / ((long long)P.num_q_heads * P.q_len));
-  int qp = P.qpos[(size_t)b * P.q_len + i];
+  const int nqi = (P.q_len + 15) / 16;
+  const int nhq = (P.num_q_heads + kQH - 1) / kQH;
+  const int task = qblk * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (task >= P.batch * nhq * nqi) return;
+  const int iq = task % nqi;
+  const int h0 = (task / nqi % nhq) * kQH;
+  const int b = task / (nqi * nhq);
+  const int i = 16 * iq + r;
+  const bool live_q = i < P.q_len;
+  int qp = live_q ? P.qpos[(size_t)b * P.q_len + i] : 0;
   if (qp < 0 || qp >= P.table_rows) qp = 0;  // the attention kernel poisons such a query's rows
   float4 cs[8];
   load_cos_sin(P.rope, qp, g, cs);
-  uint4 raw[4];
+  uint4 raw[kQH][4];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) raw[kb] = ldg16(P.q + (size_t)vv * kHeadDim + 32 * kb + 8 * g);
+  for (int h = 0; h < kQH; ++h) {
+    const bool live = live_q && h0 + h < P.num_q_heads;
+    const size_t v = ((size_t)b * P.num_q_heads + (live ? h0 + h : 0)) * P.q_len + (live ? i : 0);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) raw[h][kb] = ldg16(P.q + v * kHeadDim + 32 * kb + 8 * g);
+  }
   const bool qnorm = P.q_norm != nullptr;
   float wq[32];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int e = 0; e < 8; ++e) wq[kb * 8 + e] = qnorm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
-  bf16x8 op[4];
-  prologue_operand(raw, wq, qnorm, P.eps, cs, op);
-  if (live) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) stg16(qh + (size_t)v * kHeadDim + 32 * kb + 8 * g, as_u4(op[kb]));
+  for (int h = 0; h < kQH; ++h) {
+    if (h0 + h >= P.num_q_heads) break;  // uniform over the wavefront
+    bf16x8 op[4];
+    prologue_operand(raw[h], wq, qnorm, P.eps, cs, op);
+    if (live_q) {
+      const size_t v = ((size_t)b * P.num_q_heads + h0 + h) * P.q_len + i;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) stg16(qh + v * kHeadDim + 32 * kb + 8 * g, as_u4(op[kb]));
+    }
   }
 }
 
@@ -810,14 +827,15 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   int32_t* order = (int32_t*)(ws + kh_bytes + qh_bytes);
   int32_t* units = (int32_t*)(ws + kh_bytes + qh_bytes + order_bytes);
   // k^: per row up to max_pages_per_row * Hkv / HG tasks, 4 per workgroup, at most 512
-  // workgroups per row; two KV heads per wavefront (half the cos/sin reads) when Hkv is even.
-  // q^: 64 query vectors per workgroup.  Unit records: 8 units per workgroup.  Then one
-  // workgroup for the order of the units.
+  // workgroups per row; two KV heads per wavefront when Hkv is even, so each page's cos/sin is
+  // read once per two heads (measured: faster than one or four).  q^: 4 wavefront tasks per workgroup.  Unit records: 8
+  // units per workgroup.  Then one workgroup for the order of the units.
   const int hg = p.num_kv_heads % 2 == 0 ? 2 : 1;
   const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * (p.num_kv_heads / hg);
   const int kx = (int)std::min<long long>((row_tasks + 3) / 4, 512);
-  const long long nv = (long long)p.batch * p.num_q_heads * p.q_len;
-  const int nq = (int)((nv + 63) / 64);
+  const long long qtasks =
+      (long long)p.batch * ((p.num_q_heads + kQH - 1) / kQH) * ((p.q_len + 15) / 16);
+  const int nq = (int)((qtasks + 3) / 4);
   const int nqb = (p.q_len + kQB - 1) / kQB;
   const int U = p.batch * nqb;
   const int nu = (U + 7) / 8;
