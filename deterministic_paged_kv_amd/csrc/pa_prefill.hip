@@ -116,27 +116,30 @@ constexpr float kLazyMax = 8.0f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// One tile of one stream in LDS, both halves read with transposed 8-byte reads (32 lanes per
-// LDS cycle, 64 banks of 4 bytes).
-//   k^: the tile's two page blocks as the prologue wrote them, each [128 dims][16 keys]
-//       (4 KB), the second one 128 bytes after the first one's end: a read's four 16-lane
-//       groups then cover all 64 banks (with the blocks 4 KB apart, groups 0 and 1 share banks
-//       and every read takes two cycles).
+// One tile of one stream in LDS (64 banks of 4 bytes).
+//   k^: 32 rows (keys) of 256 bytes; the 16-byte chunk j of row r holds dims 8 (j ^ (r % 16))
+//       .. +7.  The S operands are 16-byte reads, 16 lanes per LDS cycle: 16 consecutive keys
+//       at the same logical chunk, which the swizzle spreads over all 16 physical chunks.
 //   V:  32 rows (keys) of 256 bytes; the 64-byte block j of row r holds dims 32 (j ^ (r % 4))
-//       .. +31.  A read's 32 lanes of one LDS cycle take 64 bytes of four consecutive rows at
-//       the same logical block, which the swizzle spreads over the four physical blocks.
+//       .. +31.  The P.V operands are transposed 8-byte reads, 32 lanes per LDS cycle: 64
+//       bytes of four consecutive rows at the same logical block, which the swizzle spreads
+//       over the four physical blocks.
 // Both layouts were checked free of bank conflicts with the LDS bank-conflict counter.
-constexpr int kKBlock = kHeadDim * kPageSize + 64;  // elements from one page block of k^ to the next
 struct alignas(16) TileBuf {
-  uint16_t k[2 * kKBlock];
+  uint16_t k[kKT][kHeadDim];
   uint16_t v[kKT][kHeadDim];
 };
 
+// The row's physical page numbers, for rows of up to kPageTable pages: the V loads look their
+// pages up here instead of with scalar loads, which share a wait counter with the LDS reads
+// and return out of order (a wait for one would drain every LDS read in flight).
+constexpr int kPageTable = 2048;
 struct alignas(16) AttendSmem {
   union {
-    TileBuf tiles[kStreams][kBufs];            // the walk (130 KB)
+    TileBuf tiles[kStreams][kBufs];            // the walk (128 KB)
     float merge[4][2 + 64][64];                // stream 1's states, read by stream 0 at the end
   } u;
+  int32_t pt[kPageTable];                      // 8 KB
 };
 
 // LDS byte address of a shared-memory pointer (the direct-to-LDS loads take it in M0).
@@ -228,20 +231,15 @@ __device__ void unit_order(const PrefillParams& P, int nqb, int U, int32_t* __re
 //                      written in that order, [B][Hq][Sq][128] bf16.
 //   the last one       the order of the work units, longest first.
 //
-// k^ layout: per KV head, one 4 KB block per index slot (kv_indptr[b] + page), holding the
-// page's 16 keys transposed, [128 dims][16 keys]; the attention kernel copies a tile's two
-// blocks to LDS as they are and reads its k^ operands with transposed LDS reads.  The wavefront
-// transposes each block through 4.5 KB of LDS of its own.
-constexpr int kTRow = kHeadDim + 16;  // row of the transposing buffer, padded by 32 bytes
+// k^ layout: per KV head, key j of row b at row (kv_indptr[b] * 16 + j) of [nnz * 16][128]
+// bf16 (the key's 128 dims contiguous), so a 32-key tile is 8 KB of contiguous workspace.
 constexpr int kPrologueThreads = 256;
 union PrologueSmem {
-  uint16_t tr_buf[4][kPageSize][kTRow];
   RankSmem rank;
 };
 
 template <int HG>
-__device__ void key_part(const PrefillParams& P, uint16_t* __restrict__ kh, int b, int xb, int kx,
-                         uint16_t (&tr_buf)[4][kPageSize][kTRow]) {
+__device__ void key_part(const PrefillParams& P, uint16_t* __restrict__ kh, int b, int xb, int kx) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
@@ -285,26 +283,13 @@ __device__ void key_part(const PrefillParams& P, uint16_t* __restrict__ kh, int 
     for (int h = 0; h < HG; ++h)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) raw[h][kb] = live ? ldg16(P.k_cache + src + h * kHeadDim + 32 * kb) : zero4;
-    uint16_t(&tb)[kPageSize][kTRow] = tr_buf[threadIdx.x >> 6];
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
       bf16x8 op[4];
       prologue_operand(raw[h], kw, knorm, P.eps, cs, op);
-      // key r's 128 values into row r of the transposing buffer, then out as [dim][key]: a
-      // transposed read gives lane (G, i) = (lane / 16, lane % 16) keys 4 G .. 4 G + 3 of dim
-      // 16 c + i, 8 contiguous bytes of the block's row for that dim
+      uint16_t* row = kh + (((size_t)(hk0 + h) * P.num_indices + (size_t)(p0 + pr)) * kPageSize + r) * kHeadDim;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        *reinterpret_cast<uint4*>(&tb[r][32 * kb + 8 * g]) = !key_ok ? nan4 : (live ? as_u4(op[kb]) : zero4);
-      wave_lds_sync();
-      uint16_t* blk = kh + ((size_t)(hk0 + h) * P.num_indices + (size_t)(p0 + pr)) * kPageSize * kHeadDim;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(&tb[4 * g + ((lane & 15) >> 2)][16 * c + 4 * (lane & 3)]));
-        *reinterpret_cast<i16x4*>(blk + (16 * c + (lane & 15)) * kPageSize + 4 * g) = v;
-      }
-      wave_lds_sync();
+      for (int kb = 0; kb < 4; ++kb) stg16(row + 32 * kb + 8 * g, !key_ok ? nan4 : (live ? as_u4(op[kb]) : zero4));
     }
   }
 }
@@ -426,7 +411,7 @@ __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const Prefil
   const int blk = (int)blockIdx.x;
   const int nk = P.batch * kx;
   if (blk < nk) {
-    key_part<HG>(P, kh, blk / kx, blk % kx, kx, sm.tr_buf);
+    key_part<HG>(P, kh, blk / kx, blk % kx, kx);
   } else if (blk < nk + nq) {
     query_part(P, qh, blk - nk);
   } else if (blk < nk + nq + nu) {
@@ -486,6 +471,15 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   const int free_end = load_uniform(rec, kUnitFreeEnd);
   int poison = load_uniform(rec, kUnitPoison);
   const int nsteps = (ntiles + kStreams - 1) / kStreams;
+  // the row's page numbers, loaded now and written to the LDS page table before the walk
+  const bool use_pt = nidx <= kPageTable;
+  constexpr int kPtPerThread = kPageTable / kAttendThreads;
+  int32_t ptv[kPtPerThread];
+#pragma unroll
+  for (int j = 0; j < kPtPerThread; ++j) {
+    const int i = tid + kAttendThreads * j;
+    ptv[j] = use_pt && i < nidx ? P.indices[p0 + i] : 0;
+  }
   const int qi = qb * kQB + 16 * qg + (n & 15);
   int qp = qi < Sq ? P.qpos[(size_t)b * Sq + qi] : -1;
   if (qp < 0 || qp >= P.table_rows) qp = -1;
@@ -518,9 +512,11 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   // Direct-to-LDS loads of the stream's tiles, four instructions per wavefront and step.  One
   // instruction writes 1 KB of contiguous LDS, lane l the 16 bytes at 16 l, each lane from its
   // own global address.
-  //   k^ (roles 0 and 1, page block `role` of the tile): 4 KB of contiguous workspace copied
-  //      as it is (the second block of a row's last tile may lie past the row: its keys are
-  //      masked, and the workspace is padded so the copy stays in bounds).
+  //   k^ (roles 0 and 1, keys 16 qg .. 16 qg + 15 of the tile): instruction i writes keys
+  //      16 qg + 4 i .. +3, lane l physical chunk l % 16 of key 16 qg + 4 i + l / 16, which
+  //      holds logical chunk (l % 16) ^ (key % 16) (the swizzle above).  A row's last tile may
+  //      reach past the row: those keys are masked, and the workspace is padded so the copy
+  //      stays in bounds.
   //   V (roles 2 and 3, page 2 kt + qg = rows 16 qg .. 16 qg + 15 of the tile): instruction i
   //      writes rows 4 i .. 4 i + 3 of the page, lane l physical chunk l % 16 of row 4 i + l / 16,
   //      which holds logical chunk 4 ((l % 16) / 4 ^ row % 4) + l % 4 of the row (the swizzle
@@ -528,33 +524,38 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   //      (their probabilities are 0).
   const char* kh_plane = (const char*)(kh + ((size_t)hk * P.num_indices + p0) * kPageSize * kHeadDim);
   const uint32_t v_row_bytes = (uint32_t)Hkv * kHeadDim * 2u;
-  // k^: doff = byte offset in the page block; V: doff = byte offset of the slot's row in the
-  // page, dch = of the logical chunk in the row
+  // k^: doff = byte offset of the key's logical chunk in the tile; V: doff = byte offset of
+  // the slot's row in the page, dch = of the logical chunk in the row
   uint32_t doff[4], dch[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * i + (lane >> 4);  // 0..15
     const int pch = lane & 15;
+    const int key = 16 * qg + row;
     const int lch = 4 * ((pch >> 2) ^ (row & 3)) + (pch & 3);
-    doff[i] = role < 2 ? 16u * (64 * i + lane) : (uint32_t)row * v_row_bytes;
+    doff[i] = role < 2 ? (uint32_t)key * 256u + 16u * (pch ^ (key & 15)) : (uint32_t)row * v_row_bytes;
     dch[i] = 16u * lch;
   }
   // The walk is written once per phase (HP = hp: 0 loads k^ and computes S at the start of a
   // step, 1 loads V and computes S at its end), so neither path branches on its role.
   // Physical page of this wavefront's half of the stream's tile at step t (clamped to the
   // row); phase 0 needs none.
-  auto page_of = [&](auto hpc, int t) -> int {
+  // (PT: from the LDS page table, which the walk fills before its first step; otherwise and
+  // before that, with a scalar load)
+  auto page_of = [&](auto hpc, auto ptc, int t) -> int {
     constexpr int HP = decltype(hpc)::value;
+    constexpr bool PT = decltype(ptc)::value;
     const int kt = kStreams * t + st;
     if constexpr (HP == 0) return 0;
+    else if constexpr (PT) return nidx > 0 ? __builtin_amdgcn_readfirstlane(sm.pt[min(2 * kt + qg, nidx - 1)]) : 0;
     else return nidx > 0 ? load_uniform(P.indices, p0 + min(2 * kt + qg, nidx - 1)) : 0;
   };
   auto issue = [&](auto hpc, int t, int buf, int phys) {
     constexpr int HP = decltype(hpc)::value;
     const int kt = kStreams * t + st;
     if constexpr (HP == 0) {
-      const char* kb = kh_plane + ((size_t)min(kt, ntiles - 1) * 2 + qg) * kPageSize * kHeadDim * 2;
-      const uint32_t dst = lds_address(&tb[buf].k[kKBlock * qg]);
+      const char* kb = kh_plane + (size_t)min(kt, ntiles - 1) * kKT * kHeadDim * 2;
+      const uint32_t dst = lds_address(&tb[buf].k[16 * qg][0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_dma16(dst + 1024u * i, kb, doff[i]);
     } else {
@@ -578,22 +579,16 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     if constexpr (HP == 0) wait_vmcnt<4>();
     else wait_vmcnt<8>();
   };
-  // The k^ operand of dim step s, lane (n, hh): key n, dims 16 s + 8 hh .. +7, two transposed
-  // reads of the block holding key n (lane group G = lane / 16 reads dims 16 s + 8 (G / 2) +
-  // 4 x .. +3 of keys 16 (G % 2) .. +15 of that block, and lane i of the group gets key
-  // 16 (G % 2) + i).
-  const int kg = lane >> 4;
-  const int k_row = 8 * (kg >> 1) + ((lane & 15) >> 2);
-  const int k_col = 4 * (lane & 3);
+  // The k^ operand of dim step s, lane (n, hh): key n, dims 16 s + 8 hh .. +7 = logical chunk
+  // 2 s + hh of row n, one 16-byte read at physical chunk (2 s + hh) ^ (n % 16).
+  uint32_t k_addr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) k_addr[s] = lds_address(&tb[0].k[n][8 * ((2 * s + hh) ^ (n & 15))]);
   auto read_k = [&](int buf, bf16x8 (&ka)[8]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(&tb[buf].k[kKBlock * (kg & 1) + (16 * s + k_row) * kPageSize + k_col]));
-      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(&tb[buf].k[kKBlock * (kg & 1) + (16 * s + 4 + k_row) * kPageSize + k_col]));
-      ka[s] = __builtin_bit_cast(bf16x8, concat4(a0, a1));
-    }
+    for (int s = 0; s < 8; ++s)
+      ka[s] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          (uintptr_t)(k_addr[s] + (uint32_t)(buf * sizeof(TileBuf))));
   };
   // S^T = k^ q^T of one tile
   auto mma_s = [&](const bf16x8 (&ka)[8], f32x16& s_out) {
@@ -654,10 +649,14 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   // reference move at step t rescales the accumulator after P.V of step t - 1 (relative to the
   // old reference) has been added.  On a stream's last step the scores of the next buffer are
   // computed but never used (no load into that buffer is then in flight).
-  auto step = [&](auto hpc, const int t, const int b_k, const int b_v, const int b_kload, const int b_vload,
+  auto step = [&](auto hpc, auto ptc, const int t, const int b_k, const int b_v, const int b_kload, const int b_vload,
                   int& phys_next, f32x16& s_cur, f32x16& s_nxt, bf16x8 (&pb_prev)[2]) {
     constexpr int HP = decltype(hpc)::value;
     const int kt = kStreams * t + st;
+    // the page of the next step's V load, looked up before this step's LDS reads (so that
+    // waiting for it does not wait for them)
+    const int ld = HP == 0 ? t + 3 : t + 2;
+    const int phys_after = page_of(hpc, ptc, ld + 1);
     // causal mask on tiles that reach past the block's first query, and on tiles past the
     // item's last one (a stream with one tile fewer than the other runs that step masked)
     if (kt >= ntiles || (kt + 1) * kKT > free_end) {
@@ -666,21 +665,31 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
       for (int i = 0; i < 16; ++i) s_cur[i] = 8 * (i >> 2) + (i & 3) < d ? s_cur[i] : -__builtin_inff();
     }
     bf16x8 ka[8], va[8];
-    read_k(b_k, ka);
     read_v(b_v, va);
+    read_k(b_k, ka);
     mma_pv(va, pb_prev);
+    // V reads first (P.V needs them first), then the P.V MFMAs each behind two k^ reads, so
+    // the LDS queue is not filled by one wavefront's whole burst before its MFMAs issue
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
     // k^ of step t + 3 (phase 0) or V of step t + 2 (phase 1), into the buffer freed at the
     // previous barrier.  Issued on every step (past the stream's end the tile index is clamped
     // and the loads land in buffers nothing reads), so the step has no branch around them.
-    {
-      const int ld = HP == 0 ? t + 3 : t + 2;
-      const int phys = phys_next;
-      phys_next = page_of(hpc, ld + 1);
-      issue(hpc, ld, HP == 0 ? b_kload : b_vload, phys);
-    }
+    issue(hpc, ld, HP == 0 ? b_kload : b_vload, phys_next);
+    phys_next = phys_after;
     mma_s(ka, s_nxt);
     float lp;
     tile_p(s_cur, m_neg, lp, pb_prev);
+    // the S MFMAs spread over the softmax's vector work
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+    }
     // the fix-up below runs when the probabilities against the current reference sum past
     // 2^kLazyMax (or overflow, or are NaN), or when the reference is unset and a key is visible
     const bool need = m_run == -__builtin_inff() ? lp != 0.0f : !(lp <= 256.0f);
@@ -704,7 +713,8 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
   };
 
-  auto walk = [&](auto hpc) {
+  auto walk = [&](auto hpc, auto ptc) {
+    const std::integral_constant<bool, false> scalar_pages;
     constexpr int HP = decltype(hpc)::value;
     // k^ of steps 0-2 (phase 0) or V of steps 0-1 (phase 1) go out right behind the q^ loads,
     // and one wait covers both (a single memory latency before the walk).  The wait also tells
@@ -719,12 +729,21 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
         issue(hpc, 1, 1, 0);
         issue(hpc, 2, 2, 0);
       } else {
-        issue(hpc, 0, 0, page_of(hpc, 0));
-        issue(hpc, 1, 1, page_of(hpc, 1));
-        phys_next = page_of(hpc, 2);
+        issue(hpc, 0, 0, page_of(hpc, scalar_pages, 0));
+        issue(hpc, 1, 1, page_of(hpc, scalar_pages, 1));
+        phys_next = page_of(hpc, scalar_pages, 2);
       }
     }
     wait_vmcnt<0>();
+    // every thread writes its share of the page table (whatever its own role), before the
+    // barrier below
+    if (use_pt) {
+#pragma unroll
+      for (int j = 0; j < kPtPerThread; ++j) {
+        const int i = tid + kAttendThreads * j;
+        if (i < nidx) sm.pt[i] = ptv[j];
+      }
+    }
     {
       uint32_t* z = reinterpret_cast<uint32_t*>(&tb[3].v[0][0]);
       constexpr int kWords = kKT * kHeadDim / 2;
@@ -744,14 +763,14 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     // of step k is k % 4 for both k^ and V
     int t = 0;
     for (; t + kBufs <= nsteps; t += kBufs) {
-      step(hpc, t, 1, 3, 3, 2, phys_next, s0, s1, pb);
-      step(hpc, t + 1, 2, 0, 0, 3, phys_next, s1, s0, pb);
-      step(hpc, t + 2, 3, 1, 1, 0, phys_next, s0, s1, pb);
-      step(hpc, t + 3, 0, 2, 2, 1, phys_next, s1, s0, pb);
+      step(hpc, ptc, t, 1, 3, 3, 2, phys_next, s0, s1, pb);
+      step(hpc, ptc, t + 1, 2, 0, 0, 3, phys_next, s1, s0, pb);
+      step(hpc, ptc, t + 2, 3, 1, 1, 0, phys_next, s0, s1, pb);
+      step(hpc, ptc, t + 3, 0, 2, 2, 1, phys_next, s1, s0, pb);
     }
-    if (t < nsteps) step(hpc, t, 1, 3, 3, 2, phys_next, s0, s1, pb);
-    if (t + 1 < nsteps) step(hpc, t + 1, 2, 0, 0, 3, phys_next, s1, s0, pb);
-    if (t + 2 < nsteps) step(hpc, t + 2, 3, 1, 1, 0, phys_next, s0, s1, pb);
+    if (t < nsteps) step(hpc, ptc, t, 1, 3, 3, 2, phys_next, s0, s1, pb);
+    if (t + 1 < nsteps) step(hpc, ptc, t + 1, 2, 0, 0, 3, phys_next, s1, s0, pb);
+    if (t + 2 < nsteps) step(hpc, ptc, t + 2, 3, 1, 1, 0, phys_next, s0, s1, pb);
     // P.V of the last step (its V landed before the last barrier); the loads issued past the
     // end drain before the tile buffers become the merge area
     if (nsteps > 0) {
@@ -761,8 +780,13 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     }
     wait_vmcnt<0>();
   };
-  if (hp == 0) walk(std::integral_constant<int, 0>{});
-  else walk(std::integral_constant<int, 1>{});
+  const std::integral_constant<int, 0> phase0;
+  const std::integral_constant<int, 1> phase1;
+  const std::integral_constant<bool, true> table;
+  const std::integral_constant<bool, false> no_table;
+  if (hp == 0) walk(phase0, no_table);  // phase 0 looks up no pages
+  else if (use_pt) walk(phase1, table);
+  else walk(phase1, no_table);
 
   // ---- merge the two streams of each query row (stream 0, then stream 1) and write out
   const bool out_poison = __syncthreads_or(poison) != 0;  // also: every wavefront is done with the tiles
