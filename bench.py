@@ -25,6 +25,7 @@ the host.
 Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 2000]
        python bench.py --profile-copy     # plain copy of a known size, for counter scaling
        python bench.py --ingest-counters FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
+       python bench.py --ingest-prefill-counters SQ1.csv SQ2.csv FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
            # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results of the decode run and of the copy
            # -> profiles/decode_qwen3_8b_counters.json (HBM bytes per decode launch)
 """
@@ -81,6 +82,8 @@ def source_hash(files) -> str:
 
 
 DECODE_SOURCES = ["deterministic_paged_kv_amd/csrc/pa_decode.hip", "deterministic_paged_kv_amd/csrc/pa_internal.h"]
+PREFILL_SOURCES = ["deterministic_paged_kv_amd/csrc/pa_prefill.hip", "deterministic_paged_kv_amd/csrc/pa_internal.h"]
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_chunked_counters.json")
 
 
 def traffic_from_profile(per_launch_alg_bytes):
@@ -92,6 +95,14 @@ def traffic_from_profile(per_launch_alg_bytes):
     if doc.get("source_hash") != source_hash(DECODE_SOURCES):
         return None
     return doc.get("hbm_bytes_per_launch")
+
+
+def prefill_counters_from_profile():
+    """The committed counter summary of the chunked-prefill kernels, if it matches the source."""
+    if not os.path.exists(PREFILL_COUNTERS):
+        return None
+    doc = json.load(open(PREFILL_COUNTERS))
+    return doc if doc.get("source_hash") == source_hash(PREFILL_SOURCES) else None
 
 
 def device_rotation(base, i, device):
@@ -399,11 +410,14 @@ def _counter_mean(path, counter, kernel_substr):
     kernel_substr, from a rocprofv3 counter_collection.csv."""
     import csv
 
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
-    if not vals:
+    per_dispatch = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+            # a counter may come as several rows per dispatch (one per hardware instance)
+            per_dispatch[r["Dispatch_Id"]] = per_dispatch.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per_dispatch:
         raise SystemExit(f"no {counter} rows for {kernel_substr!r} in {path}")
-    return sum(vals) / len(vals), len(vals)
+    return sum(per_dispatch.values()) / len(per_dispatch), len(per_dispatch)
 
 
 def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
@@ -443,6 +457,63 @@ def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(doc))
 
 
+# SQ counters of the attention kernel, two passes (at most 8 SQ counters per pass)
+PREFILL_SQ_PASSES = [
+    ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+     "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"],
+    ["SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES",
+     "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS"],
+]
+
+
+def ingest_prefill_counters(sq1_csv, sq2_csv, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Per-call counters of the chunked-prefill kernels (the bench.py prefill workload): SQ
+    counters of attend_kernel (mean per dispatch) and HBM bytes of both kernels from FETCH_SIZE /
+    WRITE_SIZE scaled by a plain 1 GiB copy.  Writes profiles/prefill_chunked_counters.json."""
+    import workloads
+
+    copy_bytes = 1 << 30
+    cf, _ = _counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    f_scale, w_scale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    sq = {}
+    for path, names in ((sq1_csv, PREFILL_SQ_PASSES[0]), (sq2_csv, PREFILL_SQ_PASSES[1])):
+        for c in names:
+            sq[c], _ = _counter_mean(path, c, "attend_kernel")
+    hbm = {}
+    for k in ("attend_kernel", "prologue_kernel"):
+        fk, _ = _counter_mean(fetch_csv, "FETCH_SIZE", k)
+        wk, _ = _counter_mean(write_csv, "WRITE_SIZE", k)
+        hbm[k] = {"fetch_bytes": int(fk * 1024.0 * f_scale), "write_bytes": int(wk * 1024.0 * w_scale)}
+    pb = workloads.chunked_prefill(canary=False)
+    flops = prefill_flops(pb)
+    mfma_flops = sq["SQ_INSTS_MFMA"] * 32768  # every MFMA of the kernel is v_mfma_f32_32x32x16_bf16
+    doc = {
+        "kernels": PREFILL_KERNELS, "workload": "chunked_prefill", "source_hash": source_hash(PREFILL_SOURCES),
+        "attend_sq_per_dispatch": {k: int(round(v)) for k, v in sq.items()},
+        "attend_derived": {
+            # SQ_WAVE_CYCLES and the SQ_ACTIVE/WAIT counters count in units of 4 cycles
+            "mfma_busy_cycles_per_mfma": round(sq["SQ_VALU_MFMA_BUSY_CYCLES"] / sq["SQ_INSTS_MFMA"], 2),
+            "mfma_flops_over_algorithmic": round(mfma_flops / flops, 4),
+            "valu_insts_per_mfma": round(sq["SQ_INSTS_VALU"] / sq["SQ_INSTS_MFMA"], 2),
+            "lds_insts_per_mfma": round(sq["SQ_INSTS_LDS"] / sq["SQ_INSTS_MFMA"], 2),
+            "salu_insts_per_mfma": round(sq["SQ_INSTS_SALU"] / sq["SQ_INSTS_MFMA"], 2),
+            "lds_bank_conflict_over_active": round(sq["SQ_LDS_BANK_CONFLICT"] / max(sq["SQ_LDS_IDX_ACTIVE"], 1), 4),
+            "wave_time_waiting_frac": round(sq["SQ_WAIT_ANY"] / sq["SQ_WAVE_CYCLES"], 4),
+            "wave_time_issue_stalled_frac": round(sq["SQ_WAIT_INST_ANY"] / sq["SQ_WAVE_CYCLES"], 4),
+            "wave_time_issuing_frac": round(sq["SQ_ACTIVE_INST_ANY"] / sq["SQ_WAVE_CYCLES"], 4),
+        },
+        "hbm_bytes_per_call": hbm,
+        "hbm_bytes_per_call_total": sum(v["fetch_bytes"] + v["write_bytes"] for v in hbm.values()),
+        "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+        "algorithmic_flops_per_call": flops,
+    }
+    with open(PREFILL_COUNTERS, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(doc))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,9 +525,13 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="time only the chunked prefill")
     ap.add_argument("--backward-only", action="store_true", help="time only the full-prefill backward")
     ap.add_argument("--ingest-counters", nargs=4, metavar="CSV")
+    ap.add_argument("--ingest-prefill-counters", nargs=6, metavar="CSV")
     args = ap.parse_args()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
+        return
+    if args.ingest_prefill_counters:
+        ingest_prefill_counters(*args.ingest_prefill_counters)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -640,6 +715,13 @@ def main():
                          "traffic": None, "kernel": PREFILL_KERNELS + " (whole call)",
                          "algorithmic_flops_per_call": flops, "avg_call_ms": round(p_launch, 5)},
         }
+        pc = prefill_counters_from_profile()
+        if pc is not None:
+            # HBM bytes of both kernels per call (counters of the same source), and the attention
+            # kernel's instruction mix: where the time goes, against the MFMA-bound target
+            result["prefill"]["roofline"]["traffic"] = pc["hbm_bytes_per_call_total"]
+            result["prefill"]["counters"] = {"source": os.path.relpath(PREFILL_COUNTERS, ROOT),
+                                             **pc["attend_derived"]}
         if not args.prefill_only:
             print("[bench] timing the full-prefill backward", file=sys.stderr, flush=True)
             result["prefill_backward"] = bench_backward(device, max(10, args.steps // 10), 3)
