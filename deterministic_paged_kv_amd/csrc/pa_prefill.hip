@@ -524,6 +524,8 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   //      (their probabilities are 0).
   const char* kh_plane = (const char*)(kh + ((size_t)hk * P.num_indices + p0) * kPageSize * kHeadDim);
   const uint32_t v_row_bytes = (uint32_t)Hkv * kHeadDim * 2u;
+  const uint32_t v_page_bytes = v_row_bytes * kPageSize;
+  const char* v_head = (const char*)(P.v_cache + (size_t)hk * kHeadDim);  // the KV head's slice of page 0
   // k^: doff = byte offset of the key's logical chunk in the tile; V: doff = byte offset of
   // the slot's row in the page, dch = of the logical chunk in the row
   uint32_t doff[4], dch[4];
@@ -560,8 +562,10 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
       for (int i = 0; i < 4; ++i) lds_dma16(dst + 1024u * i, kb, doff[i]);
     } else {
       // only the item's own tiles count: the walk also loads for steps past a stream's end
-      if (phys < 0 || phys >= P.num_pages) { poison |= kt < ntiles ? 1 : 0; phys = 0; }
-      const char* vb = (const char*)(P.v_cache + ((size_t)phys * kPageSize * Hkv + hk) * kHeadDim);
+      // an out-of-range page reads page 0 (and poisons the item if the tile is the item's own)
+      const bool phys_ok = (uint32_t)phys < (uint32_t)P.num_pages;
+      poison |= (!phys_ok && kt < ntiles) ? 1 : 0;
+      const char* vb = v_head + (uint64_t)(phys_ok ? (uint32_t)phys : 0u) * v_page_bytes;
       const uint32_t dst = lds_address(&tb[buf].v[16 * qg][0]);
       // the last slot of the page holding a key of the row (15 unless the page reaches the
       // row's end): the slots after it read that one (no branch: the step stays one block)
