@@ -333,9 +333,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //   order  one int32 per work unit (row, block of kPrefillQB queries): the units, longest
 //          first;
 //   units  one record of kUnitInts int32 per work unit: what the attention kernel needs of
-//          the unit's row and queries (extent, length, tiles, poison), see pa_prefill.hip.
+//          the unit's row and queries (extent, length, tiles, poison, the row's first page
+//          numbers), see pa_prefill.hip.
 constexpr int kPrefillQB = 32;  // queries per work unit of the attention kernel
-constexpr int kUnitInts = 8;
+constexpr int kUnitInts = 32;
 inline size_t prefill_kh_bytes(int hkv, int num_indices) {
   return align256(((size_t)hkv * num_indices * kPageSize + 32) * kHeadDim * 2);
 }

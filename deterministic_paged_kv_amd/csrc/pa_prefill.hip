@@ -134,10 +134,16 @@ struct alignas(16) TileBuf {
 // pages up here instead of with scalar loads, which share a wait counter with the LDS reads
 // and return out of order (a wait for one would drain every LDS read in flight).
 constexpr int kPageTable = 2048;
+// The output rows of one wavefront (32 rows of 128 BF16), padded to 264 bytes so that the
+// staging writes (lane = row, 8 bytes) spread over all banks.
+constexpr int kOutPitch = kHeadDim + 4;
 struct alignas(16) AttendSmem {
   union {
     TileBuf tiles[kStreams][kBufs];            // the walk (128 KB)
-    float merge[4][2 + 64][64];                // stream 1's states, read by stream 0 at the end
+    struct {
+      float merge[4][2 + 64][64];              // stream 1's states, read by stream 0 at the end
+      uint16_t out[4][32][kOutPitch];          // stream 0's output rows, staged for row-wise stores
+    } m;
   } u;
   int32_t pt[kPageTable];                      // 8 KB
 };
@@ -355,7 +361,12 @@ __device__ void query_part(const PrefillParams& P, uint16_t* __restrict__ qh, in
 //               query of the block has a position out of the RoPE table or a cache_position
 //               that differs from it: every output of the unit is then NaN
 // A bad row's or query's position counts as -1 (sees nothing) in ntiles and free_end.
-enum { kUnitP0 = 0, kUnitNidx, kUnitLpl, kUnitL, kUnitTiles, kUnitFreeEnd, kUnitPoison };
+enum { kUnitP0 = 0, kUnitNidx, kUnitLpl, kUnitL, kUnitTiles, kUnitFreeEnd, kUnitPoison, kUnitPage0 = 8 };
+// the record also holds the physical numbers of the row's pages 0 .. kUnitPages - 1 (clamped to
+// the last page; 0 for an empty or bad row): the V loads issued before the walk take them from
+// there instead of from the page table, one memory latency earlier
+constexpr int kUnitPages = 12;
+static_assert(kUnitPage0 + kUnitPages <= kUnitInts, "unit record size");
 __device__ void unit_part(const PrefillParams& P, int32_t* __restrict__ units, int ublk) {
   const int lane = threadIdx.x & 63;
   const int i32 = lane & 31;
@@ -398,6 +409,10 @@ __device__ void unit_part(const PrefillParams& P, int32_t* __restrict__ units, i
 #pragma unroll
     for (int f = 1; f < 7; ++f) v = i32 == f ? rec[f] : v;
     units[(size_t)u * kUnitInts + i32] = v;
+  }
+  if (live_unit && i32 >= kUnitPage0 && i32 < kUnitPage0 + kUnitPages) {
+    const int k = i32 - kUnitPage0;
+    units[(size_t)u * kUnitInts + i32] = (!bad && nidx > 0) ? P.indices[p0 + min(k, nidx - 1)] : 0;
   }
 }
 
@@ -718,7 +733,6 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   };
 
   auto walk = [&](auto hpc, auto ptc) {
-    const std::integral_constant<bool, false> scalar_pages;
     constexpr int HP = decltype(hpc)::value;
     // k^ of steps 0-2 (phase 0) or V of steps 0-1 (phase 1) go out right behind the q^ loads,
     // and one wait covers both (a single memory latency before the walk).  The wait also tells
@@ -733,9 +747,10 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
         issue(hpc, 1, 1, 0);
         issue(hpc, 2, 2, 0);
       } else {
-        issue(hpc, 0, 0, page_of(hpc, scalar_pages, 0));
-        issue(hpc, 1, 1, page_of(hpc, scalar_pages, 1));
-        phys_next = page_of(hpc, scalar_pages, 2);
+        // pages 2 kt + qg of tiles kt = st, 2 + st, 4 + st: from the unit record
+        issue(hpc, 0, 0, load_uniform(rec, kUnitPage0 + 2 * st + qg));
+        issue(hpc, 1, 1, load_uniform(rec, kUnitPage0 + 4 + 2 * st + qg));
+        phys_next = load_uniform(rec, kUnitPage0 + 8 + 2 * st + qg);
       }
     }
     wait_vmcnt<0>();
@@ -796,19 +811,19 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   const bool out_poison = __syncthreads_or(poison) != 0;  // also: every wavefront is done with the tiles
   const int pair = w >> 1;  // wavefronts 2 pair and 2 pair + 1 hold the same rows, streams 0 and 1
   if (st == 1) {
-    sm.u.merge[pair][0][lane] = m_run;
-    sm.u.merge[pair][1][lane] = l_part;
+    sm.u.m.merge[pair][0][lane] = m_run;
+    sm.u.m.merge[pair][1][lane] = l_part;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.u.merge[pair][2 + 16 * db + i][lane] = acc[db][i];
+      for (int i = 0; i < 16; ++i) sm.u.m.merge[pair][2 + 16 * db + i][lane] = acc[db][i];
   }
   __syncthreads();
   if (st == 1) return;
   {
 #pragma clang fp contract(off)
-    const float m1 = sm.u.merge[pair][0][lane];
-    const float l1 = sm.u.merge[pair][1][lane];
+    const float m1 = sm.u.m.merge[pair][0][lane];
+    const float l1 = sm.u.m.merge[pair][1][lane];
     const float mx = fmaxf(m_run, m1);
     const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx);
     const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
@@ -818,6 +833,9 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     const bool empty = l == 0.0f;
     const float inv = empty ? 0.0f : 1.0f / l;
     const size_t row = ((size_t)b * P.num_q_heads + hk * G + (gi < G ? gi : 0)) * Sq + (qi < Sq ? qi : 0);
+    // the wavefront's rows go through LDS (lane (n, hh) holds dims 32 db + 8 q4 + 4 hh .. +3
+    // of row n) and out as whole rows: 16 bytes per lane, four rows per store
+    uint16_t(&stage)[32][kOutPitch] = sm.u.m.out[pair];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -826,13 +844,23 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q4 + e;
-          const float v = acc[db][i] * a0 + sm.u.merge[pair][2 + 16 * db + i][lane] * a1;
+          const float v = acc[db][i] * a0 + sm.u.m.merge[pair][2 + 16 * db + i][lane] * a1;
           o[e] = out_poison ? __builtin_nanf("") : v * inv;
         }
-        if (live) {
-          const i16x4 pk = pack_bf16(o[0], o[1], o[2], o[3]);
-          *reinterpret_cast<i16x4*>(P.out + row * kHeadDim + 32 * db + 8 * q4 + 4 * hh) = pk;
-        }
+        *reinterpret_cast<i16x4*>(&stage[n][32 * db + 8 * q4 + 4 * hh]) = pack_bf16(o[0], o[1], o[2], o[3]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + (lane >> 4);  // row (column n of the MFMAs)
+      const int ch = lane & 15;           // 16-byte chunk of the row
+      const int gr = hg * 4 + 2 * hp + (r >> 4);
+      const int qr = qb * kQB + 16 * qg + (r & 15);
+      const uint2 lo = *reinterpret_cast<const uint2*>(&stage[r][8 * ch]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&stage[r][8 * ch + 4]);
+      if (gr < G && qr < Sq) {
+        const size_t orow = ((size_t)b * P.num_q_heads + hk * G + gr) * Sq + qr;
+        stg16(P.out + orow * kHeadDim + 8 * ch, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
     }
     if (live && hh == 0) {
