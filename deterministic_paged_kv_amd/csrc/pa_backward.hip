@@ -267,9 +267,21 @@ __device__ __forceinline__ void sum16(float v[8][4]) {
 // ---------------------------------------------------------------------------------------
 // 2. dq
 // ---------------------------------------------------------------------------------------
-struct DqSmem {
-  uint16_t k[2][kKTile][kRowB];
-  uint16_t v[2][kKTile][kRowB];
+// k^ and V tiles in LDS: rows of 256 bytes, the 16-byte chunk c of row j stored at chunk
+// c ^ dq_swz(j).  Both read patterns then use all 64 banks without conflict: the S and dP
+// operands (16-byte reads, 16 lanes per LDS cycle: 16 consecutive rows at one chunk, which
+// dq_swz maps to 16 distinct chunks) and the transposed K^T reads for dQ (8-byte reads, 32
+// lanes per cycle: 32 bytes of 8 consecutive rows, whose chunk pairs dq_swz keeps together and
+// spreads over 8 distinct pairs).  (A padded 288-byte pitch was conflict-free for the second
+// pattern only; the first then took two LDS cycles per read.)
+// The tiles are arrays of 16-byte chunks, so that the compiler emits whole 16-byte LDS
+// accesses (it splits them into 4-byte pairs where it cannot prove the alignment).
+__device__ __forceinline__ int dq_swz(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
+// chunk index of the 16-byte chunk c (dims 8 c .. 8 c + 7) of row j in a swizzled tile
+__device__ __forceinline__ int dq_chunk(int row, int c) { return row * (kHeadDim / 8) + (c ^ dq_swz(row)); }
+struct alignas(16) DqSmem {
+  uint4 k[2][kKTile * kHeadDim / 8];
+  uint4 v[2][kKTile * kHeadDim / 8];
   int kpos[2][kKTile];
 };
 
@@ -360,24 +372,33 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      *reinterpret_cast<uint4*>(&sm.k[buf][16 * u + rt][col * 8]) = kr[u];
-      *reinterpret_cast<uint4*>(&sm.v[buf][16 * u + rt][col * 8]) = vr[u];
+      sm.k[buf][dq_chunk(16 * u + rt, col)] = kr[u];
+      sm.v[buf][dq_chunk(16 * u + rt, col)] = vr[u];
     }
     if (tid < kKTile) sm.kpos[buf][tid] = kp_next;
   };
   // the first key tile at or after kt holding a key at or before the block's last query
   // position (tiles whose keys all come after every query contribute nothing)
   const int n16 = (S + 15) / 16;
+  // (the visibility of 64 consecutive tiles is one ballot; the window is kept, so the walk
+  // loads the bounds once per 64 tiles instead of waiting for them at every tile)
+  int wbase = -64;
+  unsigned long long wmask = 0;
   auto next_tile = [&](int kt) -> int {
-    for (; kt < ntiles; kt += 64) {
-      const int c = kt + lane;
-      int m = INT32_MAX;
-      if (c < ntiles) {
-        m = P.tmin[(size_t)b * n16 + 2 * c];
-        if (2 * c + 1 < n16) m = min(m, P.tmin[(size_t)b * n16 + 2 * c + 1]);
+    while (kt < ntiles) {
+      if (kt < wbase || kt >= wbase + 64) {
+        wbase = kt;
+        const int c = kt + lane;
+        int m = INT32_MAX;
+        if (c < ntiles) {
+          m = P.tmin[(size_t)b * n16 + 2 * c];
+          if (2 * c + 1 < n16) m = min(m, P.tmin[(size_t)b * n16 + 2 * c + 1]);
+        }
+        wmask = __builtin_amdgcn_ballot_w64(m <= qmax);
       }
-      const unsigned long long hit = __builtin_amdgcn_ballot_w64(m <= qmax);
+      const unsigned long long hit = wmask >> (kt - wbase);
       if (hit != 0) return kt + (int)__builtin_ctzll(hit);
+      kt = wbase + 64;
     }
     return ntiles;
   };
@@ -398,8 +419,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
           bf16x8 ka[4], va[4];
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            ka[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.k[buf][16 * ks + r][32 * kb + 8 * g]));
-            va[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.v[buf][16 * ks + r][32 * kb + 8 * g]));
+            ka[kb] = __builtin_bit_cast(bf16x8, sm.k[buf][dq_chunk(16 * ks + r, 4 * kb + g)]);
+            va[kb] = __builtin_bit_cast(bf16x8, sm.v[buf][dq_chunk(16 * ks + r, 4 * kb + g)]);
           }
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
@@ -431,8 +452,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
         // 16+4g+(e-4) (e >= 4) in both operands; K^T from two transposed reads per column block
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][jr][16 * nb + jc]));
-          const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.k[buf][16 + jr][16 * nb + jc]));
+          // dims 16 nb + jc .. +3: chunk 2 nb + jc / 8, its half jc % 8 / 4
+          const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(reinterpret_cast<char*>(&sm.k[buf][dq_chunk(jr, 2 * nb + (jc >> 3))]) + 2 * (jc & 7)));
+          const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(reinterpret_cast<char*>(&sm.k[buf][dq_chunk(16 + jr, 2 * nb + (jc >> 3))]) + 2 * (jc & 7)));
           const bf16x8 kt8 = __builtin_bit_cast(bf16x8, concat4(k0, k1));
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -574,16 +598,26 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
 
   // the first query tile at or after qt holding a query that some key of the block can see
   // (tiles where every query precedes every key contribute nothing and are not visited)
+  // (the visibility of 64 consecutive tiles is one ballot; the window is kept, so the walk
+  // loads the bounds once per 64 tiles instead of waiting for them at every tile, and every
+  // query head of the group walks the same tiles)
+  int wbase = -64;
+  unsigned long long wmask = 0;
   auto next_tile = [&](int qt) -> int {
-    for (; qt < nqt; qt += 64) {
-      const int c = qt + lane;
-      int m = -1;
-      if (c < nqt) {
-        m = P.tmax[(size_t)b * n16 + 2 * c];
-        if (2 * c + 1 < n16) m = max(m, P.tmax[(size_t)b * n16 + 2 * c + 1]);
+    while (qt < nqt) {
+      if (qt < wbase || qt >= wbase + 64) {
+        wbase = qt;
+        const int c = qt + lane;
+        int m = -1;
+        if (c < nqt) {
+          m = P.tmax[(size_t)b * n16 + 2 * c];
+          if (2 * c + 1 < n16) m = max(m, P.tmax[(size_t)b * n16 + 2 * c + 1]);
+        }
+        wmask = __builtin_amdgcn_ballot_w64(m >= bmin);
       }
-      const unsigned long long hit = __builtin_amdgcn_ballot_w64(m >= bmin);
+      const unsigned long long hit = wmask >> (qt - wbase);
       if (hit != 0) return qt + (int)__builtin_ctzll(hit);
+      qt = wbase + 64;
     }
     return nqt;
   };
