@@ -353,6 +353,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
   // position; loaded one tile ahead, written to LDS after the current tile is used
   uint4 kr[2], vr[2];
   int kp_next = INT32_MAX;
+  bool klive_next = false;
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -363,10 +364,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
       vr[u] = live ? ldg16(P.v + off) : make_uint4(0, 0, 0, 0);
     }
     if (tid < kKTile) {
+      // the raw position, checked in store_tile (so that no wait for it falls inside the
+      // current tile's work)
       const int j = kt * kKTile + tid;
-      bool kb_ = false;
-      // keys past the row get a position no query can see
-      kp_next = j < S ? safe_pos(P, b, j, kb_) : INT32_MAX;
+      klive_next = j < S;
+      kp_next = P.pos[(size_t)b * S + (klive_next ? j : 0)];
     }
   };
   auto store_tile = [&](int buf) {
@@ -375,7 +377,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
       sm.k[buf][dq_chunk(16 * u + rt, col)] = kr[u];
       sm.v[buf][dq_chunk(16 * u + rt, col)] = vr[u];
     }
-    if (tid < kKTile) sm.kpos[buf][tid] = kp_next;
+    // keys past the row get a position no query can see; a position outside the RoPE table
+    // reads as 0 (the key's own rows are poisoned)
+    if (tid < kKTile) sm.kpos[buf][tid] = !klive_next ? INT32_MAX : (kp_next < 0 || kp_next >= P.table_rows ? 0 : kp_next);
   };
   // the first key tile at or after kt holding a key at or before the block's last query
   // position (tiles whose keys all come after every query contribute nothing)
@@ -603,6 +607,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
   // query head of the group walks the same tiles)
   int wbase = -64;
   unsigned long long wmask = 0;
+  int wmax = -1;  // lane c: the greatest query position of tile wbase + c
   auto next_tile = [&](int qt) -> int {
     while (qt < nqt) {
       if (qt < wbase || qt >= wbase + 64) {
@@ -613,6 +618,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
           m = P.tmax[(size_t)b * n16 + 2 * c];
           if (2 * c + 1 < n16) m = max(m, P.tmax[(size_t)b * n16 + 2 * c + 1]);
         }
+        wmax = m;
         wmask = __builtin_amdgcn_ballot_w64(m >= bmin);
       }
       const unsigned long long hit = wmask >> (qt - wbase);
@@ -621,14 +627,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
     }
     return nqt;
   };
+  // the greatest query position of tile qt, which the current window holds
+  auto tile_qmax = [&](int qt) -> int { return __builtin_amdgcn_readlane(wmax, qt - wbase); };
 
   // a tile's share of one thread: q^ and dout rows rt and rt + 16, and (threads < 32) one
   // query's lse, Dv and position; loaded one tile ahead, written after the current tile is used
   const int rt = tid >> 4;
   const int col = tid & 15;
+  // (the loads are unconditional, on a clamped index, and nothing uses their values before
+  // store_tile: no wait for them falls inside the current tile's work)
   uint4 qr[2], dr[2];
   float lse_n = 0.0f, dv_n = 0.0f;
   int qp_n = -1;
+  bool qlive_n = false;
   auto load_tile = [&](int gi, int qt) {
     const size_t qrow0 = ((size_t)b * P.num_q_heads + hk * G + gi) * S;
 #pragma unroll
@@ -641,11 +652,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
     }
     if (tid < kQB) {
       const int i = qt * kQB + tid;
-      const bool live = i < S;
-      bool qb_ = false;
-      lse_n = live ? P.lse[qrow0 + i] * kLog2e : 0.0f;
-      dv_n = live ? P.dvec[qrow0 + i] : 0.0f;
-      qp_n = live ? safe_pos(P, b, i, qb_) : -1;
+      qlive_n = i < S;
+      const int ic = qlive_n ? i : 0;
+      lse_n = P.lse[qrow0 + ic];
+      dv_n = P.dvec[qrow0 + ic];
+      qp_n = P.pos[(size_t)b * S + ic];
     }
   };
   auto store_tile = [&](int buf) {
@@ -655,16 +666,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
       *reinterpret_cast<uint4*>(&sm[buf].d[16 * u + rt][col * 8]) = dr[u];
     }
     if (tid < kQB) {
-      sm[buf].lse2[tid] = lse_n;
-      sm[buf].dvec[tid] = dv_n;
-      sm[buf].qpos[tid] = qp_n;
+      // a position outside the RoPE table reads as 0 (the query's own rows are poisoned)
+      sm[buf].lse2[tid] = qlive_n ? lse_n * kLog2e : 0.0f;
+      sm[buf].dvec[tid] = qlive_n ? dv_n : 0.0f;
+      sm[buf].qpos[tid] = qlive_n ? (qp_n < 0 || qp_n >= P.table_rows ? 0 : qp_n) : -1;
     }
   };
 
   // query heads of the group in ascending order, each head's visited tiles in ascending order
+  // (each tile's greatest query position comes from the window, read when the tile is chosen)
   const int first = __builtin_amdgcn_readfirstlane(next_tile(0));
   if (first < nqt) {
     int gi = 0, qt = first, buf = 0;
+    int qmax = __builtin_amdgcn_readfirstlane(tile_qmax(first));
     load_tile(gi, qt);
     store_tile(0);
     __syncthreads();
@@ -673,15 +687,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
       int nq = __builtin_amdgcn_readfirstlane(next_tile(qt + 1));
       if (nq >= nqt) {
         ngi = gi + 1;
-        nq = first;
+        nq = __builtin_amdgcn_readfirstlane(next_tile(first));  // = first, with the window holding it
       }
       const bool more = ngi < G;
+      const int qmax_next = __builtin_amdgcn_readfirstlane(tile_qmax(nq < nqt ? nq : wbase));
       if (more) load_tile(ngi, nq);
       const DkdvTile& T = sm[buf];
-      int qmax = T.qpos[lane & 31];
-#pragma unroll
-      for (int sh = 1; sh < 32; sh <<= 1) qmax = max(qmax, __shfl_xor(qmax, sh));
-      qmax = __builtin_amdgcn_readfirstlane(qmax);
       if (qmax >= kmin) {
         // S = Q^ K^T and dP = dO V^T: [t] queries 16 t + 4 g + i, key r
         f32x4 sc[2], dp[2];
@@ -730,6 +741,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
       if (!more) break;
       gi = ngi;
       qt = nq;
+      qmax = qmax_next;
       buf ^= 1;
     }
   }
