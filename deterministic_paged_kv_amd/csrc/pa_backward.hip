@@ -357,11 +357,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      // a key past the row reads key 0: its position (INT32_MAX) makes its P and dS zero
       const int j = kt * kKTile + 16 * u + rt;
-      const bool live = j < S;
-      const size_t off = (krow0 + (live ? j : 0)) * kHeadDim + col * 8;
-      kr[u] = live ? ldg16(P.kh + off) : make_uint4(0, 0, 0, 0);
-      vr[u] = live ? ldg16(P.v + off) : make_uint4(0, 0, 0, 0);
+      const size_t off = (krow0 + (j < S ? j : 0)) * kHeadDim + col * 8;
+      kr[u] = ldg16(P.kh + off);
+      vr[u] = ldg16(P.v + off);
     }
     if (tid < kKTile) {
       // the raw position, checked in store_tile (so that no wait for it falls inside the
@@ -644,11 +644,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
     const size_t qrow0 = ((size_t)b * P.num_q_heads + hk * G + gi) * S;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      // a query past the row reads query 0: its position (-1) makes its P and dS zero
       const int i = qt * kQB + 16 * u + rt;
-      const bool live = i < S;
-      const size_t off = (qrow0 + (live ? i : 0)) * kHeadDim + col * 8;
-      qr[u] = live ? ldg16(P.qh + off) : make_uint4(0, 0, 0, 0);
-      dr[u] = live ? ldg16(P.dout + off) : make_uint4(0, 0, 0, 0);
+      const size_t off = (qrow0 + (i < S ? i : 0)) * kHeadDim + col * 8;
+      qr[u] = ldg16(P.qh + off);
+      dr[u] = ldg16(P.dout + off);
     }
     if (tid < kQB) {
       const int i = qt * kQB + tid;
@@ -694,7 +694,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
       if (more) load_tile(ngi, nq);
       const DkdvTile& T = sm[buf];
       if (qmax >= kmin) {
-        // S = Q^ K^T and dP = dO V^T: [t] queries 16 t + 4 g + i, key r
+        // S = Q^ K^T and dP = dO V^T: [t] queries 16 t + 4 g + i, key r.  The 16 operand
+        // reads go out first, so their LDS latency is paid once per tile.
+        bf16x8 qa[2][4], da[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            qa[t][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.q[16 * t + r][32 * kb + 8 * g]));
+            da[t][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.d[16 * t + r][32 * kb + 8 * g]));
+          }
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
         f32x4 sc[2], dp[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -702,10 +712,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
           dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.q[16 * t + r][32 * kb + 8 * g]));
-            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.d[16 * t + r][32 * kb + 8 * g]));
-            sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kop[kb], sc[t], 0, 0, 0);
-            dp[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vop[kb], dp[t], 0, 0, 0);
+            sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t][kb], kop[kb], sc[t], 0, 0, 0);
+            dp[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[t][kb], vop[kb], dp[t], 0, 0, 0);
           }
         }
         i16x4 pb[2], dsb[2];
