@@ -542,7 +542,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
 constexpr int kKBlock = 64;   // keys per workgroup, 16 per wavefront
 
 // one 32-query tile of one query head, shared by the workgroup's four wavefronts
-struct DkdvTile {
+struct alignas(16) DkdvTile {
   uint16_t q[kQB][kRowB];
   uint16_t d[kQB][kRowB];
   float lse2[kQB];
@@ -716,16 +716,38 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
             dp[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[t][kb], vop[kb], dp[t], 0, 0, 0);
           }
         }
+        // the dV and dK operands (transposed reads, 32 per tile) go out before the softmax
+        // arithmetic, which covers their LDS latency; the per-query values come as 16-byte reads
+        bf16x8 dto[8], qto[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[jr][16 * nb + jc]));
+          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[16 + jr][16 * nb + jc]));
+          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[jr][16 * nb + jc]));
+          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[16 + jr][16 * nb + jc]));
+          dto[nb] = __builtin_bit_cast(bf16x8, concat4(d0, d1));
+          qto[nb] = __builtin_bit_cast(bf16x8, concat4(q0, q1));
+        }
+        float4 lse4[2], dv4[2];
+        int4 qp4[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          lse4[t] = *reinterpret_cast<const float4*>(&T.lse2[16 * t + 4 * g]);
+          dv4[t] = *reinterpret_cast<const float4*>(&T.dvec[16 * t + 4 * g]);
+          qp4[t] = *reinterpret_cast<const int4*>(&T.qpos[16 * t + 4 * g]);
+        }
         i16x4 pb[2], dsb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+          const float lq[4] = {lse4[t].x, lse4[t].y, lse4[t].z, lse4[t].w};
+          const float dq[4] = {dv4[t].x, dv4[t].y, dv4[t].z, dv4[t].w};
+          const int pq[4] = {qp4[t].x, qp4[t].y, qp4[t].z, qp4[t].w};
           float p4[4], d4[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int qq = 16 * t + 4 * g + i;
-            const float p = kpos <= T.qpos[qq] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][i], kScoreScaleLog2, -T.lse2[qq])) : 0.0f;
+            const float p = kpos <= pq[i] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][i], kScoreScaleLog2, -lq[i])) : 0.0f;
             p4[i] = p;
-            d4[i] = p * (dp[t][i] - T.dvec[qq]);
+            d4[i] = p * (dp[t][i] - dq[i]);
           }
           pb[t] = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
           dsb[t] = pack4_bf16(d4[0], d4[1], d4[2], d4[3]);
@@ -736,12 +758,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
         const bf16x8 dk8 = __builtin_bit_cast(bf16x8, concat4(dsb[0], dsb[1]));
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[jr][16 * nb + jc]));
-          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[16 + jr][16 * nb + jc]));
-          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[jr][16 * nb + jc]));
-          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[16 + jr][16 * nb + jc]));
-          dvv[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, concat4(d0, d1)), pk, dvv[nb], 0, 0, 0);
-          dk[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, concat4(q0, q1)), dk8, dk[nb], 0, 0, 0);
+          dvv[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dto[nb], pk, dvv[nb], 0, 0, 0);
+          dk[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qto[nb], dk8, dk[nb], 0, 0, 0);
         }
       }
       if (more) store_tile(buf ^ 1);
