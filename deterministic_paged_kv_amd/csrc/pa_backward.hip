@@ -15,11 +15,13 @@
 // the gradients of the two RMSNorm weights, fp32 [128].
 //
 // Four kernels, every sum in a fixed order (no atomics):
-//  1. bwd_prep_kernel: q^ and k^ (the forward's prologue, bit for bit) into the workspace,
-//     Dv = sum_d dout * out per query (FP32: a lane's 32 terms in order, then the four lanes of
-//     the query pairwise), and the least and greatest position of every 16 tokens.
+//  1. bwd_prep_kernel: k^ (the forward's prologue, bit for bit) into the workspace, and the
+//     least and greatest position of every 16 tokens.
 //  2. bwd_dq_kernel: one workgroup per (32 queries, row, KV head, up to 4 query heads), as in
-//     the forward; per 32-key tile, staged in LDS for the 4 heads: S^T = K^ Q^T, P^T from the
+//     the forward.  It first computes its queries' q^ (the forward's prologue, bit for bit) and
+//     Dv = sum_d dout * out (FP32: a lane's 32 terms in order, then the four lanes of the query
+//     pairwise), and writes both to the workspace for kernel 3.  Then per 32-key tile, staged
+//     in LDS for the 4 heads: S^T = K^ Q^T, P^T from the
 //     forward's LSE, dP^T = V dO^T, dS^T = P^T (dP^T - Dv), dQ^T += K^T dS^T (key tiles in
 //     ascending order; tiles whose keys all follow every query are not visited).  The
 //     epilogue applies the transposed rotation and the RMSNorm backward, writes dq, and writes
@@ -112,40 +114,35 @@ __device__ __forceinline__ int safe_pos(const BwdParams& P, int b, int i, bool& 
 }
 
 // ---------------------------------------------------------------------------------------
-// 1. q^, k^ and Dv.  One wavefront per 16 tokens of one head (queries first, then keys).
+// 1. k^ and the 16-token position bounds.  One wavefront per 16 keys of one KV head.  (q^ and
+// Dv are computed by the dq kernel, whose workgroups each own their queries.)
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const BwdParams P) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int tiles = (P.seq + 15) / 16;
-  const int q_tasks = P.batch * P.num_q_heads * tiles;
   const int k_tasks = P.batch * P.num_kv_heads * tiles;
   const int waves = gridDim.x * (blockDim.x >> 6);
   const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-  for (int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < q_tasks + k_tasks; t += waves) {
-    const bool is_q = t < q_tasks;
-    const int u = is_q ? t : t - q_tasks;
-    const int H = is_q ? P.num_q_heads : P.num_kv_heads;
+  for (int u = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); u < k_tasks; u += waves) {
     const int tile = u % tiles;
-    const int bh = u / tiles;  // b * H + h
-    const int b = bh / H;
+    const int bh = u / tiles;  // b * Hkv + hk
+    const int b = bh / P.num_kv_heads;
     const int i = tile * 16 + r;
     const bool live = i < P.seq;
     bool bad = false;
     const int pos = live ? safe_pos(P, b, i, bad) : 0;
     const size_t row = ((size_t)bh * P.seq + (live ? i : 0)) * kHeadDim + 8 * g;
-    const uint16_t* src = is_q ? P.q : P.k;
-    const float* wsrc = is_q ? P.q_norm : P.k_norm;
     uint4 raw[4];
     float w[32];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      raw[kb] = live ? ldg16(src + row + 32 * kb) : make_uint4(0, 0, 0, 0);
+      raw[kb] = live ? ldg16(P.k + row + 32 * kb) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = wsrc ? wsrc[32 * kb + 8 * g + e] : 1.0f;
+      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = P.k_norm ? P.k_norm[32 * kb + 8 * g + e] : 1.0f;
     }
-    if (is_q && bh % H == 0) {
+    if (bh % P.num_kv_heads == 0) {
       // the position bounds of these 16 tokens (the same for every head), for tile skipping
       int lo = live ? pos : INT32_MAX, hi = live ? pos : -1;
 #pragma unroll
@@ -161,26 +158,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const BwdParams P
     float4 cs[8];
     load_cos_sin(P.rope, pos, g, cs);
     bf16x8 op[4];
-    prologue_operand(raw, w, wsrc != nullptr, P.eps, cs, op);
-    uint16_t* dst = (is_q ? P.qh : P.kh) + row;
+    prologue_operand(raw, w, P.k_norm != nullptr, P.eps, cs, op);
     if (live) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        *reinterpret_cast<uint4*>(dst + 32 * kb) = bad ? nan4 : __builtin_bit_cast(uint4, op[kb]);
-    }
-    if (is_q) {
-      // Dv = sum over dims of dout * out
-      float acc = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        float a[8], o[8];
-        unpack8(live ? ldg16(P.dout + row + 32 * kb) : make_uint4(0, 0, 0, 0), a);
-        unpack8(live ? ldg16(P.out + row + 32 * kb) : make_uint4(0, 0, 0, 0), o);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(a[e], o[e], acc);
-      }
-      acc = pair32_sum(pair16_sum(acc));
-      if (live && g == 0) P.dvec[(size_t)bh * P.seq + i] = acc;
+        *reinterpret_cast<uint4*>(P.kh + row + 32 * kb) = bad ? nan4 : __builtin_bit_cast(uint4, op[kb]);
     }
   }
 }
@@ -316,21 +298,49 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
   bf16x8 qop[2][4], dop[2][4];
   int qmax = -1;
   bool bad = false;
+  // q^ (the forward's prologue, same bits) and Dv = sum over dims of dout * out, for the
+  // block's queries; the workgroup owns them, so it also writes both for the dK/dV kernel
+  const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int i = qb * kQB + 16 * t + r;
     qi[t] = i;
     const bool live = i < S;
-    qpos[t] = live ? safe_pos(P, b, i, bad) : -1;
+    bool bad_t = false;
+    qpos[t] = live ? safe_pos(P, b, i, bad_t) : -1;
+    bad = bad || bad_t;
     qmax = max(qmax, qpos[t]);
     lse2[t] = live ? P.lse[qrow0 + i] * kLog2e : 0.0f;
-    dv_[t] = live ? P.dvec[qrow0 + i] : 0.0f;
+    const size_t row = (qrow0 + (live ? i : 0)) * kHeadDim + 8 * g;
+    uint4 raw[4];
+    float w[32];
+    float dsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const size_t off = (qrow0 + (live ? i : 0)) * kHeadDim + 32 * kb + 8 * g;
-      qop[t][kb] = __builtin_bit_cast(bf16x8, live ? ldg16(P.qh + off) : make_uint4(0, 0, 0, 0));
-      dop[t][kb] = __builtin_bit_cast(bf16x8, live ? ldg16(P.dout + off) : make_uint4(0, 0, 0, 0));
+      raw[kb] = live ? ldg16(P.q + row + 32 * kb) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[kb * 8 + e] = P.q_norm ? P.q_norm[32 * kb + 8 * g + e] : 1.0f;
+      const uint4 d = live ? ldg16(P.dout + row + 32 * kb) : make_uint4(0, 0, 0, 0);
+      dop[t][kb] = __builtin_bit_cast(bf16x8, d);
+      float a[8], o[8];
+      unpack8(d, a);
+      unpack8(live ? ldg16(P.out + row + 32 * kb) : make_uint4(0, 0, 0, 0), o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf(a[e], o[e], dsum);
     }
+    dsum = pair32_sum(pair16_sum(dsum));
+    dv_[t] = live ? dsum : 0.0f;
+    float4 cs[8];
+    load_cos_sin(P.rope, live ? qpos[t] : 0, g, cs);
+    bf16x8 op[4];
+    prologue_operand(raw, w, P.q_norm != nullptr, P.eps, cs, op);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 v = !live ? make_uint4(0, 0, 0, 0) : bad_t ? nan4 : __builtin_bit_cast(uint4, op[kb]);
+      qop[t][kb] = __builtin_bit_cast(bf16x8, v);
+      if (head_live && live) *reinterpret_cast<uint4*>(P.qh + row + 32 * kb) = v;
+    }
+    if (head_live && live && g == 0) P.dvec[qrow0 + i] = dsum;
   }
 #pragma unroll
   for (int sh = 1; sh < 64; sh <<= 1) qmax = max(qmax, __shfl_xor(qmax, sh));
@@ -936,7 +946,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   p.tmax = (int*)(ws + L.tmax);
   p.dwq_part = (float*)(ws + L.dwq_part);
   p.dwk_part = (float*)(ws + L.dwk_part);
-  const long long tasks = (long long)a.batch * (a.num_q_heads + a.num_kv_heads) * ((a.seq + 15) / 16);
+  const long long tasks = (long long)a.batch * a.num_kv_heads * ((a.seq + 15) / 16);
   const unsigned prep_blocks = (unsigned)std::min<long long>((tasks + 3) / 4, 8192);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(prep_blocks), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.dq_wgs), dim3(kBwdThreads), 0, stream, p);
