@@ -32,8 +32,8 @@
 //     are not visited): S = Q^ K^T, P, dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.  The
 //     epilogue writes dv, and dk through the prologue backward, and the wavefront's share of
 //     the k weight gradient.
-//  4. bwd_sum_rows_kernel: the weight-gradient shares summed by a fixed tree (64 rows per
-//     workgroup, levels until one row is left).
+//  4. bwd_sum_rows_kernel: the weight-gradient shares summed by a fixed tree (256 rows per
+//     workgroup, levels until one row is left; one launch per level for both weights).
 // MFMA operands are BF16 (q^, k^, v, dout, and P and dS rounded to BF16), accumulation FP32.
 #include "pa_internal.h"
 
@@ -834,21 +834,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
 // of in[rows][128]: four groups of 128 threads take 16 rows each in ascending order, and the
 // group sums are added in group order; levels repeat until one row is left.
 // ---------------------------------------------------------------------------------------
-constexpr int kSumRows = 64;
-__global__ __launch_bounds__(512) void bwd_sum_rows_kernel(const float* in, int rows, float* out) {
+constexpr int kSumRows = 256;  // rows per workgroup and level of the tree
+// One level of the two weight-gradient trees (q's, then k's): workgroup c < nq sums rows
+// 256 c .. 256 c + 255 of tree q, the others those of tree k.  Column d of a workgroup: four
+// groups of 64 consecutive rows, each summed in row order, then the four group sums in order.
+struct SumLevel {
+  const float* in[2];
+  float* out[2];
+  int rows[2];
+  int chunks0;
+};
+__global__ __launch_bounds__(512) void bwd_sum_rows_kernel(const SumLevel L) {
   __shared__ float part[4][kHeadDim];
+  const int tree = (int)blockIdx.x < L.chunks0 ? 0 : 1;
+  const int c = (int)blockIdx.x - (tree == 0 ? 0 : L.chunks0);
+  const float* in = L.in[tree];
+  const int rows = L.rows[tree];
   const int d = threadIdx.x & (kHeadDim - 1);
   const int grp = threadIdx.x >> 7;
-  const int r0 = blockIdx.x * kSumRows + grp * 16;
-  float v[16];
+  const int r0 = c * kSumRows + grp * (kSumRows / 4);
+  float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = r0 + i < rows ? in[(size_t)(r0 + i) * kHeadDim + d] : 0.0f;
-  float s = v[0];
+  for (int i0 = 0; i0 < kSumRows / 4; i0 += 16) {
+    float v[16];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) s += v[i];
+    for (int i = 0; i < 16; ++i) v[i] = r0 + i0 + i < rows ? in[(size_t)(r0 + i0 + i) * kHeadDim + d] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = i0 + i == 0 ? v[0] : s + v[i];
+  }
   part[grp][d] = s;
   __syncthreads();
-  if (grp == 0) out[(size_t)blockIdx.x * kHeadDim + d] = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+  if (grp == 0) L.out[tree][(size_t)c * kHeadDim + d] = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
 }
 
 // floats of the intermediate levels of the tree over `rows` rows
@@ -861,15 +877,35 @@ size_t sum_scratch_floats(long long rows) {
   return n;
 }
 
-void launch_sum_rows(const float* in, long long rows, float* scratch, float* out, hipStream_t stream) {
-  while (true) {
-    const long long chunks = (rows + kSumRows - 1) / kSumRows;
-    float* dst = chunks == 1 ? out : scratch;
-    hipLaunchKernelGGL(bwd_sum_rows_kernel, dim3((unsigned)chunks), dim3(512), 0, stream, in, (int)rows, dst);
-    if (chunks == 1) return;
-    in = dst;
-    scratch += (size_t)chunks * kHeadDim;
-    rows = chunks;
+// Both trees level by level, one launch per level (a tree with 0 rows, or already summed,
+// takes no workgroups).
+void launch_sum_rows(const float* in_q, long long rows_q, float* scratch_q, float* out_q, const float* in_k,
+                     long long rows_k, float* scratch_k, float* out_k, hipStream_t stream) {
+  const float* in[2] = {in_q, in_k};
+  long long rows[2] = {rows_q, rows_k};
+  float* scratch[2] = {scratch_q, scratch_k};
+  float* out[2] = {out_q, out_k};
+  while (rows[0] > 0 || rows[1] > 0) {
+    SumLevel L;
+    long long chunks[2];
+    for (int t = 0; t < 2; ++t) {
+      chunks[t] = (rows[t] + kSumRows - 1) / kSumRows;
+      L.in[t] = in[t];
+      L.rows[t] = (int)rows[t];
+      L.out[t] = chunks[t] == 1 ? out[t] : scratch[t];
+    }
+    L.chunks0 = (int)chunks[0];
+    hipLaunchKernelGGL(bwd_sum_rows_kernel, dim3((unsigned)(chunks[0] + chunks[1])), dim3(512), 0, stream, L);
+    for (int t = 0; t < 2; ++t) {
+      if (chunks[t] == 0) continue;
+      if (chunks[t] == 1) {
+        rows[t] = 0;  // summed
+        continue;
+      }
+      in[t] = scratch[t];
+      scratch[t] += (size_t)chunks[t] * kHeadDim;
+      rows[t] = chunks[t];
+    }
   }
 }
 
@@ -951,8 +987,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(prep_blocks), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.dq_wgs), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.dkdv_wgs), dim3(kBwdThreads), 0, stream, p);
-  if (p.dq_norm) launch_sum_rows(p.dwq_part, L.dwq_rows, (float*)(ws + L.dwq_sum), p.dq_norm, stream);
-  if (p.dk_norm) launch_sum_rows(p.dwk_part, L.dwk_rows, (float*)(ws + L.dwk_sum), p.dk_norm, stream);
+  launch_sum_rows(p.dwq_part, p.dq_norm ? L.dwq_rows : 0, (float*)(ws + L.dwq_sum), p.dq_norm, p.dwk_part,
+                  p.dk_norm ? L.dwk_rows : 0, (float*)(ws + L.dwk_sum), p.dk_norm, stream);
   return hipGetLastError();
 }
 
