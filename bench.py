@@ -82,7 +82,8 @@ def source_hash(files) -> str:
 
 
 DECODE_SOURCES = ["deterministic_paged_kv_amd/csrc/pa_decode.hip", "deterministic_paged_kv_amd/csrc/pa_internal.h"]
-PREFILL_SOURCES = ["deterministic_paged_kv_amd/csrc/pa_prefill.hip", "deterministic_paged_kv_amd/csrc/pa_internal.h"]
+PREFILL_SOURCES = ["deterministic_paged_kv_amd/csrc/pa_prefill.hip", "deterministic_paged_kv_amd/csrc/pa_internal.h",
+                   "deterministic_paged_kv_amd/csrc/pa_lds_dma.h"]
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_chunked_counters.json")
 
 

@@ -36,6 +36,7 @@
 //     workgroup, levels until one row is left; one launch per level for both weights).
 // MFMA operands are BF16 (q^, k^, v, dout, and P and dS rounded to BF16), accumulation FP32.
 #include "pa_internal.h"
+#include "pa_lds_dma.h"
 
 namespace pa {
 
@@ -43,7 +44,6 @@ namespace {
 
 constexpr int kQB = 32;                 // queries per wavefront (dq kernel) / per tile (dkdv kernel)
 constexpr int kKTile = 32;              // keys per tile (dq kernel)
-constexpr int kRowB = kHeadDim + 16;    // padded LDS row (conflict-free transposed reads)
 constexpr int kBwdThreads = 256;
 constexpr float kLog2e = 1.4426950408889634074f;
 constexpr float kSoftmaxScale = 0.08838834764831844055f;  // 1 / sqrt(128)
@@ -553,8 +553,8 @@ constexpr int kKBlock = 64;   // keys per workgroup, 16 per wavefront
 
 // one 32-query tile of one query head, shared by the workgroup's four wavefronts
 struct alignas(16) DkdvTile {
-  uint16_t q[kQB][kRowB];
-  uint16_t d[kQB][kRowB];
+  uint4 q[kQB * kHeadDim / 8];  // q^ rows, 16-byte chunks swizzled as in the dq kernel (dq_chunk)
+  uint4 d[kQB * kHeadDim / 8];  // dout rows, likewise
   float lse2[kQB];
   float dvec[kQB];
   int qpos[kQB];
@@ -640,25 +640,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
   // the greatest query position of tile qt, which the current window holds
   auto tile_qmax = [&](int qt) -> int { return __builtin_amdgcn_readlane(wmax, qt - wbase); };
 
-  // a tile's share of one thread: q^ and dout rows rt and rt + 16, and (threads < 32) one
-  // query's lse, Dv and position; loaded one tile ahead, written after the current tile is used
-  const int rt = tid >> 4;
-  const int col = tid & 15;
-  // (the loads are unconditional, on a clamped index, and nothing uses their values before
-  // store_tile: no wait for them falls inside the current tile's work)
-  uint4 qr[2], dr[2];
+  // A tile goes to LDS one tile ahead: its q^ and dout rows by direct-to-LDS loads, wavefront w
+  // rows 8 w .. 8 w + 7 of each (two loads of four rows: lane l, row 4 i + l / 16, physical
+  // chunk l % 16, which holds logical chunk (l % 16) ^ swizzle(row)); and (threads < 32) one
+  // query's lse, Dv and position through registers, written after the current tile is used.
+  // (Nothing reads a loaded value before store_tile, so no wait falls inside the current
+  // tile's work; the direct loads are waited for before the barrier that publishes the tile.)
+  uint32_t dma_off[2];
+  int dma_row[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    dma_row[u] = 8 * wave + 4 * u + (lane >> 4);
+    dma_off[u] = 16u * (uint32_t)((lane & 15) ^ dq_swz(dma_row[u]));
+  }
   float lse_n = 0.0f, dv_n = 0.0f;
   int qp_n = -1;
   bool qlive_n = false;
-  auto load_tile = [&](int gi, int qt) {
+  auto load_tile = [&](int gi, int qt, int buf) {
     const size_t qrow0 = ((size_t)b * P.num_q_heads + hk * G + gi) * S;
+    const uint16_t* qb = P.qh + qrow0 * kHeadDim;
+    const uint16_t* db = P.dout + qrow0 * kHeadDim;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       // a query past the row reads query 0: its position (-1) makes its P and dS zero
-      const int i = qt * kQB + 16 * u + rt;
-      const size_t off = (qrow0 + (i < S ? i : 0)) * kHeadDim + col * 8;
-      qr[u] = ldg16(P.qh + off);
-      dr[u] = ldg16(P.dout + off);
+      const int i = qt * kQB + dma_row[u];
+      const uint32_t voff = (uint32_t)(i < S ? i : 0) * (kHeadDim * 2) + dma_off[u];
+      const int slot = 2 * wave + u;  // 1 KB slot of the tile: rows 4 slot .. 4 slot + 3
+      lds_dma16(lds_address(&sm[buf].q[64 * slot]), qb, voff);
+      lds_dma16(lds_address(&sm[buf].d[64 * slot]), db, voff);
     }
     if (tid < kQB) {
       const int i = qt * kQB + tid;
@@ -670,11 +679,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
     }
   };
   auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      *reinterpret_cast<uint4*>(&sm[buf].q[16 * u + rt][col * 8]) = qr[u];
-      *reinterpret_cast<uint4*>(&sm[buf].d[16 * u + rt][col * 8]) = dr[u];
-    }
     if (tid < kQB) {
       // a position outside the RoPE table reads as 0 (the query's own rows are poisoned)
       sm[buf].lse2[tid] = qlive_n ? lse_n * kLog2e : 0.0f;
@@ -689,8 +693,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
   if (first < nqt) {
     int gi = 0, qt = first, buf = 0;
     int qmax = __builtin_amdgcn_readfirstlane(tile_qmax(first));
-    load_tile(gi, qt);
+    load_tile(gi, qt, 0);
     store_tile(0);
+    wait_vmcnt<0>();
     __syncthreads();
     while (true) {
       int ngi = gi;
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
       }
       const bool more = ngi < G;
       const int qmax_next = __builtin_amdgcn_readfirstlane(tile_qmax(nq < nqt ? nq : wbase));
-      if (more) load_tile(ngi, nq);
+      if (more) load_tile(ngi, nq, buf ^ 1);
       const DkdvTile& T = sm[buf];
       if (qmax >= kmin) {
         // S = Q^ K^T and dP = dO V^T: [t] queries 16 t + 4 g + i, key r.  The 16 operand
@@ -711,8 +716,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            qa[t][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.q[16 * t + r][32 * kb + 8 * g]));
-            da[t][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&T.d[16 * t + r][32 * kb + 8 * g]));
+            qa[t][kb] = __builtin_bit_cast(bf16x8, T.q[dq_chunk(16 * t + r, 4 * kb + g)]);
+            da[t][kb] = __builtin_bit_cast(bf16x8, T.d[dq_chunk(16 * t + r, 4 * kb + g)]);
           }
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
         f32x4 sc[2], dp[2];
@@ -731,10 +736,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
         bf16x8 dto[8], qto[8];
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[jr][16 * nb + jc]));
-          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.d[16 + jr][16 * nb + jc]));
-          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[jr][16 * nb + jc]));
-          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T.q[16 + jr][16 * nb + jc]));
+          // dims 16 nb + jc .. +3: chunk 2 nb + jc / 8, its half jc % 8 / 4
+          const int ch = 2 * nb + (jc >> 3);
+          const int hb = 2 * (jc & 7);
+          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(reinterpret_cast<const char*>(&T.d[dq_chunk(jr, ch)]) + hb));
+          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(reinterpret_cast<const char*>(&T.d[dq_chunk(16 + jr, ch)]) + hb));
+          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(reinterpret_cast<const char*>(&T.q[dq_chunk(jr, ch)]) + hb));
+          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(reinterpret_cast<const char*>(&T.q[dq_chunk(16 + jr, ch)]) + hb));
           dto[nb] = __builtin_bit_cast(bf16x8, concat4(d0, d1));
           qto[nb] = __builtin_bit_cast(bf16x8, concat4(q0, q1));
         }
@@ -773,6 +785,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
         }
       }
       if (more) store_tile(buf ^ 1);
+      wait_vmcnt<0>();
       __syncthreads();
       if (!more) break;
       gi = ngi;
