@@ -356,22 +356,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
     for (int nb = 0; nb < 8; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int jr = 4 * g + (r >> 2);
   const int jc = 4 * (r & 3);
-  const int rt = tid >> 4;     // staging: key rows rt and rt + 16 of a tile
-  const int col = tid & 15;
 
-  // a tile's share of one thread: k^ and V rows rt and rt + 16, and (threads < 32) one key's
-  // position; loaded one tile ahead, written to LDS after the current tile is used
-  uint4 kr[2], vr[2];
+  // A tile goes to LDS one tile ahead: its k^ and V rows by direct-to-LDS loads, wavefront w
+  // rows 8 w .. 8 w + 7 of each (two loads of four rows: lane l, row 4 i + l / 16, physical
+  // chunk l % 16, which holds logical chunk (l % 16) ^ swizzle(row)); and (threads < 32) one
+  // key's position through a register, written after the current tile is used.  The direct
+  // loads are waited for before the barrier that publishes the tile.
+  uint32_t dma_off[2];
+  int dma_row[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    dma_row[u] = 8 * wave + 4 * u + (lane >> 4);
+    dma_off[u] = 16u * (uint32_t)((lane & 15) ^ dq_swz(dma_row[u]));
+  }
+  const uint16_t* kbase = P.kh + krow0 * kHeadDim;
+  const uint16_t* vbase = P.v + krow0 * kHeadDim;
   int kp_next = INT32_MAX;
   bool klive_next = false;
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt, int buf) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       // a key past the row reads key 0: its position (INT32_MAX) makes its P and dS zero
-      const int j = kt * kKTile + 16 * u + rt;
-      const size_t off = (krow0 + (j < S ? j : 0)) * kHeadDim + col * 8;
-      kr[u] = ldg16(P.kh + off);
-      vr[u] = ldg16(P.v + off);
+      const int j = kt * kKTile + dma_row[u];
+      const uint32_t voff = (uint32_t)(j < S ? j : 0) * (kHeadDim * 2) + dma_off[u];
+      const int slot = 2 * wave + u;  // 1 KB slot of the tile: rows 4 slot .. 4 slot + 3
+      lds_dma16(lds_address(&sm.k[buf][64 * slot]), kbase, voff);
+      lds_dma16(lds_address(&sm.v[buf][64 * slot]), vbase, voff);
     }
     if (tid < kKTile) {
       // the raw position, checked in store_tile (so that no wait for it falls inside the
@@ -382,11 +392,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
     }
   };
   auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      sm.k[buf][dq_chunk(16 * u + rt, col)] = kr[u];
-      sm.v[buf][dq_chunk(16 * u + rt, col)] = vr[u];
-    }
     // keys past the row get a position no query can see; a position outside the RoPE table
     // reads as 0 (the key's own rows are poisoned)
     if (tid < kKTile) sm.kpos[buf][tid] = !klive_next ? INT32_MAX : (kp_next < 0 || kp_next >= P.table_rows ? 0 : kp_next);
@@ -418,14 +423,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
   };
   const int first = __builtin_amdgcn_readfirstlane(next_tile(0));
   if (first < ntiles) {
-    load_tile(first);
+    load_tile(first, 0);
     store_tile(0);
+    wait_vmcnt<0>();
     __syncthreads();
     int buf = 0;
     for (int kt = first;;) {
       const int nk = __builtin_amdgcn_readfirstlane(next_tile(kt + 1));
       const bool more = nk < ntiles;
-      if (more) load_tile(nk);
+      if (more) load_tile(nk, buf ^ 1);
       if (head_live) {
         f32x4 s[2][2], dp[2][2];  // [ks][t]: keys 16 ks + 4 g + i, query 16 t + r
 #pragma unroll
@@ -479,6 +485,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
         }
       }
       if (more) store_tile(buf ^ 1);
+      wait_vmcnt<0>();
       __syncthreads();
       if (!more) break;
       kt = nk;
