@@ -850,8 +850,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdParams P
 }
 
 // ---------------------------------------------------------------------------------------
-// 4. weight gradients: a fixed tree over the shares.  Each workgroup sums 64 consecutive rows
-// of in[rows][128]: four groups of 128 threads take 16 rows each in ascending order, and the
+// 4. weight gradients: a fixed tree over the shares.  Each workgroup sums 256 consecutive rows
+// of in[rows][128]: four groups of 128 threads take 64 rows each in ascending order, and the
 // group sums are added in group order; levels repeat until one row is left.
 // ---------------------------------------------------------------------------------------
 constexpr int kSumRows = 256;  // rows per workgroup and level of the tree
