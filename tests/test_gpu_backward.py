@@ -142,3 +142,27 @@ def test_backward_positions_not_in_token_order(gpu):
     torch.cuda.synchronize()
     for name, got, r in zip(("dq", "dk", "dv", "dw_q", "dw_k"), g, ref[2:]):
         _check(name, got.cpu().numpy(), r)
+
+
+def test_backward_out_of_range_position_poisons_its_token(gpu):
+    """A token whose position lies outside the RoPE table gets NaN dq and dk rows (its q^ and k^
+    are NaN, so whatever they reach in its own row is NaN too); the other row keeps the bits of
+    a clean run, since rows never mix."""
+    B, Hq, Hkv, S = 2, 8, 2, 40
+    q, k, v, do, wq, wk, pos = _case(31, B, Hq, Hkv, S)
+    plan = pa.Plan(Hq, Hkv, max_batch=B, max_q_len=S, max_pages_per_row=3)  # RoPE table: 49 rows
+    out, lse = _forward(plan, q, k, v, wq, wk, pos)
+    f = lambda a: torch.from_numpy(a).cuda()
+    res = []
+    bad = pos.copy()
+    bad[0, 5] = 10_000
+    for p in (pos, bad):
+        g = pa.prefill_backward(plan, i32(p), bf16_tensor(q), bf16_tensor(k), bf16_tensor(v), out, lse,
+                                bf16_tensor(do), q_norm_weight=f(wq), k_norm_weight=f(wk))
+        torch.cuda.synchronize()
+        res.append([t.cpu().numpy() for t in g[:3]])
+    (dq0, dk0, dv0), (dq1, dk1, dv1) = res
+    assert np.all(np.isfinite(dq0)) and np.all(np.isfinite(dk0)) and np.all(np.isfinite(dv0))
+    assert np.all(np.isnan(dq1[0, :, 5])) and np.all(np.isnan(dk1[0, :, 5]))
+    for clean, poisoned in ((dq0, dq1), (dk0, dk1), (dv0, dv1)):
+        assert np.array_equal(clean[1].view(np.uint32), poisoned[1].view(np.uint32))
