@@ -142,8 +142,8 @@ struct alignas(16) AttendSmem {
   union {
     TileBuf tiles[kStreams][kBufs];            // the walk (128 KB)
     struct {
-      float merge[4][2 + 64][64];              // stream 1's states, read by stream 0 at the end
-      uint16_t out[4][32][kOutPitch];          // stream 0's output rows, staged for row-wise stores
+      float merge[4][2][2 + 32][64];           // per pair and stream: what it hands the other
+      uint16_t out[4][32][kOutPitch];          // the pair's output rows, staged for row-wise stores
     } m;
   } u;
   int32_t pt[kPageTable];                      // 8 KB
@@ -775,53 +775,67 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   else if (use_pt) walk(phase1, table);
   else walk(phase1, no_table);
 
-  // ---- merge the two streams of each query row (stream 0, then stream 1) and write out
+  // ---- merge the two streams of each query row (stream 0, then stream 1) and write out.  The
+  // two wavefronts of a pair (the same rows, streams 0 and 1) each write half of every row:
+  // stream 0 dims 0..63 (accumulator blocks 0, 1), stream 1 dims 64..127 (blocks 2, 3).  Each
+  // hands the other its reference, partial sum and the two blocks the other writes, through
+  // LDS.  Both evaluate the merge with stream 0's terms in stream 0's roles, and the sums add
+  // two terms, which gives the same bits in either order.
   const bool out_poison = __syncthreads_or(poison) != 0;  // also: every wavefront is done with the tiles
   const int pair = w >> 1;  // wavefronts 2 pair and 2 pair + 1 hold the same rows, streams 0 and 1
-  if (st == 1) {
-    sm.u.m.merge[pair][0][lane] = m_run;
-    sm.u.m.merge[pair][1][lane] = l_part;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.u.m.merge[pair][2 + 16 * db + i][lane] = acc[db][i];
-  }
-  __syncthreads();
-  if (st == 1) return;
-  {
+  auto merge_out = [&](auto stc) {
 #pragma clang fp contract(off)
-    const float m1 = sm.u.m.merge[pair][0][lane];
-    const float l1 = sm.u.m.merge[pair][1][lane];
-    const float mx = fmaxf(m_run, m1);
-    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx);
+    constexpr int ST = decltype(stc)::value;
+    constexpr int kOwn = 2 * ST;       // first accumulator block this wavefront writes out
+    constexpr int kGive = 2 - 2 * ST;  // first block the other wavefront writes out
+    {
+      float(&snd)[2 + 32][64] = sm.u.m.merge[pair][ST];
+      snd[0][lane] = m_run;
+      snd[1][lane] = l_part;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) snd[2 + 16 * k + i][lane] = acc[kGive + k][i];
+    }
+    __syncthreads();
+    const float(&rcv)[2 + 32][64] = sm.u.m.merge[pair][1 - ST];
+    const float m_other = rcv[0][lane];
+    const float l_other = rcv[1][lane];
+    const float m0 = ST == 0 ? m_run : m_other;
+    const float m1 = ST == 0 ? m_other : m_run;
+    const float mx = fmaxf(m0, m1);
+    const float a0 = m0 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m0 - mx);
     const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
-    const float l = pair32_sum(l_part * a0 + l1 * a1);
+    const float a_own = ST == 0 ? a0 : a1;
+    const float a_other = ST == 0 ? a1 : a0;
+    const float l = pair32_sum(l_part * a_own + l_other * a_other);
     const int gi = hg * 4 + 2 * hp + (n >> 4);  // head within the GQA group
     const bool live = gi < G && qi < Sq;
     const bool empty = l == 0.0f;
     const float inv = empty ? 0.0f : 1.0f / l;
     const size_t row = ((size_t)b * P.num_q_heads + hk * G + (gi < G ? gi : 0)) * Sq + (qi < Sq ? qi : 0);
-    // the wavefront's rows go through LDS (lane (n, hh) holds dims 32 db + 8 q4 + 4 hh .. +3
-    // of row n) and out as whole rows: 16 bytes per lane, four rows per store
+    // the pair's rows go through LDS (lane (n, hh) holds dims 32 db + 8 q4 + 4 hh .. +3 of row
+    // n) and out as half rows: 16 bytes per lane, eight rows per store
     uint16_t(&stage)[32][kOutPitch] = sm.u.m.out[pair];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int k = 0; k < 2; ++k) {
+      const int db = kOwn + k;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q4 + e;
-          const float v = acc[db][i] * a0 + sm.u.m.merge[pair][2 + 16 * db + i][lane] * a1;
+          const float v = acc[db][i] * a_own + rcv[2 + 16 * k + i][lane] * a_other;
           o[e] = out_poison ? __builtin_nanf("") : v * inv;
         }
         *reinterpret_cast<i16x4*>(&stage[n][32 * db + 8 * q4 + 4 * hh]) = pack_bf16(o[0], o[1], o[2], o[3]);
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = 4 * k + (lane >> 4);  // row (column n of the MFMAs)
-      const int ch = lane & 15;           // 16-byte chunk of the row
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + (lane >> 3);     // row (column n of the MFMAs)
+      const int ch = 8 * ST + (lane & 7);    // 16-byte chunk of the row
       const int gr = hg * 4 + 2 * hp + (r >> 4);
       const int qr = qb * kQB + 16 * qg + (r & 15);
       const uint2 lo = *reinterpret_cast<const uint2*>(&stage[r][8 * ch]);
@@ -831,12 +845,14 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
         stg16(P.out + orow * kHeadDim + 8 * ch, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
     }
-    if (live && hh == 0) {
+    if (ST == 0 && live && hh == 0) {
       float lse = empty ? -__builtin_inff() : (mx + __builtin_log2f(l)) * kLn2;
       if (out_poison) lse = __builtin_nanf("");
       P.lse[row] = lse;
     }
-  }
+  };
+  if (st == 0) merge_out(std::integral_constant<int, 0>{});
+  else merge_out(std::integral_constant<int, 1>{});
 }
 
 }  // namespace
