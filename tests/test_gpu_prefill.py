@@ -47,6 +47,16 @@ def test_prefill_group_sizes(gpu, hq, hkv):
     assert_parity(out, lse, ref_out, ref_lse, f"prefill Hq={hq} Hkv={hkv}", kind="prefill")
 
 
+def test_prefill_row_past_the_page_table(gpu):
+    """A row of more than 2,048 pages (the attention kernel's LDS page table) looks its pages up
+    with scalar loads instead; a short row beside it keeps the table."""
+    b = workloads.make_batch(35, [40_000, 300], q_len=32, num_q_heads=8, num_kv_heads=2, num_pages=2600,
+                             query_mode="prefill")
+    out, lse = run("prefill", make_plan(b), DeviceBatch(b))
+    ref_out, ref_lse = oracle_ref(b)
+    assert_parity(out, lse, ref_out, ref_lse, "prefill 40,000-key row", kind="prefill")
+
+
 def test_prefill_decode_style_positions_and_no_norm(gpu):
     """Queries ending at L (keys of the chunk not all cached), and no RMSNorm."""
     b = workloads.make_batch(33, [50, 90], q_len=8, num_q_heads=8, num_kv_heads=2, num_pages=32,
