@@ -257,7 +257,8 @@ __device__ __forceinline__ void sum16(float v[8][4]) {
 // spreads over 8 distinct pairs).  (A padded 288-byte pitch was conflict-free for the second
 // pattern only; the first then took two LDS cycles per read.)
 // The tiles are arrays of 16-byte chunks, so that the compiler emits whole 16-byte LDS
-// accesses (it splits them into 4-byte pairs where it cannot prove the alignment).
+// accesses (it splits them into 4-byte pairs where it cannot prove the alignment).  The dK/dV
+// kernel's q^ and dout tiles have the same layout and the same two read patterns.
 __device__ __forceinline__ int dq_swz(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
 // chunk index of the 16-byte chunk c (dims 8 c .. 8 c + 7) of row j in a swizzled tile
 __device__ __forceinline__ int dq_chunk(int row, int c) { return row * (kHeadDim / 8) + (c ^ dq_swz(row)); }
