@@ -166,3 +166,27 @@ def test_backward_out_of_range_position_poisons_its_token(gpu):
     assert np.all(np.isnan(dq1[0, :, 5])) and np.all(np.isnan(dk1[0, :, 5]))
     for clean, poisoned in ((dq0, dq1), (dk0, dk1), (dv0, dv1)):
         assert np.array_equal(clean[1].view(np.uint32), poisoned[1].view(np.uint32))
+
+
+def test_backward_full_size_sampled_group(gpu):
+    """The bench's backward launch (B = 4 rows of 2,048 tokens at positions 0..2047, Hq 32 / Hkv 8,
+    both norms): every gradient finite, and one row's KV group (4 query heads, 1 KV head) against
+    the oracle run on that group alone (a group's dq, dk and dv depend on nothing else)."""
+    B, Hq, Hkv, S = 4, 32, 8, 2048
+    q, k, v, do, wq, wk, pos = _case(4242, B, Hq, Hkv, S)
+    plan = pa.Plan(Hq, Hkv, max_batch=B, max_q_len=S, max_pages_per_row=S // 16)
+    out, lse = _forward(plan, q, k, v, wq, wk, pos)
+    f = lambda a: torch.from_numpy(a).cuda()
+    g = pa.prefill_backward(plan, i32(pos), bf16_tensor(q), bf16_tensor(k), bf16_tensor(v), out, lse,
+                            bf16_tensor(do), q_norm_weight=f(wq), k_norm_weight=f(wk))
+    torch.cuda.synchronize()
+    dq, dk, dv, dwq, dwk = [t.cpu().numpy() for t in g]
+    for t in (dq, dk, dv, dwq, dwk):
+        assert np.all(np.isfinite(t))
+    b, hk = 2, 5
+    hq = slice(4 * hk, 4 * hk + 4)
+    ref = oracle.prefill_forward_backward(q[b:b + 1, hq], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], wq, wk,
+                                          pos[b:b + 1], do[b:b + 1, hq])
+    _check("dq", dq[b:b + 1, hq], ref[2])
+    _check("dk", dk[b:b + 1, hk:hk + 1], ref[3])
+    _check("dv", dv[b:b + 1, hk:hk + 1], ref[4])
