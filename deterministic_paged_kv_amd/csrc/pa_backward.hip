@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
   float lse2[2], dv_[2];
   bf16x8 qop[2][4], dop[2][4];
   int qmax = -1;
-  bool bad = false;
+  bool bad[2] = {false, false};  // the query's position is outside the RoPE table
   // q^ (the forward's prologue, same bits) and Dv = sum over dims of dout * out, for the
   // block's queries; the workgroup owns them, so it also writes both for the dK/dV kernel
   const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
@@ -307,9 +307,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
     const int i = qb * kQB + 16 * t + r;
     qi[t] = i;
     const bool live = i < S;
-    bool bad_t = false;
-    qpos[t] = live ? safe_pos(P, b, i, bad_t) : -1;
-    bad = bad || bad_t;
+    qpos[t] = live ? safe_pos(P, b, i, bad[t]) : -1;
     qmax = max(qmax, qpos[t]);
     lse2[t] = live ? P.lse[qrow0 + i] * kLog2e : 0.0f;
     const size_t row = (qrow0 + (live ? i : 0)) * kHeadDim + 8 * g;
@@ -337,7 +335,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
     prologue_operand(raw, w, P.q_norm != nullptr, P.eps, cs, op);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const uint4 v = !live ? make_uint4(0, 0, 0, 0) : bad_t ? nan4 : __builtin_bit_cast(uint4, op[kb]);
+      const uint4 v = !live ? make_uint4(0, 0, 0, 0) : bad[t] ? nan4 : __builtin_bit_cast(uint4, op[kb]);
       qop[t][kb] = __builtin_bit_cast(bf16x8, v);
       if (head_live && live) *reinterpret_cast<uint4*>(P.qh + row + 32 * kb) = v;
     }
@@ -534,7 +532,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdParams P) 
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         float4 o = make_float4(dx[nb][0], dx[nb][1], dx[nb][2], dx[nb][3]);
-        if (bad) o = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+        if (bad[t]) o = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
         *reinterpret_cast<float4*>(dst + 16 * nb + 4 * g) = o;
       }
 #pragma unroll
