@@ -58,14 +58,6 @@ __device__ __forceinline__ i16x4 pack_bf16(float a, float b, float c, float d) {
   return __builtin_bit_cast(i16x4, make_uint2(lo, hi));
 }
 
-// max of three floats in one v_max3_f32.  The operands are MFMA results or -inf, never
-// signalling NaNs, so the operand quieting that fmaxf would add is not needed.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // True iff kv_indptr[0..b+1] is non-decreasing.  Rows whose extents lie in such a prefix
 // never share an index slot (and so never share k^ workspace rows); a row past a decrease
 // could overlap another row's extent and is treated as bad by both kernels.  Every thread of
