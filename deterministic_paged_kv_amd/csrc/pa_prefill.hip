@@ -671,7 +671,9 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     }
     // the fix-up below runs when the probabilities against the current reference sum past
     // 2^kLazyMax (or overflow, or are NaN), or when the reference is unset and a key is visible
-    const bool need = m_run == -__builtin_inff() ? lp != 0.0f : !(lp <= 256.0f);
+    // (lp is a sum of non-negative terms, so lp != 0 is !(lp <= 0): one compare either way)
+    const float lp_max = m_run == -__builtin_inff() ? 0.0f : 256.0f;
+    const bool need = !(lp <= lp_max);
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
       float mx = s_cur[0];
 #pragma unroll
