@@ -330,11 +330,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //          32-key tiles; rows past a row's keys are masked, and the padding keeps the last
 //          row's tile in bounds);
 //   q^     [B][Hq][Sq][128] bf16;
-//   order  one int32 per work unit (row, block of kPrefillQB queries): the units, longest
-//          first;
-//   units  one record of kUnitInts int32 per work unit: what the attention kernel needs of
-//          the unit's row and queries (extent, length, tiles, poison, the row's first page
-//          numbers), see pa_prefill.hip.
+//   units  one record of kUnitInts int32 per work unit (row, block of kPrefillQB queries),
+//          stored in the order the attention kernel takes the units (longest first): the
+//          unit's number and what the kernel needs of its row and queries (extent, length,
+//          tiles, poison, the row's first page numbers), see pa_prefill.hip.
 constexpr int kPrefillQB = 32;  // queries per work unit of the attention kernel
 constexpr int kUnitInts = 32;
 inline size_t prefill_kh_bytes(int hkv, int num_indices) {
@@ -343,15 +342,11 @@ inline size_t prefill_kh_bytes(int hkv, int num_indices) {
 inline size_t prefill_qh_bytes(int hq, int batch, int q_len) {
   return align256((size_t)batch * hq * q_len * kHeadDim * 2);
 }
-inline size_t prefill_order_bytes(int batch, int q_len) {
-  return align256((size_t)batch * ((q_len + kPrefillQB - 1) / kPrefillQB) * 4);
-}
 inline size_t prefill_unit_bytes(int batch, int q_len) {
   return align256((size_t)batch * ((q_len + kPrefillQB - 1) / kPrefillQB) * kUnitInts * 4);
 }
 inline size_t prefill_workspace_bytes(int hq, int hkv, int batch, int q_len, int num_indices) {
-  return prefill_kh_bytes(hkv, num_indices) + prefill_qh_bytes(hq, batch, q_len) + prefill_order_bytes(batch, q_len) +
-         prefill_unit_bytes(batch, q_len);
+  return prefill_kh_bytes(hkv, num_indices) + prefill_qh_bytes(hq, batch, q_len) + prefill_unit_bytes(batch, q_len);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

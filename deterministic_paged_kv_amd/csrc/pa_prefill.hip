@@ -10,8 +10,8 @@
 //  1. prologue_kernel: every cached key of every KV head of every valid row, and every query
 //     vector, goes once through the shared Q/K prologue (RMSNorm, RoPE, BF16); k^ is written
 //     to the workspace in logical order, key j of row b at index slot kv_indptr[b] + j / 16
-//     (slots past a row's length are zeros), q^ as [B][Hq][Sq][128]; one workgroup writes the
-//     order of the attention kernel's work units, longest first.
+//     (slots past a row's length are zeros), q^ as [B][Hq][Sq][128]; the work units' records
+//     are written in the attention kernel's order, longest first.
 //  2. attend_kernel: one workgroup per (block of 32 queries, row, KV head, group of up to 4
 //     query heads); each wavefront holds 16 queries of two query heads of the KV head's GQA
 //     group.  Key tiles of 32 (2 pages) are split
@@ -141,11 +141,10 @@ struct alignas(16) AttendSmem {
   int32_t pt[kPageTable];                      // 8 KB
 };
 
-// Work placement: tiles per unit, and the unit picked.
+// Work placement: the tiles every unit visits, for ranking the units.
 constexpr int kMaxRankUnits = 512;
 struct RankSmem {
   int tiles[kMaxRankUnits];
-  int sel;
 };
 
 // Units (row b, query block qb) are numbered u = (nqb - 1 - qb) * batch + b.  The key tiles a
@@ -167,24 +166,8 @@ __device__ int unit_tiles(const PrefillParams& P, int nqb, int u) {
   return kend > 0 ? (kend + kKT - 1) / kKT : 0;
 }
 
-// The order of the units: more tiles first, then lower unit number (U <= kMaxRankUnits).
-// All threads of the workgroup call it.
-__device__ void unit_order(const PrefillParams& P, int nqb, int U, int32_t* __restrict__ order, RankSmem& rs) {
-  for (int u = threadIdx.x; u < U; u += blockDim.x) rs.tiles[u] = unit_tiles(P, nqb, u);
-  __syncthreads();
-  for (int u = threadIdx.x; u < U; u += blockDim.x) {
-    const int c = rs.tiles[u];
-    int rank = 0;
-    for (int v = 0; v < U; ++v) {
-      const int cv = rs.tiles[v];
-      rank += (cv > c || (cv == c && v < u)) ? 1 : 0;
-    }
-    order[rank] = u;
-  }
-}
-
 // ---------------------------------------------------------------------------------------
-// 1. the prologue: k^ of every cached key, q^ of every query, the order of the work units
+// 1. the prologue: k^ of every cached key, q^ of every query, the work units' records
 // ---------------------------------------------------------------------------------------
 // One launch of 256-thread workgroups of three kinds:
 //   [0, B * kx)        k^: row b = id / kx; its tasks are spread over its kx workgroups, 4
@@ -195,7 +178,8 @@ __device__ void unit_order(const PrefillParams& P, int nqb, int U, int32_t* __re
 //                      valid rows are written; nothing reads the other slots.
 //   [B * kx, + nq)     q^: 16 query vectors per wavefront, (b, head, i) in [B][Hq][Sq] order,
 //                      written in that order, [B][Hq][Sq][128] bf16.
-//   the last one       the order of the work units, longest first.
+//   the rest           the work units' records, 8 units per workgroup, each stored at its rank
+//                      (the attention kernel's order, longest first).
 //
 // k^ layout: per KV head, key j of row b at row (kv_indptr[b] * 16 + j) of [nnz * 16][128]
 // bf16 (the key's 128 dims contiguous), so a 32-key tile is 8 KB of contiguous workspace.
@@ -321,19 +305,41 @@ __device__ void query_part(const PrefillParams& P, uint16_t* __restrict__ qh, in
 //               query of the block has a position out of the RoPE table or a cache_position
 //               that differs from it: every output of the unit is then NaN
 // A bad row's or query's position counts as -1 (sees nothing) in ntiles and free_end.
-enum { kUnitP0 = 0, kUnitNidx, kUnitLpl, kUnitL, kUnitTiles, kUnitFreeEnd, kUnitPoison, kUnitPage0 = 8 };
+//   7 unit      the unit's number u (records are stored by rank, see below)
+enum { kUnitP0 = 0, kUnitNidx, kUnitLpl, kUnitL, kUnitTiles, kUnitFreeEnd, kUnitPoison, kUnitId, kUnitPage0 = 8 };
 // the record also holds the physical numbers of the row's pages 0 .. kUnitPages - 1 (clamped to
 // the last page; 0 for an empty or bad row): the V loads issued before the walk take them from
 // there instead of from the page table, one memory latency earlier
 constexpr int kUnitPages = 12;
 static_assert(kUnitPage0 + kUnitPages <= kUnitInts, "unit record size");
-__device__ void unit_part(const PrefillParams& P, int32_t* __restrict__ units, int ublk) {
+// The records are stored in the attention kernel's order: by rank, more tiles first, then
+// lower unit number (units past kMaxRankUnits go in number order).  Every workgroup of this
+// kind ranks its own units against all of them, so no other workgroup has to finish first.
+// All threads of the workgroup call it.
+__device__ void unit_part(const PrefillParams& P, int32_t* __restrict__ units, int ublk, RankSmem& rs) {
   const int lane = threadIdx.x & 63;
   const int i32 = lane & 31;
   const int nqb = (P.q_len + kQB - 1) / kQB;
   const int U = P.batch * nqb;
   const int u = (ublk * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 2 + (lane >> 5);
   const bool live_unit = u < U;
+  const bool ranked = U <= kMaxRankUnits;
+  if (ranked) {
+    for (int v = threadIdx.x; v < U; v += blockDim.x) rs.tiles[v] = unit_tiles(P, nqb, v);
+  }
+  __syncthreads();
+  int slot = u;
+  if (ranked) {
+    const int c = rs.tiles[live_unit ? u : 0];
+    int before = 0;
+    for (int v = i32; v < U; v += 32) {
+      const int cv = rs.tiles[v];
+      before += (cv > c || (cv == c && v < u)) ? 1 : 0;
+    }
+#pragma unroll
+    for (int sh = 1; sh < 32; sh <<= 1) before += __shfl_xor(before, sh);
+    slot = before;
+  }
   const int uu = live_unit ? u : 0;
   const int b = uu % P.batch;
   const int qb = nqb - 1 - uu / P.batch;
@@ -362,26 +368,24 @@ __device__ void unit_part(const PrefillParams& P, int32_t* __restrict__ units, i
   }
   const bool any_qbad = (uint32_t)(__builtin_amdgcn_ballot_w64(qbad) >> (lane & 32)) != 0u;
   const int kend = min(L, qmax + 1);
-  const int rec[7] = {p0, nidx, lpl, L, kend > 0 ? (kend + kKT - 1) / kKT : 0,
-                      min(L, qmin == INT32_MAX ? 0 : qmin + 1), (bad || any_qbad) ? 1 : 0};
-  if (live_unit && i32 < 7) {
+  const int rec[8] = {p0, nidx, lpl, L, kend > 0 ? (kend + kKT - 1) / kKT : 0,
+                      min(L, qmin == INT32_MAX ? 0 : qmin + 1), (bad || any_qbad) ? 1 : 0, u};
+  if (live_unit && i32 < 8) {
     int v = rec[0];
 #pragma unroll
-    for (int f = 1; f < 7; ++f) v = i32 == f ? rec[f] : v;
-    units[(size_t)u * kUnitInts + i32] = v;
+    for (int f = 1; f < 8; ++f) v = i32 == f ? rec[f] : v;
+    units[(size_t)slot * kUnitInts + i32] = v;
   }
   if (live_unit && i32 >= kUnitPage0 && i32 < kUnitPage0 + kUnitPages) {
     const int k = i32 - kUnitPage0;
-    units[(size_t)u * kUnitInts + i32] = (!bad && nidx > 0) ? P.indices[p0 + min(k, nidx - 1)] : 0;
+    units[(size_t)slot * kUnitInts + i32] = (!bad && nidx > 0) ? P.indices[p0 + min(k, nidx - 1)] : 0;
   }
 }
 
 template <int HG>
 __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const PrefillParams P, uint16_t* __restrict__ kh,
                                                                     uint16_t* __restrict__ qh,
-                                                                    int32_t* __restrict__ order,
-                                                                    int32_t* __restrict__ units, int kx, int nq,
-                                                                    int nu) {
+                                                                    int32_t* __restrict__ units, int kx, int nq) {
   __shared__ PrologueSmem sm;
   const int blk = (int)blockIdx.x;
   const int nk = P.batch * kx;
@@ -389,12 +393,8 @@ __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const Prefil
     key_part<HG>(P, kh, blk / kx, blk % kx, kx);
   } else if (blk < nk + nq) {
     query_part(P, qh, blk - nk);
-  } else if (blk < nk + nq + nu) {
-    unit_part(P, units, blk - nk - nq);
   } else {
-    const int nqb = (P.q_len + kQB - 1) / kQB;
-    const int U = P.batch * nqb;
-    if (U <= kMaxRankUnits) unit_order(P, nqb, U, order, sm.rank);
+    unit_part(P, units, blk - nk - nq, sm.rank);
   }
 }
 
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(const Prefil
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_kernel(
     const PrefillParams P, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ qh,
-    const int32_t* __restrict__ order, const int32_t* __restrict__ units) {
+    const int32_t* __restrict__ units) {
   __shared__ AttendSmem sm;
   const int G = P.group;
   const int Hkv = P.num_kv_heads;
@@ -417,10 +417,11 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   // ranks go longest first.  The order only places work; every item's arithmetic is the same
   // wherever it runs.
   const int HH = Hkv * nhg;
-  const int U = P.batch * nqb;
   const int rank = (int)blockIdx.x / HH;
   const int head = (int)blockIdx.x % HH;
-  const int unit = U <= kMaxRankUnits ? load_uniform(order, rank) : rank;
+  // the unit's record, stored at its rank by the prologue kernel
+  const int32_t* rec = units + (size_t)rank * kUnitInts;
+  const int unit = load_uniform(rec, kUnitId);
   const int qb = nqb - 1 - unit / P.batch;
   const int b = unit % P.batch;
   const int hg = head % nhg;
@@ -437,7 +438,6 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   // the unit's record (written by the prologue kernel) and this lane's query (column n: query
   // 16 qg + n % 16) with the last key it may see + 1; a query whose position is out of range
   // sees nothing (the unit is then poisoned anyway)
-  const int32_t* rec = units + (size_t)unit * kUnitInts;
   const int p0 = load_uniform(rec, kUnitP0);
   const int nidx = load_uniform(rec, kUnitNidx);
   const int lpl = load_uniform(rec, kUnitLpl);
@@ -855,15 +855,13 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   char* ws = (char*)p.workspace;
   const size_t kh_bytes = prefill_kh_bytes(p.num_kv_heads, p.num_indices);
   const size_t qh_bytes = prefill_qh_bytes(p.num_q_heads, p.batch, p.q_len);
-  const size_t order_bytes = prefill_order_bytes(p.batch, p.q_len);
   uint16_t* kh = (uint16_t*)ws;
   uint16_t* qh = (uint16_t*)(ws + kh_bytes);
-  int32_t* order = (int32_t*)(ws + kh_bytes + qh_bytes);
-  int32_t* units = (int32_t*)(ws + kh_bytes + qh_bytes + order_bytes);
+  int32_t* units = (int32_t*)(ws + kh_bytes + qh_bytes);
   // k^: per row up to max_pages_per_row * Hkv / HG tasks, 4 per workgroup, at most 512
   // workgroups per row; two KV heads per wavefront when Hkv is even, so each page's cos/sin is
-  // read once per two heads (measured: faster than one or four).  q^: 4 wavefront tasks per workgroup.  Unit records: 8
-  // units per workgroup.  Then one workgroup for the order of the units.
+  // read once per two heads (measured: faster than one or four).  q^: 4 wavefront tasks per
+  // workgroup.  Unit records: 8 units per workgroup.
   const int hg = p.num_kv_heads % 2 == 0 ? 2 : 1;
   const long long row_tasks = (long long)std::min(p.max_pages_per_row, p.num_indices) * (p.num_kv_heads / hg);
   const int kx = (int)std::min<long long>((row_tasks + 3) / 4, 512);
@@ -873,17 +871,15 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int nqb = (p.q_len + kQB - 1) / kQB;
   const int U = p.batch * nqb;
   const int nu = (U + 7) / 8;
-  const unsigned pgrid = (unsigned)((long long)p.batch * kx + nq + nu + 1);
+  const unsigned pgrid = (unsigned)((long long)p.batch * kx + nq + nu);
   if (hg == 2)
-    hipLaunchKernelGGL(prologue_kernel<2>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, units, kx,
-                       nq, nu);
+    hipLaunchKernelGGL(prologue_kernel<2>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, units, kx, nq);
   else
-    hipLaunchKernelGGL(prologue_kernel<1>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, order, units, kx,
-                       nq, nu);
+    hipLaunchKernelGGL(prologue_kernel<1>, dim3(pgrid), dim3(kPrologueThreads), 0, stream, p, kh, qh, units, kx, nq);
   const unsigned nhg = (unsigned)((p.group + 3) / 4);
   const unsigned grid = (unsigned)U * (unsigned)p.num_kv_heads * nhg;
   if (grid > 0)
-    hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh, qh, order, units);
+    hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kAttendThreads), 0, stream, p, kh, qh, units);
   return hipGetLastError();
 }
 
