@@ -57,6 +57,17 @@ def test_prefill_row_past_the_page_table(gpu):
     assert_parity(out, lse, ref_out, ref_lse, "prefill 40,000-key row", kind="prefill")
 
 
+def test_prefill_more_units_than_the_ranking_holds(gpu):
+    """520 rows of one query each: 520 work units, more than the 512 the prologue ranks, so the
+    units run in number order."""
+    lengths = np.random.default_rng(36).integers(1, 100, size=520)
+    b = workloads.make_batch(36, lengths, q_len=1, num_q_heads=8, num_kv_heads=2, num_pages=4096,
+                             query_mode="prefill")
+    out, lse = run("prefill", make_plan(b), DeviceBatch(b))
+    ref_out, ref_lse = oracle_ref(b)
+    assert_parity(out, lse, ref_out, ref_lse, "prefill, 520 units", kind="prefill")
+
+
 def test_prefill_decode_style_positions_and_no_norm(gpu):
     """Queries ending at L (keys of the chunk not all cached), and no RMSNorm."""
     b = workloads.make_batch(33, [50, 90], q_len=8, num_q_heads=8, num_kv_heads=2, num_pages=32,
