@@ -250,16 +250,21 @@ __device__ __forceinline__ void sum16(float v[8][4]) {
 // 2. dq
 // ---------------------------------------------------------------------------------------
 // k^ and V tiles in LDS: rows of 256 bytes, the 16-byte chunk c of row j stored at chunk
-// c ^ dq_swz(j).  Both read patterns then use all 64 banks without conflict: the S and dP
-// operands (16-byte reads, 16 lanes per LDS cycle: 16 consecutive rows at one chunk, which
-// dq_swz maps to 16 distinct chunks) and the transposed K^T reads for dQ (8-byte reads, 32
-// lanes per cycle: 32 bytes of 8 consecutive rows, whose chunk pairs dq_swz keeps together and
-// spreads over 8 distinct pairs).  (A padded 288-byte pitch was conflict-free for the second
-// pattern only; the first then took two LDS cycles per read.)
+// c ^ dq_swz(j), dq_swz(j) = 2 (j mod 8).  Both read patterns then use all 64 banks without
+// conflict (measured with the LDS bank-conflict counter on these exact patterns):
+//  - the S and dP operands: 16-byte reads, lane (r, g) = (lane % 16, lane / 16) at row r,
+//    chunk 4 kb + g.  Such a read is served 16 lanes per LDS cycle, and the 16 lanes of a
+//    cycle are those with equal lane bit 5 and equal parity of lane bits 2..4 (not 16
+//    consecutive lanes: a swizzle giving each run of 16 consecutive lanes 16 distinct chunks
+//    still took two cycles per group).  g ^ dq_swz(r) is then distinct within every group.
+//  - the transposed K^T (dQ) or dO^T / Q^T (dK/dV) reads: 8-byte reads, 32 lanes per cycle,
+//    32 bytes of each of 8 consecutive rows; the chunk pair {2 m, 2 m + 1} of row j lands on
+//    pair m ^ (j mod 8), distinct over the 8 rows.
+// (A padded 288-byte pitch was conflict-free for the second pattern only.)
 // The tiles are arrays of 16-byte chunks, so that the compiler emits whole 16-byte LDS
 // accesses (it splits them into 4-byte pairs where it cannot prove the alignment).  The dK/dV
 // kernel's q^ and dout tiles have the same layout and the same two read patterns.
-__device__ __forceinline__ int dq_swz(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
+__device__ __forceinline__ int dq_swz(int row) { return 2 * (row & 7); }
 // chunk index of the 16-byte chunk c (dims 8 c .. 8 c + 7) of row j in a swizzled tile
 __device__ __forceinline__ int dq_chunk(int row, int c) { return row * (kHeadDim / 8) + (c ^ dq_swz(row)); }
 struct alignas(16) DqSmem {
